@@ -1,0 +1,253 @@
+// Small kernels around the MFMA contractions: the log-sum-exp combine, operand
+// transposes, per-chunk gradient scales, the db reduction and zero fill.
+#include "kernels.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace llp {
+namespace {
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Per token: merge the per-tile (m, s) partials in increasing tile order
+// (m in log2 units, s = sum of 2^(y - m)), then lse = (M + log2 S) ln 2 and
+// logp = z[t] - lse for a target in [0, V), else +0 (RL-Kernel PR #495,
+// "Behavior changes").
+__global__ void lse_combine_kernel(const float2* __restrict__ partials, int64_t P, int64_t ldp,
+                                   const float* __restrict__ zt, const int64_t* __restrict__ targets,
+                                   int64_t V, int64_t N, float* __restrict__ logp,
+                                   float* __restrict__ lse) {
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float M = -INFINITY, S = 0.0f;
+  for (int64_t i = 0; i < P; ++i) {
+    const float2 q = partials[i * ldp + n];
+    if (q.x == -INFINITY) continue;
+    if (q.x > M) {
+      S = S * __builtin_amdgcn_exp2f(M - q.x) + q.y;
+      M = q.x;
+    } else {
+      S += q.y * __builtin_amdgcn_exp2f(q.x - M);
+    }
+  }
+  const float l = (M + __builtin_amdgcn_logf(S)) * kLn2;
+  if (lse != nullptr) lse[n] = l;
+  if (logp != nullptr) {
+    const int64_t t = targets[n];
+    logp[n] = (t >= 0 && t < V) ? zt[n] - l : 0.0f;
+  }
+}
+
+template <typename T>
+__global__ void transpose_kernel(const T* __restrict__ src, int64_t rows, int64_t cols, int64_t lds,
+                                 T* __restrict__ dst, int64_t ldd) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = src[r * lds + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < cols && r < rows) dst[c * ldd + r] = tile[tx][i];
+  }
+}
+
+// s = smallest power of two >= max |g| over the chunk (1 if that maximum is 0
+// or not finite), so that dlogits / s stays within [-1, 1] and fp16 keeps its
+// precision; multiplying by s again is exact.
+__global__ void chunk_scales_kernel(const float* __restrict__ g, int64_t N, int64_t C,
+                                    float2* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t k = blockIdx.x;
+  const int64_t c0 = k * C, c1 = min(N, c0 + C);
+  float m = 0.0f;
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += blockDim.x) m = fmaxf(m, fabsf(g[i]));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    int e = 0;
+    if (m > 0.0f && isfinite(m)) {
+      frexpf(m, &e);  // m = f 2^e, f in [0.5, 1)  ->  2^e >= m
+      e = max(-126, min(127, e));
+    }
+    scales[k] = make_float2(ldexpf(1.0f, e), ldexpf(1.0f, -e));
+  }
+}
+
+__device__ __forceinline__ bool tok_valid(const int64_t* targets, const float* g, int64_t tok,
+                                          int64_t V, int64_t& t) {
+  t = targets[tok];
+  return t >= 0 && t < V && g[tok] != 0.0f;
+}
+
+template <typename T, typename TT>
+__global__ void db_accum_kernel(const T* __restrict__ dSt, int64_t ldSt, int64_t V, int64_t C,
+                                const float2* __restrict__ scales, int chunk,
+                                const int32_t* __restrict__ head, const int32_t* __restrict__ next,
+                                const int64_t* __restrict__ targets, const float* __restrict__ g,
+                                const float* __restrict__ tcoef, int64_t tok0, TT* __restrict__ db) {
+  const int lane = threadIdx.x & 63;
+  const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (v >= V) return;  // uniform per wave
+  float s = 0.0f;
+  for (int64_t c = lane; c < C; c += 64) s += (float)dSt[v * ldSt + c];
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) {
+    float val = s * scales[chunk].x;
+    int32_t j = head[v];
+    int64_t t;
+    if (j >= 0 && j < C && tok_valid(targets, g, tok0 + j, V, t) && t == v) {
+      for (int64_t it = 0; it < C && j >= 0 && j < C; ++it) {
+        val += tcoef[tok0 + j];
+        j = next[j];
+      }
+    }
+    db[v] = (TT)((float)db[v] + val);
+  }
+}
+
+// One thread per chunk token; the chunk's targets are staged through LDS in
+// slices. A valid token with no earlier valid token of the same target writes
+// head[t]; every valid token writes next[] (the first later valid token with
+// the same target, or -1). No atomics: the lists are in token order.
+__global__ void target_lists_kernel(const int64_t* __restrict__ targets, const float* __restrict__ g,
+                                    int64_t tok0, int64_t C, int64_t V, int32_t* __restrict__ head,
+                                    int32_t* __restrict__ next) {
+  constexpr int kSlice = 2048;
+  __shared__ int32_t st[kSlice];  // target, or -1 for an invalid token
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t t = -1;
+  const bool mine = n < C && tok_valid(targets, g, tok0 + n, V, t);
+  bool first = true;
+  int64_t nxt = -1;
+  for (int64_t base = 0; base < C; base += kSlice) {
+    const int64_t len = min((int64_t)kSlice, C - base);
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < len; i += blockDim.x) {
+      int64_t tj;
+      st[i] = tok_valid(targets, g, tok0 + base + i, V, tj) ? (int32_t)tj : -1;
+    }
+    __syncthreads();
+    if (mine) {
+      for (int64_t i = 0; i < len; ++i) {
+        const int64_t j = base + i;
+        if (st[i] != (int32_t)t) continue;
+        if (j < n) first = false;
+        if (j > n && nxt < 0) nxt = j;
+      }
+    }
+  }
+  if (mine) {
+    next[n] = (int32_t)nxt;
+    if (first) head[t] = (int32_t)n;
+  }
+}
+
+__global__ void zero_kernel(uint32_t* __restrict__ p, int64_t nwords) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) p[i] = 0u;
+}
+
+__global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+template <typename T>
+hipError_t transpose_t(const void* src, int64_t rows, int64_t cols, int64_t lds, void* dst,
+                       int64_t ldd, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols + 63) / 64));  // cols <= 2^22 (validated)
+  transpose_kernel<T><<<grid, 256, 0, s>>>(static_cast<const T*>(src), rows, cols, lds,
+                                           static_cast<T*>(dst), ldd);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t db_t(const void* dSt, int64_t ldSt, int64_t V, int64_t C, const float2* scales, int chunk,
+                const int32_t* head, const int32_t* next, const int64_t* targets, const float* g,
+                const float* tcoef, int64_t tok0, void* db, int tdt, hipStream_t s) {
+  dim3 grid((unsigned)((V + 3) / 4));
+  if (tdt == DT_F32)
+    db_accum_kernel<T, float><<<grid, 256, 0, s>>>(static_cast<const T*>(dSt), ldSt, V, C, scales, chunk,
+                                                   head, next, targets, g, tcoef, tok0,
+                                                   static_cast<float*>(db));
+  else
+    db_accum_kernel<T, T><<<grid, 256, 0, s>>>(static_cast<const T*>(dSt), ldSt, V, C, scales, chunk,
+                                               head, next, targets, g, tcoef, tok0, static_cast<T*>(db));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,
+                              const int64_t* targets, int64_t V, int64_t N, float* logp,
+                              float* lse, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  lse_combine_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(partials, P, ldp, zt, targets, V, N,
+                                                                 logp, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(int dt, const void* src, int64_t rows, int64_t cols, int64_t lds,
+                            void* dst, int64_t ldd, hipStream_t s) {
+  switch (dt) {
+    case DT_F32: return transpose_t<float>(src, rows, cols, lds, dst, ldd, s);
+    case DT_BF16:
+    case DT_F16: return transpose_t<uint16_t>(src, rows, cols, lds, dst, ldd, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, float2* scales,
+                               hipStream_t s) {
+  if (K == 0) return hipSuccess;
+  chunk_scales_kernel<<<(unsigned)K, 256, 0, s>>>(g, N, C, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_db_accum(int dt, const void* dSt, int64_t ldSt, int64_t V, int64_t C,
+                           const float2* scales, int chunk, const int32_t* head, const int32_t* next,
+                           const int64_t* targets, const float* g, const float* tcoef, int64_t tok0,
+                           void* db, int tdt, hipStream_t s) {
+  switch (dt) {
+    case DT_F32:
+      return db_t<float>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, db, tdt, s);
+    case DT_BF16:
+      return db_t<__bf16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, db, tdt, s);
+    case DT_F16:
+      return db_t<_Float16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, db, tdt, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_target_lists(const int64_t* targets, const float* g, int64_t tok0, int64_t C,
+                               int64_t V, int32_t* head, int32_t* next, hipStream_t s) {
+  if (C == 0) return hipSuccess;
+  target_lists_kernel<<<(unsigned)((C + 255) / 256), 256, 0, s>>>(targets, g, tok0, C, V, head, next);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, int64_t n, int esize, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t bytes = n * esize;
+  if (bytes % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 3) == 0) {
+    const int64_t words = bytes / 4;
+    const unsigned blocks = (unsigned)std::min<int64_t>((words + 255) / 256, 65536);
+    zero_kernel<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words);
+  } else {
+    const int64_t halves = bytes / 2;
+    const unsigned blocks = (unsigned)std::min<int64_t>((halves + 255) / 256, 65536);
+    zero_u16_kernel<<<blocks, 256, 0, s>>>(static_cast<uint16_t*>(p), halves);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace llp

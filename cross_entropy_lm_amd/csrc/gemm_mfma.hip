@@ -1,0 +1,455 @@
+// MFMA contraction kernels for gfx950 (CDNA4) with the fused log-prob epilogues.
+//
+// Every contraction of the operator is written as C[m, n] = sum_k A[m, k] B[n, k]
+// with both operands K-contiguous (row-major [rows][ld]):
+//   logits (forward and backward recompute): A = W [V, D], B = h [N, D]
+//   dH = dlogits W:                         A = dlogits [C, V], B = W^T [D, V]
+//   dW += dlogits^T h:                      A = dlogits^T [V, C], B = h^T [D, C]
+// (the transposed operands are produced in the caller's workspace).
+//
+// Tile: 256 x 256 outputs per workgroup of 256 threads (4 waves in a 2 x 2
+// grid, each wave 128 x 128 = 4 x 4 blocks of the 32x32 MFMA). K advances 128
+// bytes per stage (64 bf16/fp16 or 32 fp32); the two operand tiles of a stage
+// are staged through LDS with a 16-byte row pad, double-buffered (144 KiB).
+//
+// MFMA operand layout: for the 32x32 instructions lane l supplies row (l % 32)
+// of A (and column (l % 32) of B) and a group of K values selected by l / 32;
+// A and B use the same lane -> k mapping, so the order of k inside a stage is
+// free. Output: lane l, accumulator r holds C[(r/4)*8 + (l/32)*4 + r%4][l % 32].
+//
+// The epilogues implement, on the fp32 tile of logits z (vocab rows x token
+// columns):
+//   LSE_PARTIAL: per token, m = max_v z and s = sum_v exp(z - m) over the wave's
+//     128 vocab rows (the online max / sum-exp of RL-Kernel PR #495, "Summary",
+//     done per tile), plus the target logit z[t]. exp/log use the hardware
+//     base-2 instructions with z scaled by log2(e).
+//   DLOGITS: dlogits = g [v == t] - g exp(z - lse) (RL-Kernel PR #495,
+//     "Summary", second commit), divided by the chunk's power-of-two scale s
+//     and rounded to the operand dtype; +0 for an out-of-range target or g = 0
+//     ("Behavior changes").
+//   STORE: dH rows = s * C.   ACCUM: table += s * C, in place (RL-Kernel issue
+//     #261, "Current accumulation"; Liger-Kernel PR #1324, "Details").
+#include "kernels.h"
+
+#include <math.h>
+
+namespace llp {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+constexpr int kRowBytes = 128;          // K bytes of one tile row per stage
+constexpr int kPitch = kRowBytes + 16;  // LDS row pitch: the pad puts 8 consecutive rows on distinct banks
+constexpr int kStageBytes = (kTileM + kTileN) * kPitch;
+constexpr int kLdsBytes = 2 * kStageBytes;
+constexpr int kLoadsPerThread = kTileM * (kRowBytes / 16) / kThreads;  // 16-byte chunks per operand
+static_assert(kTileM == kTileN, "loader assumes square tiles");
+
+template <typename T> struct ET;
+template <> struct ET<__bf16> { static constexpr int per16 = 8; };
+template <> struct ET<_Float16> { static constexpr int per16 = 8; };
+template <> struct ET<float> { static constexpr int per16 = 4; };
+
+__device__ __forceinline__ f32x16 mfma_step(__bf16*, u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_step(_Float16*, u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+// fp32: four K=2 steps per 16-byte fragment. Each element is copied to a
+// scalar before the bit cast: a bit cast applied directly to an ext-vector
+// element expression is lowered to element 0 by this compiler.
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ f32x16 mfma_step(float*, u32x4 a, u32x4 b, f32x16 c) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t aj = a[j], bj = b[j];
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(as_f32(aj), as_f32(bj), c, 0, 0, 0);
+  }
+  return c;
+}
+
+// One 16-byte chunk of row `row`, elements [k, k + per16), zero outside [0, rows) x [0, K).
+template <typename T>
+__device__ __forceinline__ u32x4 load_chunk(const T* base, int64_t ld, int64_t row, int64_t rows, int64_t k,
+                                   int64_t K, bool vec) {
+  constexpr int per16 = ET<T>::per16;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < rows && k < K) {
+    const T* p = base + row * ld + k;
+    if (vec && k + per16 <= K) {
+      v = *reinterpret_cast<const u32x4*>(p);
+    } else {
+      union {
+        T e[per16];
+        u32x4 u;
+      } tmp;
+#pragma unroll
+      for (int e = 0; e < per16; ++e) tmp.e[e] = (k + e < K) ? p[e] : (T)0.0f;
+      v = tmp.u;
+    }
+  }
+  return v;
+}
+
+// Tile order: groups of 8 tiles along M, N-major inside a group, so that the
+// workgroups running together share A rows and B rows in L2.
+__device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int G = 8;
+  const int group_size = G * tiles_n;
+  const int group = id / group_size;
+  const int first = group * G;
+  const int gm = min(tiles_m - first, G);
+  const int in = id - group * group_size;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_f32(const T* p, int64_t i) {
+  return (float)p[i];
+}
+
+struct Frag {
+  int lane, wm, wn;
+  __device__ inline int row(int mi, int r) const {  // row inside the 256-row tile
+    return wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+  }
+  __device__ inline int col(int ni) const { return wn * 128 + ni * 32 + (lane & 31); }
+};
+
+// ---------------------------------------------------------------- epilogues
+template <typename T>
+__device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, f32x16 (&acc)[4][4], int tm, int64_t m0,
+                                int64_t n0, const Frag& f) {
+  const EpiParams& e = p.ep;
+  const T* bias = static_cast<const T*>(e.bias);
+  int64_t tgt[4];
+  float mx[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int64_t n = n0 + f.col(ni);
+    tgt[ni] = (n < p.N) ? e.targets[e.tok0 + n] : -1;
+    mx[ni] = -INFINITY;
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = m0 + f.row(mi, r);
+      const bool vv = v < p.M;
+      const float bv = (bias != nullptr && vv) ? ld_f32(bias, v) : 0.0f;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const float z = vv ? acc[mi][ni][r] + bv : -INFINITY;
+        acc[mi][ni][r] = z;
+        mx[ni] = fmaxf(mx[ni], z);
+        if (vv && v == tgt[ni]) e.zt[e.tok0 + n0 + f.col(ni)] = z;
+      }
+    }
+  }
+  float m2[4], s[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    mx[ni] = fmaxf(mx[ni], __shfl_xor(mx[ni], 32));
+    m2[ni] = mx[ni] * kLog2e;
+    s[ni] = 0.0f;
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        s[ni] += __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2[ni]));
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    float sv = s[ni] + __shfl_xor(s[ni], 32);
+    if (mx[ni] == -INFINITY) sv = 0.0f;  // this wave's rows all lie past V
+    const int64_t n = n0 + f.col(ni);
+    if (f.lane < 32 && n < p.N)
+      e.partials[(int64_t)(tm * kWaveM + f.wm) * e.ldp + n] = make_float2(m2[ni], sv);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void epi_dlogits(const GemmProblem& p, f32x16 (&acc)[4][4], int64_t m0,
+                                            int64_t n0, const Frag& f) {
+  const EpiParams& e = p.ep;
+  const T* bias = static_cast<const T*>(e.bias);
+  T* dS = static_cast<T*>(e.dS);
+  T* dSt = static_cast<T*>(e.dSt);
+  const float inv = e.scales[e.chunk].y;
+  int64_t tgt[4];
+  float gv[4], gs[4], l2[4];
+  bool rv[4];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int64_t n = n0 + f.col(ni);
+    const bool nv = n < p.N;
+    const int64_t tok = e.tok0 + n;
+    tgt[ni] = nv ? e.targets[tok] : -1;
+    gv[ni] = nv ? e.g[tok] : 0.0f;
+    rv[ni] = nv && tgt[ni] >= 0 && tgt[ni] < p.M && gv[ni] != 0.0f;
+    gs[ni] = gv[ni] * inv;
+    l2[ni] = nv ? e.lse[tok] * kLog2e : 0.0f;
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = m0 + f.row(mi, r);
+      if (v >= p.M) continue;
+      const float bv = (bias != nullptr) ? ld_f32(bias, v) : 0.0f;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int64_t n = n0 + f.col(ni);
+        if (n >= p.N) continue;
+        const float z = acc[mi][ni][r] + bv;
+        const float pr = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -l2[ni]));
+        float d = 0.0f;  // +0 for a row that takes no part
+        if (rv[ni]) {
+          if (v == tgt[ni]) {
+            e.tcoef[e.tok0 + n] = fmaf(-gv[ni], pr, gv[ni]);  // g (1 - p_t), exact part
+          } else {
+            d = -gs[ni] * pr;
+          }
+        }
+        const T dt = (T)d;
+        if (dS != nullptr) dS[n * e.ldS + v] = dt;
+        if (dSt != nullptr) dSt[v * e.ldSt + n] = dt;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ bool token_valid(const EpiParams& e, int64_t tok, int64_t& t) {
+  t = e.targets[tok];
+  return t >= 0 && t < e.V && e.g[tok] != 0.0f;
+}
+
+// dH rows of the chunk: out[m, :] = s C[m, :] + tcoef[m] W[t_m, :].
+template <typename T>
+__device__ __forceinline__ void epi_store(const GemmProblem& p, f32x16 (&acc)[4][4], int64_t m0,
+                                          int64_t n0, const Frag& f) {
+  const EpiParams& e = p.ep;
+  T* out = static_cast<T*>(e.out);
+  const T* W = static_cast<const T*>(e.W);
+  const float sc = e.scales[e.chunk].x;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t m = m0 + f.row(mi, r);
+      if (m >= p.M) continue;
+      int64_t t;
+      const bool valid = token_valid(e, e.tok0 + m, t);
+      const float c = valid ? e.tcoef[e.tok0 + m] : 0.0f;
+      const T* wrow = W + (valid ? t : 0) * e.ldW;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int64_t n = n0 + f.col(ni);
+        if (n < p.N) {
+          float val = acc[mi][ni][r] * sc;
+          if (valid) val = fmaf(c, ld_f32(wrow, n), val);
+          out[m * e.ldo + n] = (T)val;
+        }
+      }
+    }
+}
+
+// dW rows: table[v, :] += s C[v, :] + sum, in token order, of tcoef[n] h[n, :]
+// over the chunk's valid tokens with target v.
+template <typename T, typename TT>
+__device__ __forceinline__ void epi_accum_t(const GemmProblem& p, f32x16 (&acc)[4][4], int64_t m0,
+                                            int64_t n0, const Frag& f) {
+  const EpiParams& e = p.ep;
+  TT* tab = static_cast<TT*>(e.out);
+  const T* h = static_cast<const T*>(e.h);
+  const float sc = e.scales[e.chunk].x;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t m = m0 + f.row(mi, r);
+      if (m >= p.M) continue;
+      float val[4];
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) val[ni] = acc[mi][ni][r] * sc;
+      // head entries of targets absent from this chunk are stale: accept only
+      // an index of this chunk whose token is valid and has target m
+      int32_t j = e.head[m];
+      int64_t t;
+      if (j >= 0 && j < e.ntok && token_valid(e, e.tok0 + j, t) && t == m) {
+        // at most ntok steps: the walk ends even if the list were malformed
+        for (int64_t it = 0; it < e.ntok && j >= 0 && j < e.ntok; ++it) {
+          const float c = e.tcoef[e.tok0 + j];
+          const T* hrow = h + (e.tok0 + j) * e.ldh;
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) {
+            const int64_t n = n0 + f.col(ni);
+            if (n < p.N) val[ni] = fmaf(c, ld_f32(hrow, n), val[ni]);
+          }
+          j = e.next[j];
+        }
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int64_t n = n0 + f.col(ni);
+        if (n < p.N) {
+          TT* q = tab + m * e.ldo + n;
+          *q = (TT)((float)*q + val[ni]);
+        }
+      }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void epi_accum(const GemmProblem& p, f32x16 (&acc)[4][4], int64_t m0, int64_t n0,
+                          const Frag& f) {
+  if (p.ep.out_dt == DT_F32)
+    epi_accum_t<T, float>(p, acc, m0, n0, f);
+  else
+    epi_accum_t<T, T>(p, acc, m0, n0, f);
+}
+
+// ---------------------------------------------------------------- main loop
+template <typename T, int E>
+__device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* smem) {
+  constexpr int per16 = ET<T>::per16;
+  constexpr int BK = (kRowBytes / 16) * per16;  // K elements per stage
+  int tm, tn;
+  tile_coords(id, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kTileM;
+  const int64_t n0 = (int64_t)tn * kTileN;
+  const int tid = threadIdx.x;
+  Frag f;
+  f.lane = tid & 63;
+  f.wm = (tid >> 6) >> 1;
+  f.wn = (tid >> 6) & 1;
+  const T* A = static_cast<const T*>(p.A);
+  const T* B = static_cast<const T*>(p.B);
+  const int64_t nk = (p.K + BK - 1) / BK;
+  const bool avec = p.a_vec != 0, bvec = p.b_vec != 0;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
+  auto gload = [&](int64_t kt) {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) {
+      const int c = tid + i * kThreads;
+      const int row = c >> 3;
+      const int64_t k = kt * BK + (c & 7) * per16;
+      ra[i] = load_chunk<T>(A, p.lda, m0 + row, p.M, k, p.K, avec);
+      rb[i] = load_chunk<T>(B, p.ldb, n0 + row, p.N, k, p.K, bvec);
+    }
+  };
+  auto sstore = [&](int buf) {
+    char* sa = smem + buf * kStageBytes;
+    char* sb = sa + kTileM * kPitch;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerThread; ++i) {
+      const int c = tid + i * kThreads;
+      const int off = (c >> 3) * kPitch + (c & 7) * 16;
+      *reinterpret_cast<u32x4*>(sa + off) = ra[i];
+      *reinterpret_cast<u32x4*>(sb + off) = rb[i];
+    }
+  };
+  auto compute = [&](int buf) {
+    const char* sa = smem + buf * kStageBytes;
+    const char* sb = sa + kTileM * kPitch;
+    const int lrow = f.lane & 31;
+    const int lk = (f.lane >> 5) * 16;
+#pragma unroll
+    for (int s = 0; s < kRowBytes / 32; ++s) {
+      u32x4 af[4], bf[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const u32x4*>(sa + (f.wm * 128 + mi * 32 + lrow) * kPitch + s * 32 + lk);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        bf[ni] = *reinterpret_cast<const u32x4*>(sb + (f.wn * 128 + ni * 32 + lrow) * kPitch + s * 32 + lk);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_step((T*)nullptr, af[mi], bf[ni], acc[mi][ni]);
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    if (kt + 1 < nk) gload(kt + 1);
+    compute(buf);
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if constexpr (E == EPI_LSE_PARTIAL) epi_lse_partial<T>(p, acc, tm, m0, n0, f);
+  if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f);
+  if constexpr (E == EPI_STORE) epi_store<T>(p, acc, m0, n0, f);
+  if constexpr (E == EPI_ACCUM) epi_accum<T>(p, acc, m0, n0, f);
+}
+
+template <typename T, int E0, int E1>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmProblem p1, int ntiles0) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  const int bid = blockIdx.x;
+  if (bid < ntiles0) {
+    tile_run<T, E0>(p0, bid, smem);
+  } else {
+    if constexpr (E1 != EPI_NONE) tile_run<T, E1>(p1, bid - ntiles0, smem);
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s) {
+  const int nt0 = p0 ? p0->tiles_m * p0->tiles_n : 0;
+  const int nt1 = p1 ? p1->tiles_m * p1->tiles_n : 0;
+  if (nt0 + nt1 == 0) return hipSuccess;
+  GemmProblem empty = {};
+  const GemmProblem& a = p0 ? *p0 : empty;
+  const GemmProblem& b = p1 ? *p1 : empty;
+  const int e0 = p0 ? p0->epi : EPI_NONE;
+  const int e1 = p1 ? p1->epi : EPI_NONE;
+  dim3 grid(nt0 + nt1), block(kThreads);
+  if (e0 == EPI_LSE_PARTIAL && e1 == EPI_NONE) {
+    gemm_kernel<T, EPI_LSE_PARTIAL, EPI_NONE><<<grid, block, 0, s>>>(a, b, nt0);
+  } else if (e0 == EPI_DLOGITS && e1 == EPI_NONE) {
+    gemm_kernel<T, EPI_DLOGITS, EPI_NONE><<<grid, block, 0, s>>>(a, b, nt0);
+  } else if ((e0 == EPI_STORE || e0 == EPI_NONE) && (e1 == EPI_ACCUM || e1 == EPI_NONE)) {
+    gemm_kernel<T, EPI_STORE, EPI_ACCUM><<<grid, block, 0, s>>>(a, b, nt0);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int dt, const GemmProblem* p0, const GemmProblem* p1, hipStream_t s) {
+  switch (dt) {
+    case DT_BF16: return launch_t<__bf16>(p0, p1, s);
+    case DT_F16: return launch_t<_Float16>(p0, p1, s);
+    case DT_F32: return launch_t<float>(p0, p1, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace llp

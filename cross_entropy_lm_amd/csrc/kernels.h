@@ -1,0 +1,122 @@
+// Internal launch interface between the C-ABI layer (llp_api.hip) and the
+// gfx950 kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llp {
+
+// Element type codes (same values as llp_dtype).
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+inline int dt_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+// Epilogue kinds of the MFMA contraction C[m, n] = sum_k A[m, k] B[n, k].
+enum Epi : int {
+  EPI_NONE = 0,
+  EPI_LSE_PARTIAL = 1,  // logits tile -> per-token (max, sum-exp) partials + target logit
+  EPI_DLOGITS = 2,      // logits tile -> dlogits / scale, stored token-major and/or vocab-major
+  EPI_STORE = 3,        // out[m, n] = scale * C, rounded to the operand dtype (dH)
+  EPI_ACCUM = 4         // table[m, n] += scale * C (dW, fp32 or operand-dtype table)
+};
+
+// Tile geometry shared by host (grid sizing, workspace layout) and device.
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+constexpr int kWaveM = 2;  // waves along M; each wave owns 128 rows of the tile
+constexpr int kThreads = 256;
+
+// dlogits = g (onehot(t) - softmax(z)) is split into its softmax part
+// -g p, stored in the operand dtype (divided by the chunk's power-of-two
+// scale s) as the contraction operand, and its one-hot part g (1 - p_t), one
+// fp32 value per token ("tcoef") that the epilogues add exactly:
+//   dH[n, :] += tcoef[n] W[t_n, :],  dW[t_n, :] += tcoef[n] h[n, :],  db[t_n] += tcoef[n].
+// A token takes part only if 0 <= t < V and g != 0 ("valid").
+struct EpiParams {
+  const void* bias;        // [V] operand dtype, or null
+  const int64_t* targets;  // [tokens], indexed tok0 + local token
+  const float* g;          // [tokens] upstream gradient
+  int64_t tok0;            // first token of this problem
+  int64_t V;
+  // EPI_LSE_PARTIAL (M = vocab, N = tokens)
+  float2* partials;        // [2 * tiles_m][ldp]: (max * log2 e, sum exp2) per wave-row block
+  int64_t ldp;
+  float* zt;               // [tokens] target logit
+  // EPI_DLOGITS (M = vocab, N = chunk tokens)
+  const float* lse;        // [tokens]
+  void* dS;                // [N][ldS] token-major softmax part / s, or null
+  int64_t ldS;
+  void* dSt;               // [V][ldSt] vocab-major softmax part / s, or null
+  int64_t ldSt;
+  float* tcoef;            // [tokens] one-hot part g (1 - p_t) (written here, read below)
+  // EPI_STORE (M = chunk tokens, N = D): out = s C + tcoef W[t]
+  const void* W;
+  int64_t ldW;
+  // EPI_ACCUM (M = V, N = D): table += s C + sum over the chunk's tokens with target m of tcoef h
+  const void* h;
+  int64_t ldh;
+  const int32_t* head;     // [V] first chunk token with target v (entries for absent v are stale)
+  const int32_t* next;     // [C] next chunk token with the same target, -1 at the end
+  int64_t ntok;            // tokens in the chunk
+  // EPI_STORE and EPI_ACCUM
+  void* out;
+  int64_t ldo;
+  int out_dt;              // dtype of out (EPI_ACCUM table: DT_F32 or the operand dtype)
+  // backward epilogues: scales[chunk] = (s, 1/s)
+  const float2* scales;
+  int chunk;
+};
+
+struct GemmProblem {
+  const void* A;  // [M][lda], K contiguous
+  const void* B;  // [N][ldb], K contiguous
+  int64_t lda, ldb;
+  int64_t M, N, K;
+  int a_vec, b_vec;  // 1: rows may be read with 16-byte vector loads
+  int tiles_m, tiles_n;
+  int epi;
+  EpiParams ep;
+};
+
+// Launch one or two independent problems of the same operand dtype in one
+// grid (the second problem's tiles follow the first's). Returns hipError_t.
+hipError_t launch_gemm(int dt, const GemmProblem* p0, const GemmProblem* p1, hipStream_t s);
+
+// partials [P][N] + zt -> logp, lse (one thread per token, fixed order over P).
+hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,
+                              const int64_t* targets, int64_t V, int64_t N, float* logp,
+                              float* lse, hipStream_t s);
+
+// dst[c][r] = src[r][c] for r < rows, c < cols (element size from dt).
+hipError_t launch_transpose(int dt, const void* src, int64_t rows, int64_t cols, int64_t lds,
+                            void* dst, int64_t ldd, hipStream_t s);
+
+// scales[k] = (s, 1/s), s = smallest power of two >= max |g| over chunk k (1 if that is 0).
+hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, float2* scales,
+                               hipStream_t s);
+
+// db[v] += s_k * sum_{c < C} dSt[v][c] + sum of tcoef over the chunk's tokens with target v
+// (table dtype tdt; dSt in operand dtype dt).
+hipError_t launch_db_accum(int dt, const void* dSt, int64_t ldSt, int64_t V, int64_t C,
+                           const float2* scales, int chunk, const int32_t* head, const int32_t* next,
+                           const int64_t* targets, const float* g, const float* tcoef, int64_t tok0,
+                           void* db, int tdt, hipStream_t s);
+
+// Per chunk [tok0, tok0 + C): head[t] = first valid token with target t and
+// next[n] = the following one (-1 at the end), local indices, in token order.
+// Only head entries of targets present in the chunk are written.
+hipError_t launch_target_lists(const int64_t* targets, const float* g, int64_t tok0, int64_t C,
+                               int64_t V, int32_t* head, int32_t* next, hipStream_t s);
+
+// Fill n elements of size esize with +0.
+hipError_t launch_zero(void* p, int64_t n, int esize, hipStream_t s);
+
+// Logits-only rows.
+hipError_t launch_rows_fwd(int dt, const void* logits, int64_t N, int64_t V,
+                           const int64_t* targets, float* logp, float* lse, hipStream_t s);
+hipError_t launch_rows_bwd(int dt, const void* logits, int64_t N, int64_t V,
+                           const int64_t* targets, const float* g, const float* lse,
+                           void* dlogits, hipStream_t s);
+
+}  // namespace llp

@@ -1,0 +1,274 @@
+// C ABI entry points (declared in include/llp.h): validate, lay out the
+// caller's workspace, and enqueue the kernels on the caller's stream.
+#include <string.h>
+
+#include "../../include/llp.h"
+#include "kernels.h"
+#include "plan.h"
+
+namespace llp {
+namespace {
+
+inline char* at(void* base, int64_t off) { return static_cast<char*>(base) + off; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+inline int st_hip(hipError_t e) { return e == hipSuccess ? LLP_OK : LLP_EHIP; }
+
+#define LLP_TRY(expr)                      \
+  do {                                     \
+    const hipError_t e_ = (expr);          \
+    if (e_ != hipSuccess) return LLP_EHIP; \
+  } while (0)
+
+// Logits tile problem over tokens [tok0, tok0 + n) of h: A = W [V][D], B = h rows.
+GemmProblem logits_problem(int64_t tok0, int64_t n, int64_t D, int64_t V, int dtype,
+                           const void* h, const void* W) {
+  GemmProblem p = {};
+  const int64_t e = esize(dtype);
+  const int per16 = (int)(16 / e);
+  p.A = W;
+  p.B = static_cast<const char*>(h) + tok0 * D * e;
+  p.lda = D;
+  p.ldb = D;
+  p.M = V;
+  p.N = n;
+  p.K = D;
+  p.a_vec = (D % per16 == 0) && aligned16(W);
+  p.b_vec = (D % per16 == 0) && aligned16(p.B);
+  p.tiles_m = (int)ceil_div(V, kTile);
+  p.tiles_n = (int)ceil_div(n, kTile);
+  return p;
+}
+
+// Forward into (partials, zt) then the combine; shared by linear_logp_fwd and
+// by the backward when no lse is given.
+int run_forward(int64_t N, int64_t D, int64_t V, int dtype, const void* h, const void* W,
+                const void* b, const int64_t* targets, float* logp, float* lse, void* ws,
+                const FwdPlan& fp, hipStream_t s) {
+  float2* partials = reinterpret_cast<float2*>(at(ws, fp.off_partials));
+  float* zt = reinterpret_cast<float*>(at(ws, fp.off_zt));
+  GemmProblem p = logits_problem(0, N, D, V, dtype, h, W);
+  p.epi = EPI_LSE_PARTIAL;
+  p.ep.bias = b;
+  p.ep.targets = targets;
+  p.ep.tok0 = 0;
+  p.ep.partials = partials;
+  p.ep.ldp = N;
+  p.ep.zt = zt;
+  LLP_TRY(launch_gemm(dtype, &p, nullptr, s));
+  LLP_TRY(launch_lse_combine(partials, fp.P, N, zt, targets, V, N, logp, lse, s));
+  return LLP_OK;
+}
+
+}  // namespace
+}  // namespace llp
+
+using namespace llp;
+
+extern "C" {
+
+int llp_version(void) { return 100; }
+
+const char* llp_strerror(int status) {
+  switch (status) {
+    case LLP_OK: return "ok";
+    case LLP_EINVAL: return "invalid argument";
+    case LLP_EWORKSPACE: return "workspace too small";
+    case LLP_EOVERFLOW: return "size overflow";
+    case LLP_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t linear_logp_chunk_rows(int64_t N, int64_t V, int64_t chunk) { return chunk_rows(N, V, chunk); }
+
+int64_t linear_logp_num_chunks(int64_t N, int64_t V, int64_t chunk) {
+  const int64_t c = chunk_rows(N, V, chunk);
+  if (c < 0) return -1;
+  return N > 0 ? ceil_div(N, c) : 0;
+}
+
+int linear_logp_fwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return LLP_EINVAL;
+  FwdPlan fp;
+  const int st = plan_fwd(N, D, V, dtype, &fp);
+  if (st != LLP_OK) return st;
+  *bytes = (size_t)fp.bytes;
+  return LLP_OK;
+}
+
+int linear_logp_fwd(int64_t N, int64_t D, int64_t V, int dtype, const void* h, const void* W,
+                    const void* b, const int64_t* targets, float* logp, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  FwdPlan fp;
+  int st = plan_fwd(N, D, V, dtype, &fp);
+  if (st != LLP_OK) return st;
+  if (N == 0) return LLP_OK;
+  if (h == nullptr || W == nullptr || targets == nullptr || logp == nullptr) return LLP_EINVAL;
+  if ((size_t)fp.bytes > workspace_bytes || (fp.bytes > 0 && workspace == nullptr)) return LLP_EWORKSPACE;
+  return run_forward(N, D, V, dtype, h, W, b, targets, logp, lse, workspace, fp,
+                     static_cast<hipStream_t>(stream));
+}
+
+int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
+                                   int want_dH, int want_dW, int want_db, int have_lse,
+                                   size_t* bytes) {
+  if (bytes == nullptr) return LLP_EINVAL;
+  BwdPlan bp;
+  const int st = plan_bwd(N, D, V, dtype, chunk, want_dH, want_dW, want_db, have_lse, &bp);
+  if (st != LLP_OK) return st;
+  *bytes = (size_t)bp.bytes;
+  return LLP_OK;
+}
+
+int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, const void* h,
+                    const void* W, const void* b, const int64_t* targets, const float* g,
+                    const float* lse, void* dH, void* dW, int dW_dtype, void* db, int accumulate,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const bool want_dH = dH != nullptr, want_dW = dW != nullptr, want_db = db != nullptr;
+  BwdPlan bp;
+  int st = plan_bwd(N, D, V, dtype, chunk, want_dH, want_dW, want_db, lse != nullptr, &bp);
+  if (st != LLP_OK) return st;
+  if (accumulate != 0 && accumulate != 1) return LLP_EINVAL;
+  if ((want_dW || want_db) && !(dW_dtype == LLP_F32 || dW_dtype == dtype)) return LLP_EINVAL;
+  if (want_db && b == nullptr) return LLP_EINVAL;
+  if (N > 0 && (want_dH || want_dW || want_db) &&
+      (h == nullptr || W == nullptr || targets == nullptr || g == nullptr))
+    return LLP_EINVAL;
+  if ((size_t)bp.bytes > workspace_bytes || (bp.bytes > 0 && workspace == nullptr)) return LLP_EWORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t e = esize(dtype);
+  const int64_t te = (dW_dtype == LLP_F32) ? 4 : e;
+  if (!accumulate) {
+    if (want_dW) LLP_TRY(launch_zero(dW, V * D, (int)te, s));
+    if (want_db) LLP_TRY(launch_zero(db, V, (int)te, s));
+  }
+  if (N == 0 || !(want_dH || want_dW || want_db)) return LLP_OK;
+
+  float2* scales = reinterpret_cast<float2*>(at(workspace, bp.off_scales));
+  LLP_TRY(launch_chunk_scales(g, N, bp.C, bp.K, scales, s));
+  const float* lse_use = lse;
+  if (lse == nullptr) {
+    float* lse_ws = reinterpret_cast<float*>(at(workspace, bp.off_lse));
+    void* fws = at(workspace, bp.off_fwd);
+    st = run_forward(N, D, V, dtype, h, W, b, targets, nullptr, lse_ws, fws, bp.fwd, s);
+    if (st != LLP_OK) return st;
+    lse_use = lse_ws;
+  }
+  void* Wt = want_dH ? at(workspace, bp.off_Wt) : nullptr;
+  void* dS = want_dH ? at(workspace, bp.off_dS) : nullptr;
+  void* dSt = (want_dW || want_db) ? at(workspace, bp.off_dSt) : nullptr;
+  void* ht = want_dW ? at(workspace, bp.off_ht) : nullptr;
+  float* tcoef = reinterpret_cast<float*>(at(workspace, bp.off_tcoef));
+  int32_t* head = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_head)) : nullptr;
+  int32_t* next = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_next)) : nullptr;
+  if (want_dH) LLP_TRY(launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
+
+  for (int64_t k = 0; k < bp.K; ++k) {
+    const int64_t c0 = k * bp.C;
+    const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
+    // dlogits of the chunk, recomputed from the logits tile and the saved lse
+    GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
+    p.epi = EPI_DLOGITS;
+    p.ep.bias = b;
+    p.ep.targets = targets;
+    p.ep.tok0 = c0;
+    p.ep.V = V;
+    p.ep.g = g;
+    p.ep.lse = lse_use;
+    p.ep.tcoef = tcoef;
+    p.ep.dS = dS;
+    p.ep.ldS = bp.ldS;
+    p.ep.dSt = dSt;
+    p.ep.ldSt = bp.ldSt;
+    p.ep.scales = scales;
+    p.ep.chunk = (int)k;
+    LLP_TRY(launch_gemm(dtype, &p, nullptr, s));
+    if (want_dW)
+      LLP_TRY(launch_transpose(dtype, static_cast<const char*>(h) + c0 * D * e, Ck, D, D, ht, bp.ldSt, s));
+    if (want_dW || want_db) LLP_TRY(launch_target_lists(targets, g, c0, Ck, V, head, next, s));
+    if (want_db)
+      LLP_TRY(launch_db_accum(dtype, dSt, bp.ldSt, V, Ck, scales, (int)k, head, next, targets, g, tcoef,
+                              c0, db, dW_dtype, s));
+    GemmProblem ph = {}, pw = {};
+    if (want_dH) {
+      ph.A = dS;
+      ph.B = Wt;
+      ph.lda = bp.ldS;
+      ph.ldb = bp.ldWt;
+      ph.M = Ck;
+      ph.N = D;
+      ph.K = V;
+      ph.a_vec = ph.b_vec = 1;
+      ph.tiles_m = (int)ceil_div(Ck, kTile);
+      ph.tiles_n = (int)ceil_div(D, kTile);
+      ph.epi = EPI_STORE;
+      ph.ep.out = static_cast<char*>(dH) + c0 * D * e;
+      ph.ep.ldo = D;
+      ph.ep.out_dt = dtype;
+      ph.ep.targets = targets;
+      ph.ep.g = g;
+      ph.ep.tok0 = c0;
+      ph.ep.V = V;
+      ph.ep.tcoef = tcoef;
+      ph.ep.W = W;
+      ph.ep.ldW = D;
+      ph.ep.scales = scales;
+      ph.ep.chunk = (int)k;
+    }
+    if (want_dW) {
+      pw.A = dSt;
+      pw.B = ht;
+      pw.lda = bp.ldSt;
+      pw.ldb = bp.ldSt;
+      pw.M = V;
+      pw.N = D;
+      pw.K = Ck;
+      pw.a_vec = pw.b_vec = 1;
+      pw.tiles_m = (int)ceil_div(V, kTile);
+      pw.tiles_n = (int)ceil_div(D, kTile);
+      pw.epi = EPI_ACCUM;
+      pw.ep.out = dW;
+      pw.ep.ldo = D;
+      pw.ep.out_dt = dW_dtype;
+      pw.ep.targets = targets;
+      pw.ep.g = g;
+      pw.ep.tok0 = c0;
+      pw.ep.V = V;
+      pw.ep.tcoef = tcoef;
+      pw.ep.h = h;
+      pw.ep.ldh = D;
+      pw.ep.head = head;
+      pw.ep.next = next;
+      pw.ep.ntok = Ck;
+      pw.ep.scales = scales;
+      pw.ep.chunk = (int)k;
+    }
+    if (want_dH || want_dW)
+      LLP_TRY(launch_gemm(dtype, want_dH ? &ph : nullptr, want_dW ? &pw : nullptr, s));
+  }
+  return LLP_OK;
+}
+
+int logp_fwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t* targets, float* logp,
+             float* lse, void* stream) {
+  const int st = check_rows(N, V, dtype);
+  if (st != LLP_OK) return st;
+  if (N == 0) return LLP_OK;
+  if (logits == nullptr || targets == nullptr || logp == nullptr) return LLP_EINVAL;
+  return st_hip(launch_rows_fwd(dtype, logits, N, V, targets, logp, lse, static_cast<hipStream_t>(stream)));
+}
+
+int logp_bwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t* targets, const float* g,
+             const float* lse, void* dlogits, void* stream) {
+  const int st = check_rows(N, V, dtype);
+  if (st != LLP_OK) return st;
+  if (N == 0) return LLP_OK;
+  if (logits == nullptr || targets == nullptr || g == nullptr || dlogits == nullptr) return LLP_EINVAL;
+  return st_hip(launch_rows_bwd(dtype, logits, N, V, targets, g, lse, dlogits,
+                                static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+// Host-side argument checks, chunk policy and workspace layout of the C ABI.
+// Pure C++: no HIP call, so every error path can be exercised without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/llp.h"
+
+namespace llp {
+
+constexpr int64_t kMaxD = int64_t(1) << 22;     // transpose grid.y and tile count limits
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;  // one workgroup per row / grid.x
+constexpr int64_t kTile = 256;                  // contraction tile edge (M and N)
+constexpr int64_t kAlign = 256;                 // workspace region alignment (bytes)
+
+inline bool dtype_ok(int dt) { return dt == LLP_F32 || dt == LLP_BF16 || dt == LLP_F16; }
+inline int64_t esize(int dt) { return dt == LLP_F32 ? 4 : 2; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// a * b with overflow detection (a, b >= 0).
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+inline bool add_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a > INT64_MAX - b) return false;
+  *out = a + b;
+  return true;
+}
+
+inline int64_t chunk_rows(int64_t N, int64_t V, int64_t chunk) {
+  if (N < 0 || V < 1) return -1;
+  int64_t c = chunk > 0 ? chunk : (int64_t(1) << 24) / V;
+  if (c < 1) c = 1;
+  const int64_t cap = N > 0 ? N : 1;
+  return c < cap ? c : cap;
+}
+
+// Byte layout of a workspace: regions appended at kAlign boundaries.
+struct Layout {
+  int64_t bytes = 0;
+  bool ok = true;
+  int64_t add(int64_t n) {  // returns the region's offset, or -1 (sets ok = false)
+    if (!ok) return -1;
+    int64_t off = round_up(bytes, kAlign);
+    int64_t end;
+    if (n < 0 || !add_ok(off, n, &end)) {
+      ok = false;
+      return -1;
+    }
+    bytes = end;
+    return off;
+  }
+};
+
+// Shapes common to both linear entry points; returns an llp_status.
+inline int check_linear_shapes(int64_t N, int64_t D, int64_t V, int dtype) {
+  if (!dtype_ok(dtype)) return LLP_EINVAL;
+  if (N < 0 || D < 1 || V < 1) return LLP_EINVAL;
+  if (N > kMaxRows || V > kMaxRows || D > kMaxD) return LLP_EOVERFLOW;
+  int64_t t;
+  if (!mul_ok(N, D, &t) || !mul_ok(t, esize(dtype), &t)) return LLP_EOVERFLOW;
+  if (!mul_ok(V, D, &t) || !mul_ok(t, 4, &t)) return LLP_EOVERFLOW;
+  // one workgroup per 256 x 256 output tile: the tile count must fit grid.x
+  if (ceil_div(V, kTile) * ceil_div(N > 0 ? N : 1, kTile) > kMaxRows) return LLP_EOVERFLOW;
+  if (ceil_div(V, kTile) * ceil_div(D, kTile) > kMaxRows) return LLP_EOVERFLOW;
+  return LLP_OK;
+}
+
+struct FwdPlan {
+  int64_t P = 0;             // partial rows: 2 per vocab tile
+  int64_t off_partials = 0;  // float2 [P][N]
+  int64_t off_zt = 0;        // float [N]
+  int64_t bytes = 0;
+};
+
+inline int plan_fwd(int64_t N, int64_t D, int64_t V, int dtype, FwdPlan* p) {
+  int st = check_linear_shapes(N, D, V, dtype);
+  if (st != LLP_OK) return st;
+  *p = FwdPlan();
+  if (N == 0) return LLP_OK;
+  p->P = 2 * ceil_div(V, kTile);
+  Layout L;
+  int64_t n;
+  if (!mul_ok(p->P, N, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
+  p->off_partials = L.add(n);
+  p->off_zt = L.add(N * 4);
+  if (!L.ok) return LLP_EOVERFLOW;
+  p->bytes = L.bytes;
+  return LLP_OK;
+}
+
+struct BwdPlan {
+  int64_t C = 0, K = 0;                  // tokens per chunk, number of chunks
+  int64_t ldWt = 0, ldS = 0, ldSt = 0;   // leading dimensions (elements), multiples of 8
+  int64_t off_scales = -1;               // float2 [K]
+  int64_t off_lse = -1;                  // float [N] when the caller gives no lse
+  FwdPlan fwd;                           // and the forward's workspace, placed after it
+  int64_t off_fwd = -1;
+  int64_t off_Wt = -1;                   // W^T [D][ldWt]            (dH)
+  int64_t off_dS = -1;                   // dlogits [C][ldS]         (dH)
+  int64_t off_dSt = -1;                  // dlogits^T [V][ldSt]      (dW or db)
+  int64_t off_ht = -1;                   // h^T of one chunk [D][ldSt] (dW)
+  int64_t off_tcoef = -1;                // float [N]: one-hot part g (1 - p_t) per token
+  int64_t off_head = -1;                 // int32 [V]: first chunk token per target   (dW or db)
+  int64_t off_next = -1;                 // int32 [C]: next chunk token, same target (dW or db)
+  int64_t bytes = 0;
+};
+
+inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, int want_dH,
+                    int want_dW, int want_db, int have_lse, BwdPlan* p) {
+  int st = check_linear_shapes(N, D, V, dtype);
+  if (st != LLP_OK) return st;
+  *p = BwdPlan();
+  p->C = chunk_rows(N, V, chunk);
+  p->K = N > 0 ? ceil_div(N, p->C) : 0;
+  if (N == 0 || !(want_dH || want_dW || want_db)) return LLP_OK;
+  const int64_t e = esize(dtype);
+  p->ldWt = round_up(V, 8);
+  p->ldS = round_up(V, 8);
+  p->ldSt = round_up(p->C, 8);
+  Layout L;
+  int64_t n;
+  p->off_scales = L.add(p->K * 8);
+  if (!have_lse) {
+    p->off_lse = L.add(N * 4);
+    st = plan_fwd(N, D, V, dtype, &p->fwd);
+    if (st != LLP_OK) return st;
+    p->off_fwd = L.add(p->fwd.bytes);
+  }
+  if (want_dH) {
+    if (!mul_ok(D, p->ldWt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
+    p->off_Wt = L.add(n);
+    if (!mul_ok(p->C, p->ldS, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
+    p->off_dS = L.add(n);
+  }
+  if (want_dW || want_db) {
+    if (!mul_ok(V, p->ldSt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
+    p->off_dSt = L.add(n);
+  }
+  if (want_dW) {
+    if (!mul_ok(D, p->ldSt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
+    p->off_ht = L.add(n);
+  }
+  p->off_tcoef = L.add(N * 4);
+  if (want_dW || want_db) {
+    p->off_head = L.add(V * 4);
+    p->off_next = L.add(p->C * 4);
+  }
+  if (!L.ok) return LLP_EOVERFLOW;
+  // the chunk's contraction tiles must fit grid.x too
+  if (ceil_div(p->C, kTile) * ceil_div(V, kTile) > kMaxRows) return LLP_EOVERFLOW;
+  p->bytes = L.bytes;
+  return LLP_OK;
+}
+
+inline int check_rows(int64_t N, int64_t V, int dtype) {
+  if (!dtype_ok(dtype)) return LLP_EINVAL;
+  if (N < 0 || V < 1) return LLP_EINVAL;
+  if (N > kMaxRows) return LLP_EOVERFLOW;
+  int64_t t;
+  if (!mul_ok(N, V, &t) || !mul_ok(t, esize(dtype), &t)) return LLP_EOVERFLOW;
+  return LLP_OK;
+}
+
+}  // namespace llp

@@ -1,0 +1,216 @@
+"""ctypes binding of ``libllp.so`` with the C ABI's names (include/llp.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. torch provides device memory and the current stream; outputs and
+workspaces that the caller does not pass are allocated here with
+``torch.empty`` (the library itself allocates nothing). There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libllp.so")
+
+LLP_F32, LLP_BF16, LLP_F16 = 0, 1, 2
+LLP_OK, LLP_EINVAL, LLP_EWORKSPACE, LLP_EOVERFLOW, LLP_EHIP = 0, 1, 2, 3, 4
+
+_lib = None
+
+_i64, _int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+# name -> (restype, argtypes), mirroring include/llp.h
+SIGNATURES = {
+    "llp_version": (_int, []),
+    "llp_strerror": (ctypes.c_char_p, [_int]),
+    "linear_logp_chunk_rows": (_i64, [_i64, _i64, _i64]),
+    "linear_logp_num_chunks": (_i64, [_i64, _i64, _i64]),
+    "linear_logp_fwd_workspace_size": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]),
+    "linear_logp_fwd": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "linear_logp_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int, _i64, _int, _int, _int, _int,
+                                              ctypes.POINTER(_sz)]),
+    "linear_logp_bwd": (_int, [_i64, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _int, _vp, _int, _vp, _sz, _vp]),
+    "logp_fwd": (_int, [_i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
+    "logp_bwd": (_int, [_i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
+}
+
+
+class LlpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {llp_strerror(status)} (status {status})")
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m cross_entropy_lm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(st: int, where: str):
+    if st != LLP_OK:
+        raise LlpError(st, where)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def dtype_code(dt) -> int:
+    torch = _torch()
+    codes = {torch.float32: LLP_F32, torch.bfloat16: LLP_BF16, torch.float16: LLP_F16}
+    if dt not in codes:
+        raise TypeError(f"unsupported dtype {dt}")
+    return codes[dt]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _contig(t, name):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def llp_version() -> int:
+    return lib().llp_version()
+
+
+def llp_strerror(status: int) -> str:
+    return lib().llp_strerror(status).decode()
+
+
+def linear_logp_chunk_rows(N: int, V: int, chunk: int = 0) -> int:
+    return lib().linear_logp_chunk_rows(N, V, chunk)
+
+
+def linear_logp_num_chunks(N: int, V: int, chunk: int = 0) -> int:
+    return lib().linear_logp_num_chunks(N, V, chunk)
+
+
+def linear_logp_fwd_workspace_size(N: int, D: int, V: int, dtype: int) -> int:
+    out = _sz(0)
+    _check(lib().linear_logp_fwd_workspace_size(N, D, V, dtype, ctypes.byref(out)),
+           "linear_logp_fwd_workspace_size")
+    return out.value
+
+
+def linear_logp_bwd_workspace_size(N, D, V, dtype, chunk=0, want_dH=True, want_dW=True,
+                                   want_db=False, have_lse=True) -> int:
+    out = _sz(0)
+    _check(lib().linear_logp_bwd_workspace_size(N, D, V, dtype, chunk, int(want_dH), int(want_dW),
+                                                int(want_db), int(have_lse), ctypes.byref(out)),
+           "linear_logp_bwd_workspace_size")
+    return out.value
+
+
+def _workspace(nbytes, workspace, device):
+    if workspace is not None:
+        return workspace
+    return _torch().empty(max(nbytes, 1), dtype=_torch().uint8, device=device)
+
+
+def linear_logp_fwd(h, W, b, targets, logp=None, lse=None, workspace=None, stream=None,
+                    want_lse=True):
+    """logp [N] (and lse [N]) for h [N, D], W [V, D], b [V] or None, targets [N] int64."""
+    torch = _torch()
+    for t, n in ((h, "h"), (W, "W"), (b, "b"), (targets, "targets")):
+        _contig(t, n)
+    N, D = h.shape
+    V = W.shape[0]
+    dt = dtype_code(h.dtype)
+    if logp is None:
+        logp = torch.empty(N, dtype=torch.float32, device=h.device)
+    if lse is None and want_lse:
+        lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    nbytes = linear_logp_fwd_workspace_size(N, D, V, dt)
+    ws = _workspace(nbytes, workspace, h.device)
+    st = lib().linear_logp_fwd(N, D, V, dt, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(logp),
+                               _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "linear_logp_fwd")
+    return logp, lse
+
+
+def linear_logp_bwd(h, W, b, targets, g, lse=None, want_dH=True, want_dW=True, want_db=False,
+                    dW_dtype=None, chunk=0, accumulate=False, dH=None, dW=None, db=None,
+                    workspace=None, stream=None):
+    """(dH, dW, db) for the requested outputs (None for the others).
+
+    ``dW_dtype`` is the dW/db table dtype (torch.float32 by default, or the
+    operand dtype). With ``accumulate`` the caller's dW/db are added into.
+    """
+    torch = _torch()
+    for t, n in ((h, "h"), (W, "W"), (b, "b"), (targets, "targets"), (g, "g"), (lse, "lse")):
+        _contig(t, n)
+    N, D = h.shape
+    V = W.shape[0]
+    dt = dtype_code(h.dtype)
+    tdt = torch.float32 if dW_dtype is None else dW_dtype
+    if want_dH and dH is None:
+        dH = torch.empty((N, D), dtype=h.dtype, device=h.device)
+    if want_dW and dW is None:
+        dW = (torch.zeros if accumulate else torch.empty)((V, D), dtype=tdt, device=h.device)
+    if want_db and db is None:
+        db = (torch.zeros if accumulate else torch.empty)((V,), dtype=tdt, device=h.device)
+    if dW is not None:
+        tdt = dW.dtype
+    elif db is not None:
+        tdt = db.dtype
+    nbytes = linear_logp_bwd_workspace_size(N, D, V, dt, chunk, dH is not None, dW is not None,
+                                            db is not None, lse is not None)
+    ws = _workspace(nbytes, workspace, h.device)
+    st = lib().linear_logp_bwd(N, D, V, dt, chunk, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(g),
+                               _ptr(lse), _ptr(dH), _ptr(dW), dtype_code(tdt), _ptr(db),
+                               int(bool(accumulate)), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream))
+    _check(st, "linear_logp_bwd")
+    return dH, dW, db
+
+
+def logp_fwd(logits, targets, logp=None, lse=None, want_lse=True, stream=None):
+    torch = _torch()
+    _contig(logits, "logits")
+    N, V = logits.shape
+    if logp is None:
+        logp = torch.empty(N, dtype=torch.float32, device=logits.device)
+    if lse is None and want_lse:
+        lse = torch.empty(N, dtype=torch.float32, device=logits.device)
+    st = lib().logp_fwd(N, V, dtype_code(logits.dtype), _ptr(logits), _ptr(targets), _ptr(logp),
+                        _ptr(lse), _stream(stream))
+    _check(st, "logp_fwd")
+    return logp, lse
+
+
+def logp_bwd(logits, targets, g, lse=None, dlogits=None, stream=None):
+    torch = _torch()
+    _contig(logits, "logits")
+    N, V = logits.shape
+    if dlogits is None:
+        dlogits = torch.empty_like(logits)
+    st = lib().logp_bwd(N, V, dtype_code(logits.dtype), _ptr(logits), _ptr(targets), _ptr(g),
+                        _ptr(lse), _ptr(dlogits), _stream(stream))
+    _check(st, "logp_bwd")
+    return dlogits

@@ -1,0 +1,160 @@
+/*
+ * llp.h -- C ABI of the fused linear log-prob library for AMD MI355X (gfx950).
+ *
+ * Operators
+ * ---------
+ * linear_logp: for hidden states h [N, D], a weight W [V, D] (the layout of a
+ * linear layer's weight), an optional bias b [V] and integer targets t [N],
+ *     z      = h W^T + b                      (logits, never stored in memory)
+ *     lse[n] = log sum_v exp(z[n, v])
+ *     logp[n]= z[n, t_n] - lse[n]
+ * and, for an upstream gradient g [N] of logp,
+ *     dlogits = g (onehot(t) - softmax(z))    (recomputed, never stored whole)
+ *     dH = dlogits W,  dW = dlogits^T h (added in place into one table),
+ *     db = sum_n dlogits.
+ * Sources: RL-Kernel issue #261 "Accumulate portable linear_logp backward dW
+ * with FP32 addmm_" (sections "Current production path", "Current
+ * accumulation", "Correctness boundary"); Liger-Kernel PR #1324 "Use direct
+ * FLCE weight-gradient accumulation for FP16, BF16, and FP32" ("Summary",
+ * "Details"); RL-Kernel PR #495 "fused zero-workspace backward for the generic
+ * CUDA fused logp" ("Summary", "Behavior changes").
+ *
+ * logp: the same log-prob and gradient computed from given logits [N, V]
+ * (RL-Kernel PR #495, "Summary" and "Results").
+ *
+ * Conventions (every entry point)
+ * -------------------------------
+ * - Memory: every pointer argument is DEVICE memory on the current HIP device
+ *   unless stated, row-major and contiguous; the caller owns all of it. The
+ *   library allocates nothing: scratch space comes from the caller's
+ *   `workspace`, sized by the matching *_workspace_size query.
+ * - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *   stream) and the call returns without waiting for it. The library keeps no
+ *   mutable global state; calls on different streams must not share output
+ *   or workspace buffers.
+ * - dtypes: operands h, W, b, logits, dH and dlogits use `dtype` (LLP_F32,
+ *   LLP_BF16 or LLP_F16). logp, lse and g are float32. Targets are int64.
+ *   Arithmetic accumulates in float32; 16-bit results are rounded to nearest
+ *   even.
+ * - Targets outside [0, V) (for example -100) are not errors: that row gets
+ *   logp = +0 and an all +0 gradient row (RL-Kernel PR #495, "Behavior
+ *   changes"). lse is still reported for it.
+ * - Errors: a nonzero llp_status is returned. All argument checks happen
+ *   before any HIP call, so on LLP_EINVAL / LLP_EWORKSPACE / LLP_EOVERFLOW
+ *   nothing was enqueued and no output was touched. LLP_EHIP reports a failed
+ *   kernel launch (hipGetLastError); outputs are then unspecified.
+ * - Sizes are int64 everywhere; element offsets are computed in 64 bits
+ *   (N * V may exceed 2^31; RL-Kernel PR #495 review of the INT_MAX loop
+ *   counters).
+ */
+#ifndef LLP_H
+#define LLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef LLP_API
+#define LLP_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LLP_F32 = 0, LLP_BF16 = 1, LLP_F16 = 2 } llp_dtype;
+
+typedef enum {
+  LLP_OK = 0,
+  LLP_EINVAL = 1,     /* bad shape, NULL required pointer, bad dtype/flag combination */
+  LLP_EWORKSPACE = 2, /* workspace smaller than the query's answer, or NULL when nonzero is needed */
+  LLP_EOVERFLOW = 3,  /* an element count or byte size does not fit int64 / size_t */
+  LLP_EHIP = 4        /* a HIP launch failed */
+} llp_status;
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+LLP_API int llp_version(void);
+
+/* Static message for a status code; never NULL. */
+LLP_API const char* llp_strerror(int status);
+
+/*
+ * Tokens per backward chunk. chunk > 0 is used as given (clamped to N);
+ * chunk <= 0 selects floor(2^24 / V) (RL-Kernel issue #261, "Static traffic
+ * model"), clamped to [1, max(N, 1)]. Returns -1 on N < 0 or V < 1.
+ */
+LLP_API int64_t linear_logp_chunk_rows(int64_t N, int64_t V, int64_t chunk);
+
+/* Number of backward chunks, ceil(N / chunk_rows); 0 for N = 0; -1 on bad input. */
+LLP_API int64_t linear_logp_num_chunks(int64_t N, int64_t V, int64_t chunk);
+
+/*
+ * Workspace bytes linear_logp_fwd needs for these shapes (0 for N = 0).
+ * Returns a status; *bytes is written on LLP_OK.
+ */
+LLP_API int linear_logp_fwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, size_t* bytes);
+
+/*
+ * Forward. h [N, D], W [V, D], b [V] or NULL, targets [N]  ->  logp [N]
+ * (required) and lse [N] (NULL to skip). lse is the residual the backward
+ * consumes. N = 0 enqueues nothing. D >= 1, V >= 1.
+ */
+LLP_API int linear_logp_fwd(int64_t N, int64_t D, int64_t V, int dtype,
+                    const void* h, const void* W, const void* b, const int64_t* targets,
+                    float* logp, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes linear_logp_bwd needs. It depends on which outputs are
+ * requested (want_* nonzero) and on whether the caller passes lse
+ * (have_lse nonzero); unrequested outputs add nothing.
+ */
+LLP_API int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
+                                   int want_dH, int want_dW, int want_db, int have_lse,
+                                   size_t* bytes);
+
+/*
+ * Backward, over ceil(N / C) chunks of C = linear_logp_chunk_rows(N, V, chunk)
+ * tokens, in increasing chunk order (RL-Kernel issue #261, "Current
+ * accumulation"; Liger-Kernel PR #1324, "Details").
+ *
+ * g [N]: upstream gradient of logp (float32). lse [N]: the forward's lse, or
+ * NULL to recompute it here.
+ * dH [N, D] (dtype) or NULL: written once per row, no chunk rounding.
+ * dW [V, D] or NULL, of dW_dtype (LLP_F32, or the operand dtype): each chunk's
+ *   dlogits^T h is added into this table in place, with no [V, D] temporary.
+ * db [V] or NULL, same dtype as dW_dtype; requires b != NULL.
+ * accumulate = 0: dW and db are first set to +0 (the zero-initialised table
+ *   of RL-Kernel issue #261, "Correctness boundary"), so that g = 0 gives +0
+ *   with a clear sign bit; accumulate = 1: chunks are added into the caller's
+ *   values (gradient accumulation across calls).
+ * NULL outputs are never read or written. N = 0 writes only the zero fill of
+ * dW/db (when accumulate = 0).
+ * Deterministic: the same inputs give bit-identical outputs on every call.
+ */
+LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
+                    const void* h, const void* W, const void* b, const int64_t* targets,
+                    const float* g, const float* lse,
+                    void* dH, void* dW, int dW_dtype, void* db, int accumulate,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Logits-only forward (RL-Kernel PR #495): logits [N, V] of dtype ->
+ * logp [N] (required), lse [N] (NULL to skip). One read of the logits.
+ */
+LLP_API int logp_fwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t* targets,
+             float* logp, float* lse, void* stream);
+
+/*
+ * Logits-only backward: dlogits [N, V] (dtype) = g (onehot - softmax). With
+ * lse from logp_fwd the logits are read once; lse = NULL recomputes it per
+ * row (two reads). dlogits may alias logits (in-place gradient): each element
+ * is read before it is written by the same thread.
+ */
+LLP_API int logp_bwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t* targets,
+             const float* g, const float* lse, void* dlogits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLP_H */

@@ -1,0 +1,136 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+symbol include/llp.h declares, and every argument check returns its status
+before any HIP call (nothing here launches a kernel)."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from cross_entropy_lm_amd import llp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "page_figures.json")))
+
+F32, BF16, F16 = llp.LLP_F32, llp.LLP_BF16, llp.LLP_F16
+FAKE = 0x10000  # a non-null pointer value that is never dereferenced: every call below fails validation first
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "llp.h")).read()
+    return re.findall(r"LLP_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) == 10
+    L = llp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in llp.SIGNATURES, n
+    assert llp.llp_version() == 100
+    assert llp.llp_strerror(llp.LLP_EWORKSPACE) == "workspace too small"
+    assert llp.llp_strerror(99) == "unknown status"
+
+
+def test_default_chunk_policy_matches_the_pages():
+    tm = GOLD["traffic_model"]
+    assert llp.linear_logp_chunk_rows(tm["N"], tm["V"], 0) == tm["chunk_rows"]
+    assert llp.linear_logp_num_chunks(tm["N"], tm["V"], 0) == tm["chunks"]
+    # floor(2^24 / 151936) = 110 rows, the 2^24-element row of RL-Kernel PR #495's sweep
+    sweep = GOLD["chunk_sweep_rows"]
+    assert llp.linear_logp_chunk_rows(32768, sweep["V"], 0) == sweep["elems_to_rows"][str(1 << 24)]
+    assert llp.linear_logp_chunk_rows(100, 1 << 25, 0) == 1  # V > 2^24 -> one row per chunk
+    assert llp.linear_logp_chunk_rows(10, 1024, 0) == 10  # clamped to N
+    assert llp.linear_logp_chunk_rows(0, 1024, 0) == 1
+    assert llp.linear_logp_num_chunks(0, 1024, 0) == 0
+    assert llp.linear_logp_num_chunks(256, 1024, 64) == 4
+    assert llp.linear_logp_num_chunks(8192, 151936, 0) == 75
+    assert llp.linear_logp_chunk_rows(-1, 10, 0) == -1
+    assert llp.linear_logp_chunk_rows(5, 0, 0) == -1
+
+
+def test_workspace_queries():
+    f = llp.linear_logp_fwd_workspace_size
+    assert f(0, 128, 1024, F32) == 0
+    assert f(256, 128, 1024, F32) >= 2 * 4 * 256 * 8 + 256 * 4
+    b = llp.linear_logp_bwd_workspace_size
+    assert b(256, 128, 1024, F32, 64, False, False, False, True) == 0
+    full = b(16384, 4096, 32000, BF16, 2048, True, True, False, True)
+    only_dh = b(16384, 4096, 32000, BF16, 2048, True, False, False, True)
+    only_dw = b(16384, 4096, 32000, BF16, 2048, False, True, False, True)
+    no_lse = b(16384, 4096, 32000, BF16, 2048, True, True, False, False)
+    assert only_dh < full and only_dw < full and no_lse > full
+    # chunk workspace: W^T, dlogits and dlogits^T in bf16 plus h^T of one chunk
+    expect = 32000 * 4096 * 2 + 2048 * 32000 * 2 * 2 + 4096 * 2048 * 2
+    assert expect <= full < expect + (1 << 20)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 128, 1024, F32), llp.LLP_EINVAL),
+    ((4, 0, 1024, F32), llp.LLP_EINVAL),
+    ((4, 128, 0, F32), llp.LLP_EINVAL),
+    ((4, 128, 1024, 7), llp.LLP_EINVAL),
+    ((1 << 31, 128, 1024, F32), llp.LLP_EOVERFLOW),
+    ((4, 1 << 23, 1024, F32), llp.LLP_EOVERFLOW),
+    ((1 << 30, 1 << 22, 1 << 30, BF16), llp.LLP_EOVERFLOW),
+])
+def test_fwd_shape_errors(args, status):
+    out = ctypes.c_size_t(0)
+    assert llp.lib().linear_logp_fwd_workspace_size(*args, ctypes.byref(out)) == status
+    N, D, V, dt = args
+    st = llp.lib().linear_logp_fwd(N, D, V, dt, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == status
+
+
+def test_fwd_pointer_and_workspace_errors():
+    L = llp.lib()
+    N, D, V = 256, 128, 1024
+    need = llp.linear_logp_fwd_workspace_size(N, D, V, F32)
+    for null in range(4):  # h, W, targets, logp are required
+        p = [FAKE] * 4
+        p[null] = None
+        st = L.linear_logp_fwd(N, D, V, F32, p[0], p[1], None, p[2], p[3], None, FAKE, need, None)
+        assert st == llp.LLP_EINVAL
+    assert L.linear_logp_fwd(N, D, V, F32, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, need - 1, None) \
+        == llp.LLP_EWORKSPACE
+    assert L.linear_logp_fwd(N, D, V, F32, FAKE, FAKE, None, FAKE, FAKE, None, None, need, None) \
+        == llp.LLP_EWORKSPACE
+    # N = 0 is a no-op that touches nothing, even with null pointers
+    assert L.linear_logp_fwd(0, D, V, F32, None, None, None, None, None, None, None, 0, None) == llp.LLP_OK
+
+
+def _bwd(N=256, D=128, V=1024, dt=F32, chunk=64, h=FAKE, W=FAKE, b=FAKE, t=FAKE, g=FAKE, lse=FAKE,
+         dH=FAKE, dW=FAKE, tdt=F32, db=FAKE, acc=0, ws=FAKE, nbytes=1 << 40):
+    return llp.lib().linear_logp_bwd(N, D, V, dt, chunk, h, W, b, t, g, lse, dH, dW, tdt, db, acc, ws,
+                                     nbytes, None)
+
+
+def test_bwd_argument_errors():
+    E = llp.LLP_EINVAL
+    assert _bwd(N=-1) == E
+    assert _bwd(D=0) == E
+    assert _bwd(V=0) == E
+    assert _bwd(dt=3) == E
+    assert _bwd(acc=2) == E
+    assert _bwd(tdt=F16) == E          # table dtype must be fp32 or the operand dtype
+    assert _bwd(dt=BF16, tdt=F16) == E
+    assert _bwd(b=None) == E           # db requested without a bias
+    assert _bwd(h=None) == E
+    assert _bwd(W=None) == E
+    assert _bwd(t=None) == E
+    assert _bwd(g=None) == E
+    need = llp.linear_logp_bwd_workspace_size(256, 128, 1024, F32, 64, True, True, True, True)
+    assert _bwd(nbytes=need - 1) == llp.LLP_EWORKSPACE
+    assert _bwd(ws=None, nbytes=need) == llp.LLP_EWORKSPACE
+    assert _bwd(N=1 << 31) == llp.LLP_EOVERFLOW
+
+
+def test_header_documents_each_entry_point():
+    text = open(os.path.join(ROOT, "include", "llp.h")).read()
+    assert "RL-Kernel issue #261" in text and "Liger-Kernel PR #1324" in text and "RL-Kernel PR #495" in text
+    for n in declared_symbols():
+        i = text.index(n + "(")
+        assert "*/" in text[max(0, i - 1500):i], n  # a comment precedes every declaration
