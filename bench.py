@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused linear log-prob on one MI355X.
+
+Default workload: linear_logp forward + backward at N = 16384 tokens, D = 4096,
+V = 32000, bf16 operands, 2048-token chunks, FP32 dW table, no bias, mean-loss
+upstream g = -1/N (the fused linear cross-entropy benchmark of Liger-Kernel
+PR #1324, "Benchmark results"). A step is one linear_logp_fwd + one
+linear_logp_bwd (dH and dW, including the table's zero fill) through the C ABI
+on synthetic device-resident inputs. Other workloads (--workload) are
+parity-test shapes and the logits-only log-prob.
+
+Prints ONE JSON line (throughput, roofline of the dominant kernel from live
+per-kernel HIP-event timing, and the FP64 oracle timed on a bounded sample on
+the host cores). Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from cross_entropy_lm_amd import accounting as A  # noqa: E402
+
+# MI355X published peaks (dense): bf16/fp16 MFMA 2.5 PFLOP/s, fp32 MFMA 157.3
+# TFLOP/s, HBM3E 8 TB/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "fwd+bwd tokens/s linear_logp N16384 D4096 V32000 bf16; % MFMA peak"
+# Liger FLCE BF16 at this workload (Liger-Kernel PR #1324, "Full all-dtype
+# comparison"): another machine's figure, context only.
+PAGES_TOKENS_PER_S = 18263.8
+
+WORKLOADS = {w.name: w for w in [synth.FLCE, synth.FLCE_F16, synth.FLCE_F32, synth.RL_DEFAULT,
+                                 synth.BIAS_BIGV, synth.TINY, synth.LOGITS]}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "cross_entropy_lm_amd", "csrc"))):
+        with open(os.path.join(ROOT, "cross_entropy_lm_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# ----------------------------------------------------------------------------- linear
+def run_linear(w, args, torch, llp):
+    dev = torch.device("cuda:0")
+    chunk = args.chunk if args.chunk is not None else w.chunk
+    tdt = torch.float32 if args.table == "f32" else {"bf16": torch.bfloat16, "f16": torch.float16,
+                                                      "f32": torch.float32}[w.dtype]
+    log(f"generating {w.name} on the device")
+    d = synth.make_linear_t(w, dev)
+    N, D, V = w.N, w.D, w.V
+    op_dt = llp.dtype_code(d["h"].dtype)
+    C = llp.linear_logp_chunk_rows(N, V, chunk)
+    K = llp.linear_logp_num_chunks(N, V, chunk)
+    logp = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    dH = torch.empty((N, D), dtype=d["h"].dtype, device=dev)
+    dW = torch.empty((V, D), dtype=tdt, device=dev)
+    db = torch.empty((V,), dtype=tdt, device=dev) if w.bias else None
+    ws_f = torch.empty(max(1, llp.linear_logp_fwd_workspace_size(N, D, V, op_dt)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, llp.linear_logp_bwd_workspace_size(N, D, V, op_dt, chunk, True, True, w.bias, True)),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        llp.linear_logp_fwd(d["h"], d["W"], d["b"], d["t"], logp=logp, lse=lse, workspace=ws_f)
+        llp.linear_logp_bwd(d["h"], d["W"], d["b"], d["t"], d["g"], lse, True, True, w.bias, chunk=chunk,
+                            dH=dH, dW=dW, db=db, workspace=ws_b)
+
+    step()
+    torch.cuda.synchronize()
+
+    # correctness gate before timing (and the CPU baseline on the same sample)
+    cpu = None
+    if not args.no_gate or not args.no_cpu_baseline:
+        cpu = oracle_sample(w, args, logp, dH)
+
+    log(f"warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    llp.llp_trace_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    llp.llp_trace_enable(False)
+    tr = llp.llp_trace_read()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    flops = A.linear_fwd_bwd_flops(N, D, V)
+    per_launch_flops = {
+        "fwd_lse": 2 * N * V * D,
+        "dlogits": 2 * N * V * D / K,
+        "dh_dw": 4 * N * V * D / K,
+    }
+    kernels = {}
+    for k, (tms, cnt) in tr.items():
+        if cnt == 0:
+            continue
+        kernels[k] = {"ms_per_step": tms / args.steps, "launches_per_step": cnt / args.steps,
+                      "avg_launch_ms": tms / cnt}
+        if k in per_launch_flops:
+            kernels[k]["tflops"] = per_launch_flops[k] / (tms / cnt * 1e-3) / 1e12
+    mfma = {k: v for k, v in kernels.items() if k in per_launch_flops}
+    dom = max(mfma, key=lambda k: mfma[k]["ms_per_step"])
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = mfma[dom]["tflops"]
+    traffic = traffic_from_profiles(dom, w.name)
+    tokens_s = A.tokens_per_s(N, ms)
+    out = {
+        "metric": METRIC if w.name == "flce_bf16" else f"fwd+bwd tokens/s linear_logp {w.name}",
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": tokens_s / PAGES_TOKENS_PER_S if w.name == "flce_bf16" and args.table == "f32" else None,
+        "vs_baseline_ref": "Liger FLCE BF16 18263.8 tokens/s (Liger-Kernel PR #1324; other hardware, context)",
+        "dtype": w.dtype,
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": {"workload": w.name, "N": N, "D": D, "V": V, "chunk": C, "chunks": K,
+                   "bias": w.bias, "g": w.g, "dW_table": args.table, "outputs": "logp,lse,dH,dW" +
+                   (",db" if w.bias else "")},
+        "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / (peak * 1e12),
+        "pct_mfma_peak_model_flops": 100.0 * A.linear_model_flops(N, D, V) / (ms * 1e-3) / (peak * 1e12),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic},
+        "kernels": kernels,
+    }
+    if cpu is not None and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu
+    return out
+
+
+def oracle_sample(w, args, logp, dH):
+    """FP64 oracle forward + backward (logp, dH, dW) on the first S tokens,
+    timed on the host cores; the GPU's logp and dH rows are gated against it."""
+    from oracle import linear_logp as O
+
+    S = min(args.cpu_sample_tokens, w.N)
+    rows = np.arange(S)
+    log(f"oracle sample: {S} tokens (host generation first)")
+    host = synth.make_linear_np(w, rows=rows)
+    t0 = time.perf_counter()
+    rlogp, _ = O.linear_logp_fwd(host["h64"], host["W64"], host["b64"], host["t"])
+    rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True, True,
+                                      w.bias)
+    dt = time.perf_counter() - t0
+    gl = logp[:S].double().cpu().numpy()
+    gh = dH[:S].double().cpu().numpy()
+    tl = {"f32": (1e-5, 5e-4)}.get(w.dtype, (5e-3, 5e-2))
+    tg = {"f32": (1e-5, 5e-4)}.get(w.dtype, (5e-4, 2e-2))
+    ok_l = np.all(np.abs(gl - rlogp) <= tl[0] + tl[1] * np.abs(rlogp))
+    ok_h = np.all(np.abs(gh - rdH) <= tg[0] + tg[1] * np.abs(rdH))
+    if not args.no_gate and not (ok_l and ok_h):
+        raise SystemExit(f"correctness gate failed: logp ok={ok_l} dH ok={ok_h}")
+    log(f"gate ok (logp, dH on {S} tokens); oracle {dt:.1f} s")
+    return {"value": S / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {S} tokens of {w.name}: FP64 numpy oracle forward + backward (logp, dH, dW)"
+                      f"{' + db' if w.bias else ''}, {dt:.2f} s"}
+
+
+# ----------------------------------------------------------------------------- logits only
+def run_logits(w, args, torch, llp):
+    from oracle import linear_logp as O
+
+    dev = torch.device("cuda:0")
+    log(f"generating {w.name} on the device")
+    d = synth.make_logits_t(w, dev)
+    N, V = w.N, w.V
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    logp = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    dl = torch.empty_like(d["logits"])
+
+    def step():
+        llp.logp_fwd(d["logits"], d["t"], logp=logp, lse=lse)
+        llp.logp_bwd(d["logits"], d["t"], d["g"], lse, dlogits=dl)
+
+    step()
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base
+    S = min(args.cpu_sample_tokens, 64)
+    rows = np.arange(S)
+    host = synth.make_logits_rows_np(w, rows)
+    t0 = time.perf_counter()
+    rlogp, _ = O.logp_fwd(host["logits64"], host["t"])
+    rd = O.logp_bwd(host["logits64"], host["t"], host["g64"])
+    dt = time.perf_counter() - t0
+    gl = logp[:S].double().cpu().numpy()
+    gd = dl[:S].double().cpu().numpy()
+    if not args.no_gate:
+        if not (np.all(np.abs(gl - rlogp) <= 5e-3 + 5e-2 * np.abs(rlogp))
+                and np.all(np.abs(gd - rd) <= 5e-4 + 2e-2 * np.abs(rd))):
+            raise SystemExit("correctness gate failed (logits-only)")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    llp.llp_trace_enable(True)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    llp.llp_trace_enable(False)
+    tr = llp.llp_trace_read()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = {"rows_fwd": N * V * 2, "rows_bwd": 2 * N * V * 2}
+    kernels = {}
+    for k, (tms, cnt) in tr.items():
+        if cnt:
+            kernels[k] = {"ms_per_step": tms / args.steps, "avg_launch_ms": tms / cnt,
+                          "GBps": nbytes[k] / (tms / cnt * 1e-3) / 1e9}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    total = A.logits_only_bytes(N, V, 2)
+    return {
+        "metric": "fwd+bwd logits-only logp N32768 V151936 bf16; GB/s",
+        "value": total / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded counter-based generator)",
+        "config": {"workload": w.name, "N": N, "V": V, "peak_extra_bytes": peak_extra},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBps"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": kernels[dom]["GBps"] / PEAK_HBM_GBS,
+                     "traffic": traffic_from_profiles(dom, w.name)},
+        "kernels": kernels,
+        "cpu_baseline": {"value": S * V * 3 * 2 / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": f"first {S} rows: FP64 numpy oracle logp + dlogits, {dt:.2f} s"},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="flce_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--chunk", type=int, default=None, help="tokens per backward chunk (default: the workload's)")
+    ap.add_argument("--table", default="f32", choices=["f32", "op"], help="dW table dtype")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gate", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a "
+              "design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from cross_entropy_lm_amd import llp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    llp.lib()  # fail loudly if the HIP library is missing
+    w = WORKLOADS[args.workload]
+    if isinstance(w, synth.LogitsWorkload):
+        out = run_logits(w, args, torch, llp)
+    else:
+        out = run_linear(w, args, torch, llp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -113,40 +113,38 @@ __global__ void db_accum_kernel(const T* __restrict__ dSt, int64_t ldSt, int64_t
   }
 }
 
-// One thread per chunk token; the chunk's targets are staged through LDS in
-// slices. A valid token with no earlier valid token of the same target writes
-// head[t]; every valid token writes next[] (the first later valid token with
-// the same target, or -1). No atomics: the lists are in token order.
+// One wave per chunk token n: the 64 lanes split the scan over the chunk, then
+// a valid token with no earlier valid token of the same target writes
+// head[t], and every valid token writes next[n] (the first later valid token
+// with the same target, or -1). No atomics: the lists are in token order.
 __global__ void target_lists_kernel(const int64_t* __restrict__ targets, const float* __restrict__ g,
                                     int64_t tok0, int64_t C, int64_t V, int32_t* __restrict__ head,
                                     int32_t* __restrict__ next) {
-  constexpr int kSlice = 2048;
-  __shared__ int32_t st[kSlice];  // target, or -1 for an invalid token
-  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t t = -1;
-  const bool mine = n < C && tok_valid(targets, g, tok0 + n, V, t);
-  bool first = true;
-  int64_t nxt = -1;
-  for (int64_t base = 0; base < C; base += kSlice) {
-    const int64_t len = min((int64_t)kSlice, C - base);
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < len; i += blockDim.x) {
-      int64_t tj;
-      st[i] = tok_valid(targets, g, tok0 + base + i, V, tj) ? (int32_t)tj : -1;
-    }
-    __syncthreads();
-    if (mine) {
-      for (int64_t i = 0; i < len; ++i) {
-        const int64_t j = base + i;
-        if (st[i] != (int32_t)t) continue;
-        if (j < n) first = false;
-        if (j > n && nxt < 0) nxt = j;
-      }
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (n >= C) return;  // uniform per wave
+  int64_t t;
+  if (!tok_valid(targets, g, tok0 + n, V, t)) return;
+  bool earlier = false;
+  int64_t nxt = INT64_MAX;
+  for (int64_t j = lane; j < C; j += 64) {
+    int64_t tj;
+    if (j != n && tok_valid(targets, g, tok0 + j, V, tj) && tj == t) {
+      if (j < n) earlier = true;
+      else if (j < nxt) nxt = j;
     }
   }
-  if (mine) {
-    next[n] = (int32_t)nxt;
-    if (first) head[t] = (int32_t)n;
+  // every lane takes part in every shuffle (no short-circuit around them)
+  int any_earlier = earlier ? 1 : 0;
+  for (int o = 32; o > 0; o >>= 1) {
+    any_earlier |= __shfl_xor(any_earlier, o);
+    const int64_t other = __shfl_xor(nxt, o);
+    nxt = other < nxt ? other : nxt;
+  }
+  earlier = any_earlier != 0;
+  if (lane == 0) {
+    next[n] = nxt == INT64_MAX ? -1 : (int32_t)nxt;
+    if (!earlier) head[t] = (int32_t)n;
   }
 }
 
@@ -231,7 +229,7 @@ hipError_t launch_db_accum(int dt, const void* dSt, int64_t ldSt, int64_t V, int
 hipError_t launch_target_lists(const int64_t* targets, const float* g, int64_t tok0, int64_t C,
                                int64_t V, int32_t* head, int32_t* next, hipStream_t s) {
   if (C == 0) return hipSuccess;
-  target_lists_kernel<<<(unsigned)((C + 255) / 256), 256, 0, s>>>(targets, g, tok0, C, V, head, next);
+  target_lists_kernel<<<(unsigned)((C + 3) / 4), 256, 0, s>>>(targets, g, tok0, C, V, head, next);
   return hipGetLastError();
 }
 

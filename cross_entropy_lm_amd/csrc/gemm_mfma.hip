@@ -7,10 +7,12 @@
 //   dW += dlogits^T h:                      A = dlogits^T [V, C], B = h^T [D, C]
 // (the transposed operands are produced in the caller's workspace).
 //
-// Tile: 256 x 256 outputs per workgroup of 256 threads (4 waves in a 2 x 2
-// grid, each wave 128 x 128 = 4 x 4 blocks of the 32x32 MFMA). K advances 128
-// bytes per stage (64 bf16/fp16 or 32 fp32); the two operand tiles of a stage
-// are staged through LDS with a 16-byte row pad, double-buffered (144 KiB).
+// Tile: 256 x 256 outputs per workgroup of kWaveM x kWaveN waves (each wave
+// owns MI x NI blocks of the 32x32 MFMA). K advances 128 bytes per stage (64
+// bf16/fp16 or 32 fp32); the two operand tiles of a stage are staged through
+// LDS with a 16-byte row pad, double-buffered (144 KiB). Workgroups are
+// remapped so that each XCD (own L2) works on a contiguous range of tiles,
+// taken in groups of kGroupM tiles along M.
 //
 // MFMA operand layout: for the 32x32 instructions lane l supplies row (l % 32)
 // of A (and column (l % 32) of B) and a group of K values selected by l / 32;
@@ -20,7 +22,7 @@
 // The epilogues implement, on the fp32 tile of logits z (vocab rows x token
 // columns):
 //   LSE_PARTIAL: per token, m = max_v z and s = sum_v exp(z - m) over the wave's
-//     128 vocab rows (the online max / sum-exp of RL-Kernel PR #495, "Summary",
+//     rows of the tile (the online max / sum-exp of RL-Kernel PR #495, "Summary",
 //     done per tile), plus the target logit z[t]. exp/log use the hardware
 //     base-2 instructions with z scaled by log2(e).
 //   DLOGITS: dlogits = g [v == t] - g exp(z - lse) (RL-Kernel PR #495,
@@ -48,7 +50,12 @@ constexpr int kPitch = kRowBytes + 16;  // LDS row pitch: the pad puts 8 consecu
 constexpr int kStageBytes = (kTileM + kTileN) * kPitch;
 constexpr int kLdsBytes = 2 * kStageBytes;
 constexpr int kLoadsPerThread = kTileM * (kRowBytes / 16) / kThreads;  // 16-byte chunks per operand
+constexpr int MI = kTileM / (32 * kWaveM);  // 32x32 blocks per wave along M
+constexpr int NI = kTileN / (32 * kWaveN);  // ... along N
+constexpr int kWaveRowsM = 32 * MI;
+constexpr int kWaveColsN = 32 * NI;
 static_assert(kTileM == kTileN, "loader assumes square tiles");
+typedef f32x16 Acc[MI][NI];
 
 template <typename T> struct ET;
 template <> struct ET<__bf16> { static constexpr int per16 = 8; };
@@ -99,14 +106,22 @@ __device__ __forceinline__ u32x4 load_chunk(const T* base, int64_t ld, int64_t r
   return v;
 }
 
-// Tile order: groups of 8 tiles along M, N-major inside a group, so that the
-// workgroups running together share A rows and B rows in L2.
+// Block -> tile. The hardware deals workgroups round-robin to the XCDs
+// (block b runs on XCD b % 8); remap so that XCD x takes the contiguous tile
+// range [x * T / 8, (x + 1) * T / 8), then walk that range in groups of
+// kGroupM tiles along M, N-major inside a group, so the workgroups resident on
+// one XCD share A rows and B rows in its L2.
+__device__ __forceinline__ int xcd_remap(int b, int T) {
+  const int per = T / kXcds, rem = T % kXcds;
+  const int x = b % kXcds, local = b / kXcds;
+  return x * per + min(x, rem) + local;
+}
+
 __device__ __forceinline__ void tile_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int G = 8;
-  const int group_size = G * tiles_n;
+  const int group_size = kGroupM * tiles_n;
   const int group = id / group_size;
-  const int first = group * G;
-  const int gm = min(tiles_m - first, G);
+  const int first = group * kGroupM;
+  const int gm = min(tiles_m - first, kGroupM);
   const int in = id - group * group_size;
   tm = first + in % gm;
   tn = in / gm;
@@ -120,34 +135,34 @@ __device__ __forceinline__ float ld_f32(const T* p, int64_t i) {
 struct Frag {
   int lane, wm, wn;
   __device__ inline int row(int mi, int r) const {  // row inside the 256-row tile
-    return wm * 128 + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    return wm * kWaveRowsM + mi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
   }
-  __device__ inline int col(int ni) const { return wn * 128 + ni * 32 + (lane & 31); }
+  __device__ inline int col(int ni) const { return wn * kWaveColsN + ni * 32 + (lane & 31); }
 };
 
 // ---------------------------------------------------------------- epilogues
 template <typename T>
-__device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, f32x16 (&acc)[4][4], int tm, int64_t m0,
+__device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, int tm, int64_t m0,
                                 int64_t n0, const Frag& f) {
   const EpiParams& e = p.ep;
   const T* bias = static_cast<const T*>(e.bias);
-  int64_t tgt[4];
-  float mx[4];
+  int64_t tgt[NI];
+  float mx[NI];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < NI; ++ni) {
     const int64_t n = n0 + f.col(ni);
     tgt[ni] = (n < p.N) ? e.targets[e.tok0 + n] : -1;
     mx[ni] = -INFINITY;
   }
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t v = m0 + f.row(mi, r);
       const bool vv = v < p.M;
       const float bv = (bias != nullptr && vv) ? ld_f32(bias, v) : 0.0f;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+      for (int ni = 0; ni < NI; ++ni) {
         const float z = vv ? acc[mi][ni][r] + bv : -INFINITY;
         acc[mi][ni][r] = z;
         mx[ni] = fmaxf(mx[ni], z);
@@ -155,22 +170,22 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, f32x16 (&a
       }
     }
   }
-  float m2[4], s[4];
+  float m2[NI], s[NI];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < NI; ++ni) {
     mx[ni] = fmaxf(mx[ni], __shfl_xor(mx[ni], 32));
     m2[ni] = mx[ni] * kLog2e;
     s[ni] = 0.0f;
   }
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < NI; ++ni)
         s[ni] += __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2[ni]));
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < NI; ++ni) {
     float sv = s[ni] + __shfl_xor(s[ni], 32);
     if (mx[ni] == -INFINITY) sv = 0.0f;  // this wave's rows all lie past V
     const int64_t n = n0 + f.col(ni);
@@ -180,18 +195,18 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, f32x16 (&a
 }
 
 template <typename T>
-__device__ __forceinline__ void epi_dlogits(const GemmProblem& p, f32x16 (&acc)[4][4], int64_t m0,
+__device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int64_t m0,
                                             int64_t n0, const Frag& f) {
   const EpiParams& e = p.ep;
   const T* bias = static_cast<const T*>(e.bias);
   T* dS = static_cast<T*>(e.dS);
   T* dSt = static_cast<T*>(e.dSt);
   const float inv = e.scales[e.chunk].y;
-  int64_t tgt[4];
-  float gv[4], gs[4], l2[4];
-  bool rv[4];
+  int64_t tgt[NI];
+  float gv[NI], gs[NI], l2[NI];
+  bool rv[NI];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < NI; ++ni) {
     const int64_t n = n0 + f.col(ni);
     const bool nv = n < p.N;
     const int64_t tok = e.tok0 + n;
@@ -202,14 +217,14 @@ __device__ __forceinline__ void epi_dlogits(const GemmProblem& p, f32x16 (&acc)[
     l2[ni] = nv ? e.lse[tok] * kLog2e : 0.0f;
   }
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t v = m0 + f.row(mi, r);
       if (v >= p.M) continue;
       const float bv = (bias != nullptr) ? ld_f32(bias, v) : 0.0f;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+      for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
         if (n >= p.N) continue;
         const float z = acc[mi][ni][r] + bv;
@@ -237,14 +252,14 @@ __device__ __forceinline__ bool token_valid(const EpiParams& e, int64_t tok, int
 
 // dH rows of the chunk: out[m, :] = s C[m, :] + tcoef[m] W[t_m, :].
 template <typename T>
-__device__ __forceinline__ void epi_store(const GemmProblem& p, f32x16 (&acc)[4][4], int64_t m0,
+__device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_t m0,
                                           int64_t n0, const Frag& f) {
   const EpiParams& e = p.ep;
   T* out = static_cast<T*>(e.out);
   const T* W = static_cast<const T*>(e.W);
   const float sc = e.scales[e.chunk].x;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t m = m0 + f.row(mi, r);
@@ -254,7 +269,7 @@ __device__ __forceinline__ void epi_store(const GemmProblem& p, f32x16 (&acc)[4]
       const float c = valid ? e.tcoef[e.tok0 + m] : 0.0f;
       const T* wrow = W + (valid ? t : 0) * e.ldW;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+      for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
         if (n < p.N) {
           float val = acc[mi][ni][r] * sc;
@@ -268,21 +283,21 @@ __device__ __forceinline__ void epi_store(const GemmProblem& p, f32x16 (&acc)[4]
 // dW rows: table[v, :] += s C[v, :] + sum, in token order, of tcoef[n] h[n, :]
 // over the chunk's valid tokens with target v.
 template <typename T, typename TT>
-__device__ __forceinline__ void epi_accum_t(const GemmProblem& p, f32x16 (&acc)[4][4], int64_t m0,
+__device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int64_t m0,
                                             int64_t n0, const Frag& f) {
   const EpiParams& e = p.ep;
   TT* tab = static_cast<TT*>(e.out);
   const T* h = static_cast<const T*>(e.h);
   const float sc = e.scales[e.chunk].x;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t m = m0 + f.row(mi, r);
       if (m >= p.M) continue;
-      float val[4];
+      float val[NI];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) val[ni] = acc[mi][ni][r] * sc;
+      for (int ni = 0; ni < NI; ++ni) val[ni] = acc[mi][ni][r] * sc;
       // head entries of targets absent from this chunk are stale: accept only
       // an index of this chunk whose token is valid and has target m
       int32_t j = e.head[m];
@@ -293,7 +308,7 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, f32x16 (&acc)[
           const float c = e.tcoef[e.tok0 + j];
           const T* hrow = h + (e.tok0 + j) * e.ldh;
 #pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
+          for (int ni = 0; ni < NI; ++ni) {
             const int64_t n = n0 + f.col(ni);
             if (n < p.N) val[ni] = fmaf(c, ld_f32(hrow, n), val[ni]);
           }
@@ -301,7 +316,7 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, f32x16 (&acc)[
         }
       }
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+      for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
         if (n < p.N) {
           TT* q = tab + m * e.ldo + n;
@@ -312,7 +327,7 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, f32x16 (&acc)[
 }
 
 template <typename T>
-__device__ __forceinline__ void epi_accum(const GemmProblem& p, f32x16 (&acc)[4][4], int64_t m0, int64_t n0,
+__device__ __forceinline__ void epi_accum(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
                           const Frag& f) {
   if (p.ep.out_dt == DT_F32)
     epi_accum_t<T, float>(p, acc, m0, n0, f);
@@ -321,41 +336,53 @@ __device__ __forceinline__ void epi_accum(const GemmProblem& p, f32x16 (&acc)[4]
 }
 
 // ---------------------------------------------------------------- main loop
-template <typename T, int E>
-__device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* smem) {
+// Operand staging: each thread moves kLoadsPerThread 16-byte chunks of A and
+// of B per stage; chunk c covers row c / 8 of the tile, bytes (c % 8) * 16.
+//
+// Fast path (both operands 16-byte aligned): rows past M / N are clamped to
+// the last valid row (finite data; those outputs are never stored, and the
+// log-sum-exp epilogue masks them to -inf), and every stage but a partial
+// last one is loaded with unconditional vector loads. The partial last stage
+// (K % BK != 0) goes through load_chunk, which zero-fills k >= K.
+template <typename T, bool kFast>
+__device__ __forceinline__ void mainloop(const GemmProblem& p, int64_t m0, int64_t n0, const Frag& f,
+                                         char* smem, Acc& acc) {
   constexpr int per16 = ET<T>::per16;
   constexpr int BK = (kRowBytes / 16) * per16;  // K elements per stage
-  int tm, tn;
-  tile_coords(id, p.tiles_m, p.tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * kTileM;
-  const int64_t n0 = (int64_t)tn * kTileN;
   const int tid = threadIdx.x;
-  Frag f;
-  f.lane = tid & 63;
-  f.wm = (tid >> 6) >> 1;
-  f.wn = (tid >> 6) & 1;
   const T* A = static_cast<const T*>(p.A);
   const T* B = static_cast<const T*>(p.B);
-  const int64_t nk = (p.K + BK - 1) / BK;
-  const bool avec = p.a_vec != 0, bvec = p.b_vec != 0;
+  const int64_t nfull = kFast ? p.K / BK : 0;              // stages loaded without masks
+  const int64_t nstage = (p.K + BK - 1) / BK;              // >= 1
+  const int64_t kc = (tid & 7) * per16;                    // this thread's k offset in a stage
 
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-
-  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-  auto gload = [&](int64_t kt) {
+  const T* pa[kLoadsPerThread];
+  const T* pb[kLoadsPerThread];
+  if constexpr (kFast) {
 #pragma unroll
     for (int i = 0; i < kLoadsPerThread; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c >> 3;
-      const int64_t k = kt * BK + (c & 7) * per16;
-      ra[i] = load_chunk<T>(A, p.lda, m0 + row, p.M, k, p.K, avec);
-      rb[i] = load_chunk<T>(B, p.ldb, n0 + row, p.N, k, p.K, bvec);
+      const int row = (tid >> 3) + i * (kThreads / 8);
+      const int64_t ra = min(m0 + row, p.M - 1), rb = min(n0 + row, p.N - 1);
+      pa[i] = A + ra * p.lda + kc;
+      pb[i] = B + rb * p.ldb + kc;
+    }
+  }
+  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
+  auto gload = [&](int64_t kt) {
+    if (kFast && kt < nfull) {
+#pragma unroll
+      for (int i = 0; i < kLoadsPerThread; ++i) {
+        ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + kt * BK);
+        rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + kt * BK);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoadsPerThread; ++i) {
+        const int row = (tid >> 3) + i * (kThreads / 8);
+        const int64_t k = kt * BK + kc;
+        ra[i] = load_chunk<T>(A, p.lda, m0 + row, p.M, k, p.K, p.a_vec != 0);
+        rb[i] = load_chunk<T>(B, p.ldb, n0 + row, p.N, k, p.K, p.b_vec != 0);
+      }
     }
   };
   auto sstore = [&](int buf) {
@@ -369,37 +396,71 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* sme
       *reinterpret_cast<u32x4*>(sb + off) = rb[i];
     }
   };
+  const int lrow = f.lane & 31;
+  const int lk = (f.lane >> 5) * 16;
   auto compute = [&](int buf) {
-    const char* sa = smem + buf * kStageBytes;
-    const char* sb = sa + kTileM * kPitch;
-    const int lrow = f.lane & 31;
-    const int lk = (f.lane >> 5) * 16;
+    const char* sa = smem + buf * kStageBytes + (f.wm * kWaveRowsM + lrow) * kPitch + lk;
+    const char* sb = smem + buf * kStageBytes + kTileM * kPitch + (f.wn * kWaveColsN + lrow) * kPitch + lk;
+    u32x4 af[2][MI], bf[2][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) af[0][mi] = *reinterpret_cast<const u32x4*>(sa + mi * 32 * kPitch);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) bf[0][ni] = *reinterpret_cast<const u32x4*>(sb + ni * 32 * kPitch);
 #pragma unroll
     for (int s = 0; s < kRowBytes / 32; ++s) {
-      u32x4 af[4], bf[4];
+      const int cur = s & 1;
+      if (s + 1 < kRowBytes / 32) {  // fragments of the next slab while this one multiplies
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const u32x4*>(sa + (f.wm * 128 + mi * 32 + lrow) * kPitch + s * 32 + lk);
+        for (int mi = 0; mi < MI; ++mi)
+          af[cur ^ 1][mi] = *reinterpret_cast<const u32x4*>(sa + mi * 32 * kPitch + (s + 1) * 32);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        bf[ni] = *reinterpret_cast<const u32x4*>(sb + (f.wn * 128 + ni * 32 + lrow) * kPitch + s * 32 + lk);
+        for (int ni = 0; ni < NI; ++ni)
+          bf[cur ^ 1][ni] = *reinterpret_cast<const u32x4*>(sb + ni * 32 * kPitch + (s + 1) * 32);
+      }
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma_step((T*)nullptr, af[mi], bf[ni], acc[mi][ni]);
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = mfma_step((T*)nullptr, af[cur][mi], bf[cur][ni], acc[mi][ni]);
     }
   };
 
   gload(0);
   sstore(0);
   __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
+  for (int64_t kt = 0; kt < nstage; ++kt) {
     const int buf = (int)(kt & 1);
-    if (kt + 1 < nk) gload(kt + 1);
+    if (kt + 1 < nstage) gload(kt + 1);
     compute(buf);
-    if (kt + 1 < nk) sstore(buf ^ 1);
+    if (kt + 1 < nstage) sstore(buf ^ 1);
     __syncthreads();
   }
+}
+
+template <typename T, int E>
+__device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* smem) {
+  int tm, tn;
+  tile_coords(id, p.tiles_m, p.tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * kTileM;
+  const int64_t n0 = (int64_t)tn * kTileN;
+  const int tid = threadIdx.x;
+  Frag f;
+  f.lane = tid & 63;
+  f.wm = (tid >> 6) / kWaveN;
+  f.wn = (tid >> 6) % kWaveN;
+
+  Acc acc;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  if (p.a_vec && p.b_vec)
+    mainloop<T, true>(p, m0, n0, f, smem, acc);
+  else
+    mainloop<T, false>(p, m0, n0, f, smem, acc);
 
   if constexpr (E == EPI_LSE_PARTIAL) epi_lse_partial<T>(p, acc, tm, m0, n0, f);
   if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f);
@@ -412,9 +473,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmP
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   const int bid = blockIdx.x;
   if (bid < ntiles0) {
-    tile_run<T, E0>(p0, bid, smem);
+    tile_run<T, E0>(p0, xcd_remap(bid, ntiles0), smem);
   } else {
-    if constexpr (E1 != EPI_NONE) tile_run<T, E1>(p1, bid - ntiles0, smem);
+    const int b1 = bid - ntiles0;
+    if constexpr (E1 != EPI_NONE) tile_run<T, E1>(p1, xcd_remap(b1, (int)gridDim.x - ntiles0), smem);
   }
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tile_config.h"
+
 namespace llp {
 
 // Element type codes (same values as llp_dtype).
@@ -21,12 +23,6 @@ enum Epi : int {
   EPI_ACCUM = 4         // table[m, n] += scale * C (dW, fp32 or operand-dtype table)
 };
 
-// Tile geometry shared by host (grid sizing, workspace layout) and device.
-constexpr int kTileM = 256;
-constexpr int kTileN = 256;
-constexpr int kWaveM = 2;  // waves along M; each wave owns 128 rows of the tile
-constexpr int kThreads = 256;
-
 // dlogits = g (onehot(t) - softmax(z)) is split into its softmax part
 // -g p, stored in the operand dtype (divided by the chunk's power-of-two
 // scale s) as the contraction operand, and its one-hot part g (1 - p_t), one
@@ -40,7 +36,7 @@ struct EpiParams {
   int64_t tok0;            // first token of this problem
   int64_t V;
   // EPI_LSE_PARTIAL (M = vocab, N = tokens)
-  float2* partials;        // [2 * tiles_m][ldp]: (max * log2 e, sum exp2) per wave-row block
+  float2* partials;        // [kWaveM * tiles_m][ldp]: (max * log2 e, sum exp2) per wave-row block
   int64_t ldp;
   float* zt;               // [tokens] target logit
   // EPI_DLOGITS (M = vocab, N = chunk tokens)

@@ -2,6 +2,8 @@
 // caller's workspace, and enqueue the kernels on the caller's stream.
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/llp.h"
 #include "kernels.h"
 #include "plan.h"
@@ -13,13 +15,55 @@ inline char* at(void* base, int64_t off) { return static_cast<char*>(base) + off
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-inline int st_hip(hipError_t e) { return e == hipSuccess ? LLP_OK : LLP_EHIP; }
-
 #define LLP_TRY(expr)                      \
   do {                                     \
     const hipError_t e_ = (expr);          \
     if (e_ != hipSuccess) return LLP_EHIP; \
   } while (0)
+
+// Opt-in per-thread launch tracing (llp_trace_enable / llp_trace_read).
+struct TraceRec {
+  int kind;
+  hipEvent_t start, stop;
+};
+struct Trace {
+  bool on = false;
+  std::vector<hipEvent_t> pool;  // created on demand, reused across traces
+  size_t used = 0;
+  std::vector<TraceRec> recs;
+  int64_t dropped = 0;
+};
+thread_local Trace g_trace;
+
+hipEvent_t trace_event() {
+  Trace& t = g_trace;
+  if (t.used == t.pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    t.pool.push_back(e);
+  }
+  return t.pool[t.used++];
+}
+
+template <class F>
+hipError_t traced(int kind, hipStream_t s, F&& launch) {
+  Trace& t = g_trace;
+  if (!t.on) return launch();
+  if (t.recs.size() >= (size_t)LLP_TRACE_MAX) {
+    ++t.dropped;
+    return launch();
+  }
+  hipEvent_t a = trace_event(), b = trace_event();
+  if (a == nullptr || b == nullptr) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e == hipSuccess) t.recs.push_back({kind, a, b});
+  return e;
+}
+#define LLP_LAUNCH(kind, expr) LLP_TRY(traced((kind), s, [&]() { return (expr); }))
 
 // Logits tile problem over tokens [tok0, tok0 + n) of h: A = W [V][D], B = h rows.
 GemmProblem logits_problem(int64_t tok0, int64_t n, int64_t D, int64_t V, int dtype,
@@ -56,8 +100,8 @@ int run_forward(int64_t N, int64_t D, int64_t V, int dtype, const void* h, const
   p.ep.partials = partials;
   p.ep.ldp = N;
   p.ep.zt = zt;
-  LLP_TRY(launch_gemm(dtype, &p, nullptr, s));
-  LLP_TRY(launch_lse_combine(partials, fp.P, N, zt, targets, V, N, logp, lse, s));
+  LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &p, nullptr, s));
+  LLP_LAUNCH(LLP_K_COMBINE, launch_lse_combine(partials, fp.P, N, zt, targets, V, N, logp, lse, s));
   return LLP_OK;
 }
 
@@ -142,13 +186,13 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
   const int64_t e = esize(dtype);
   const int64_t te = (dW_dtype == LLP_F32) ? 4 : e;
   if (!accumulate) {
-    if (want_dW) LLP_TRY(launch_zero(dW, V * D, (int)te, s));
-    if (want_db) LLP_TRY(launch_zero(db, V, (int)te, s));
+    if (want_dW) LLP_LAUNCH(LLP_K_SMALL, launch_zero(dW, V * D, (int)te, s));
+    if (want_db) LLP_LAUNCH(LLP_K_SMALL, launch_zero(db, V, (int)te, s));
   }
   if (N == 0 || !(want_dH || want_dW || want_db)) return LLP_OK;
 
   float2* scales = reinterpret_cast<float2*>(at(workspace, bp.off_scales));
-  LLP_TRY(launch_chunk_scales(g, N, bp.C, bp.K, scales, s));
+  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, bp.C, bp.K, scales, s));
   const float* lse_use = lse;
   if (lse == nullptr) {
     float* lse_ws = reinterpret_cast<float*>(at(workspace, bp.off_lse));
@@ -164,7 +208,7 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
   float* tcoef = reinterpret_cast<float*>(at(workspace, bp.off_tcoef));
   int32_t* head = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_head)) : nullptr;
   int32_t* next = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_next)) : nullptr;
-  if (want_dH) LLP_TRY(launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
+  if (want_dH) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
 
   for (int64_t k = 0; k < bp.K; ++k) {
     const int64_t c0 = k * bp.C;
@@ -185,12 +229,12 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
     p.ep.ldSt = bp.ldSt;
     p.ep.scales = scales;
     p.ep.chunk = (int)k;
-    LLP_TRY(launch_gemm(dtype, &p, nullptr, s));
+    LLP_LAUNCH(LLP_K_DLOGITS, launch_gemm(dtype, &p, nullptr, s));
     if (want_dW)
-      LLP_TRY(launch_transpose(dtype, static_cast<const char*>(h) + c0 * D * e, Ck, D, D, ht, bp.ldSt, s));
-    if (want_dW || want_db) LLP_TRY(launch_target_lists(targets, g, c0, Ck, V, head, next, s));
+      LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, static_cast<const char*>(h) + c0 * D * e, Ck, D, D, ht, bp.ldSt, s));
+    if (want_dW || want_db) LLP_LAUNCH(LLP_K_SMALL, launch_target_lists(targets, g, c0, Ck, V, head, next, s));
     if (want_db)
-      LLP_TRY(launch_db_accum(dtype, dSt, bp.ldSt, V, Ck, scales, (int)k, head, next, targets, g, tcoef,
+      LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, bp.ldSt, V, Ck, scales, (int)k, head, next, targets, g, tcoef,
                               c0, db, dW_dtype, s));
     GemmProblem ph = {}, pw = {};
     if (want_dH) {
@@ -247,7 +291,7 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
       pw.ep.chunk = (int)k;
     }
     if (want_dH || want_dW)
-      LLP_TRY(launch_gemm(dtype, want_dH ? &ph : nullptr, want_dW ? &pw : nullptr, s));
+      LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, want_dH ? &ph : nullptr, want_dW ? &pw : nullptr, s));
   }
   return LLP_OK;
 }
@@ -258,7 +302,9 @@ int logp_fwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t*
   if (st != LLP_OK) return st;
   if (N == 0) return LLP_OK;
   if (logits == nullptr || targets == nullptr || logp == nullptr) return LLP_EINVAL;
-  return st_hip(launch_rows_fwd(dtype, logits, N, V, targets, logp, lse, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LLP_LAUNCH(LLP_K_ROWS_FWD, launch_rows_fwd(dtype, logits, N, V, targets, logp, lse, s));
+  return LLP_OK;
 }
 
 int logp_bwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t* targets, const float* g,
@@ -267,8 +313,38 @@ int logp_bwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t*
   if (st != LLP_OK) return st;
   if (N == 0) return LLP_OK;
   if (logits == nullptr || targets == nullptr || g == nullptr || dlogits == nullptr) return LLP_EINVAL;
-  return st_hip(launch_rows_bwd(dtype, logits, N, V, targets, g, lse, dlogits,
-                                static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LLP_LAUNCH(LLP_K_ROWS_BWD, launch_rows_bwd(dtype, logits, N, V, targets, g, lse, dlogits, s));
+  return LLP_OK;
+}
+
+int llp_trace_enable(int on) {
+  Trace& t = g_trace;
+  if (on) {
+    t.recs.clear();
+    t.used = 0;
+    t.dropped = 0;
+  }
+  t.on = on != 0;
+  return LLP_OK;
+}
+
+int llp_trace_read(double* ms, int64_t* count, int n) {
+  if (n < 0) return LLP_EINVAL;
+  for (int k = 0; k < n; ++k) {
+    if (ms) ms[k] = 0.0;
+    if (count) count[k] = 0;
+  }
+  for (const TraceRec& r : g_trace.recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return LLP_EHIP;
+    float e = 0.0f;
+    if (hipEventElapsedTime(&e, r.start, r.stop) != hipSuccess) return LLP_EHIP;
+    if (r.kind >= 0 && r.kind < n) {
+      if (ms) ms[r.kind] += e;
+      if (count) count[r.kind] += 1;
+    }
+  }
+  return g_trace.dropped ? LLP_EOVERFLOW : LLP_OK;
 }
 
 }  // extern "C"

@@ -6,12 +6,14 @@
 #include <stdint.h>
 
 #include "../../include/llp.h"
+#include "tile_config.h"
 
 namespace llp {
 
 constexpr int64_t kMaxD = int64_t(1) << 22;     // transpose grid.y and tile count limits
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;  // one workgroup per row / grid.x
-constexpr int64_t kTile = 256;                  // contraction tile edge (M and N)
+constexpr int64_t kTile = kTileM;               // contraction tile edge (M and N)
+static_assert(kTileM == kTileN, "square tiles");
 constexpr int64_t kAlign = 256;                 // workspace region alignment (bytes)
 
 inline bool dtype_ok(int dt) { return dt == LLP_F32 || dt == LLP_BF16 || dt == LLP_F16; }
@@ -72,7 +74,7 @@ inline int check_linear_shapes(int64_t N, int64_t D, int64_t V, int dtype) {
 }
 
 struct FwdPlan {
-  int64_t P = 0;             // partial rows: 2 per vocab tile
+  int64_t P = 0;             // partial rows: kWaveM per vocab tile
   int64_t off_partials = 0;  // float2 [P][N]
   int64_t off_zt = 0;        // float [N]
   int64_t bytes = 0;
@@ -83,7 +85,7 @@ inline int plan_fwd(int64_t N, int64_t D, int64_t V, int dtype, FwdPlan* p) {
   if (st != LLP_OK) return st;
   *p = FwdPlan();
   if (N == 0) return LLP_OK;
-  p->P = 2 * ceil_div(V, kTile);
+  p->P = kWaveM * ceil_div(V, kTile);
   Layout L;
   int64_t n;
   if (!mul_ok(p->P, N, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;

@@ -36,7 +36,12 @@ SIGNATURES = {
                                _vp, _vp, _int, _vp, _int, _vp, _sz, _vp]),
     "logp_fwd": (_int, [_i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "logp_bwd": (_int, [_i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "llp_trace_enable": (_int, [_int]),
+    "llp_trace_read": (_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64), _int]),
 }
+
+# kernel kinds of the launch trace (llp_kernel_kind)
+TRACE_KINDS = ["fwd_lse", "combine", "dlogits", "dh_dw", "transpose", "small", "rows_fwd", "rows_bwd"]
 
 
 class LlpError(RuntimeError):
@@ -214,3 +219,18 @@ def logp_bwd(logits, targets, g, lse=None, dlogits=None, stream=None):
                         _ptr(lse), _ptr(dlogits), _stream(stream))
     _check(st, "logp_bwd")
     return dlogits
+
+
+def llp_trace_enable(on: bool = True) -> None:
+    _check(lib().llp_trace_enable(int(bool(on))), "llp_trace_enable")
+
+
+def llp_trace_read() -> dict:
+    """{kind: (total ms, launches)} of the current thread's trace (waits for its events)."""
+    n = len(TRACE_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (_i64 * n)()
+    st = lib().llp_trace_read(ms, cnt, n)
+    if st not in (LLP_OK, LLP_EOVERFLOW):
+        _check(st, "llp_trace_read")
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(TRACE_KINDS)}

@@ -153,6 +153,35 @@ LLP_API int logp_fwd(int64_t N, int64_t V, int dtype, const void* logits, const 
 LLP_API int logp_bwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t* targets,
              const float* g, const float* lse, void* dlogits, void* stream);
 
+/*
+ * Tracing (opt-in, per calling thread). While enabled, every kernel the
+ * library enqueues from this thread is bracketed by a pair of HIP events on
+ * its stream, and the elapsed times are summed per kernel kind. Intended for
+ * benchmarks that need per-kernel durations on the launch stream; the events
+ * are created on first use and reused. Tracing does not change results.
+ *
+ * llp_trace_enable(1) starts (and clears) a trace; llp_trace_enable(0) stops.
+ * llp_trace_read waits for the recorded events, then writes for each kind k
+ * in [0, n) the total milliseconds ms[k] and the launch count count[k]
+ * (either array may be NULL). Returns a status. At most LLP_TRACE_MAX
+ * launches are recorded per trace; later ones are counted in
+ * llp_trace_read's return of LLP_EOVERFLOW (the recorded ones stay valid).
+ */
+#define LLP_TRACE_MAX 65536
+typedef enum {
+  LLP_K_FWD_LSE = 0,    /* forward logits tile + online max/sum-exp partials */
+  LLP_K_COMBINE = 1,    /* per-token merge of partials -> logp, lse */
+  LLP_K_DLOGITS = 2,    /* backward logits recompute -> dlogits of a chunk */
+  LLP_K_DH_DW = 3,      /* dH and/or dW contractions of a chunk (one grid) */
+  LLP_K_TRANSPOSE = 4,  /* W^T and per-chunk h^T operand copies */
+  LLP_K_SMALL = 5,      /* chunk scales, target lists, db, zero fill */
+  LLP_K_ROWS_FWD = 6,   /* logits-only forward */
+  LLP_K_ROWS_BWD = 7,   /* logits-only backward */
+  LLP_K_COUNT = 8
+} llp_kernel_kind;
+LLP_API int llp_trace_enable(int on);
+LLP_API int llp_trace_read(double* ms, int64_t* count, int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 12
     L = llp.lib()
     for n in names:
         assert hasattr(L, n), n

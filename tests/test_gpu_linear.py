@@ -74,16 +74,45 @@ def test_linear_matches_oracle(w):
         assert_close(db, rdb, *tg, "db")
 
 
+def chunk_rounding_budget(w, host, esize_bits):
+    """Bound on the extra error of an operand-dtype table: after each chunk the
+    running table is rounded to the operand dtype, which moves it by at most
+    2^-p |running value| (p = 8 for bf16, 11 for fp16). The running values are
+    the oracle's partial sums over the chunks' tokens."""
+    run_w = np.zeros((w.V, w.D))
+    run_b = np.zeros(w.V)
+    bw = np.zeros((w.V, w.D))
+    bb = np.zeros(w.V)
+    for c0 in range(0, w.N, w.chunk):
+        c1 = min(w.N, c0 + w.chunk)
+        _, dw, db = O.linear_logp_bwd(host["h64"][c0:c1], host["W64"], host["b64"], host["t"][c0:c1],
+                                      host["g64"][c0:c1], False, True, w.bias)
+        run_w += dw
+        bw += np.abs(run_w) * 2.0 ** -esize_bits
+        if w.bias:
+            run_b += db
+            bb += np.abs(run_b) * 2.0 ** -esize_bits
+    return bw, bb
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_operand_dtype_table(dt):
+    # The stated gradient tolerance plus the table's own re-rounding after
+    # every chunk (an operand-dtype table is rounded K times).
     w = synth.LinearWorkload(f"optable_{dt}", 300, 136, 1031, dt, True, 128, "normal")
     _, _, _, dH, dW, db = run_case(w, tdt=torch_dtype(dt))
     assert dW.dtype == torch_dtype(dt) and db.dtype == torch_dtype(dt)
-    _, _, _, rdH, rdW, rdb = oracle_case(w)
-    tg = TOL[dt]["grad"]
-    assert_close(dH, rdH, *tg, "dH")
-    assert_close(dW, rdW, *tg, "dW (operand-dtype table)")
-    assert_close(db, rdb, *tg, "db (operand-dtype table)")
+    host, _, _, rdH, rdW, rdb = oracle_case(w)
+    bw, bb = chunk_rounding_budget(w, host, 8 if dt == "bf16" else 11)
+    atol, rtol = TOL[dt]["grad"]
+    assert_close(dH, rdH, atol, rtol, "dH")
+    gw = dW.double().cpu().numpy()
+    gb = db.double().cpu().numpy()
+    assert np.all(np.abs(gw - rdW) <= atol + rtol * np.abs(rdW) + bw), "dW (operand-dtype table)"
+    assert np.all(np.abs(gb - rdb) <= atol + rtol * np.abs(rdb) + bb), "db (operand-dtype table)"
+    # and the FP32 table of the same run meets the stated tolerance without the budget
+    _, _, _, _, dW32, db32 = run_case(w)
+    assert_close(dW32, rdW, atol, rtol, "dW (fp32 table)")
 
 
 def test_recomputed_lse_is_bitwise_the_forward_lse():
