@@ -58,9 +58,12 @@ __global__ void transpose_kernel(const T* __restrict__ src, int64_t rows, int64_
 }
 
 // s = smallest power of two >= max |g| over the chunk (1 if that maximum is 0
-// or not finite), so that dlogits / s stays within [-1, 1] and fp16 keeps its
-// precision; multiplying by s again is exact.
-__global__ void chunk_scales_kernel(const float* __restrict__ g, int64_t N, int64_t C,
+// or not finite), so that the stored softmax part (g / s) p lies in [-1, 1];
+// `headroom` further multiplies it by 2^headroom (15 for fp16, whose normal
+// range would otherwise lose the typical p ~ 1/V to subnormals; 2^15 * 1 stays
+// below fp16's maximum). scales[k] = (s 2^-headroom, 2^headroom / s): the
+// first undoes the second exactly in the epilogues.
+__global__ void chunk_scales_kernel(const float* __restrict__ g, int64_t N, int64_t C, int headroom,
                                     float2* __restrict__ scales) {
   __shared__ float red[4];
   const int64_t k = blockIdx.x;
@@ -75,9 +78,9 @@ __global__ void chunk_scales_kernel(const float* __restrict__ g, int64_t N, int6
     int e = 0;
     if (m > 0.0f && isfinite(m)) {
       frexpf(m, &e);  // m = f 2^e, f in [0.5, 1)  ->  2^e >= m
-      e = max(-126, min(127, e));
+      e = max(-100, min(100, e));
     }
-    scales[k] = make_float2(ldexpf(1.0f, e), ldexpf(1.0f, -e));
+    scales[k] = make_float2(ldexpf(1.0f, e - headroom), ldexpf(1.0f, headroom - e));
   }
 }
 
@@ -204,10 +207,10 @@ hipError_t launch_transpose(int dt, const void* src, int64_t rows, int64_t cols,
   }
 }
 
-hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, float2* scales,
-                               hipStream_t s) {
+hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, int headroom,
+                               float2* scales, hipStream_t s) {
   if (K == 0) return hipSuccess;
-  chunk_scales_kernel<<<(unsigned)K, 256, 0, s>>>(g, N, C, scales);
+  chunk_scales_kernel<<<(unsigned)K, 256, 0, s>>>(g, N, C, headroom, scales);
   return hipGetLastError();
 }
 

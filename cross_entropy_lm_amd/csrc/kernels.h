@@ -59,7 +59,7 @@ struct EpiParams {
   void* out;
   int64_t ldo;
   int out_dt;              // dtype of out (EPI_ACCUM table: DT_F32 or the operand dtype)
-  // backward epilogues: scales[chunk] = (s, 1/s)
+  // backward epilogues: scales[chunk] = (multiplier applied to C, divisor of the stored part)
   const float2* scales;
   int chunk;
 };
@@ -88,9 +88,10 @@ hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, co
 hipError_t launch_transpose(int dt, const void* src, int64_t rows, int64_t cols, int64_t lds,
                             void* dst, int64_t ldd, hipStream_t s);
 
-// scales[k] = (s, 1/s), s = smallest power of two >= max |g| over chunk k (1 if that is 0).
-hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, float2* scales,
-                               hipStream_t s);
+// scales[k] = (s 2^-headroom, 2^headroom / s), s = smallest power of two >= max |g|
+// over chunk k (1 if that is 0); headroom = 15 for fp16 operands, else 0.
+hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, int headroom,
+                               float2* scales, hipStream_t s);
 
 // db[v] += s_k * sum_{c < C} dSt[v][c] + sum of tcoef over the chunk's tokens with target v
 // (table dtype tdt; dSt in operand dtype dt).

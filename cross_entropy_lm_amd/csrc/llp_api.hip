@@ -192,7 +192,7 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
   if (N == 0 || !(want_dH || want_dW || want_db)) return LLP_OK;
 
   float2* scales = reinterpret_cast<float2*>(at(workspace, bp.off_scales));
-  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, bp.C, bp.K, scales, s));
+  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, bp.C, bp.K, dtype == LLP_F16 ? 15 : 0, scales, s));
   const float* lse_use = lse;
   if (lse == nullptr) {
     float* lse_ws = reinterpret_cast<float*>(at(workspace, bp.off_lse));

@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -99,18 +100,36 @@ def _normal_from_bits_np(u: np.ndarray) -> np.ndarray:
     return t0 + e
 
 
-def normal_rows_np(seed: int, tid: int, cols: int, rows_idx, scale: float = 1.0) -> np.ndarray:
-    """fp32 N(0, scale^2) values of the given rows of a [*, cols] tensor."""
+def normal_rows_np(seed: int, tid: int, cols: int, rows_idx, scale: float = 1.0,
+                   threads: int | None = None) -> np.ndarray:
+    """fp32 N(0, scale^2) values of the given rows of a [*, cols] tensor.
+
+    Cache-sized row blocks, spread over a thread pool for large requests
+    (numpy releases the GIL inside its array operations).
+    """
     r = np.asarray(rows_idx, dtype=np.uint64).reshape(-1)
     out = np.empty((r.size, cols), dtype=np.float32)
-    step = max(1, (1 << 16) // max(cols, 1))  # cache-sized blocks
+    step = max(1, (1 << 16) // max(cols, 1))
     cidx = np.arange(cols, dtype=np.uint64)[None, :]
-    for i in range(0, r.size, step):
+
+    def fill(i):
         idx = r[i:i + step, None] * np.uint64(cols) + cidx
         x = _normal_from_bits_np(bits_np(seed, tid, idx))
         if scale != 1.0:
             x = x * np.float32(scale)
         out[i:i + step] = x
+
+    starts = range(0, r.size, step)
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1) if r.size * cols >= (1 << 22) else 1
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, starts))
+    else:
+        for i in starts:
+            fill(i)
     return out
 
 
