@@ -194,9 +194,13 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, 
   }
 }
 
+// The token-major copy of the softmax part is staged through LDS (the
+// operand buffers are free once the K loop has ended) so that it leaves as
+// 16-byte row segments; the vocab-major copy leaves straight from the
+// accumulator layout, where 32 lanes hold 32 consecutive tokens of one row.
 template <typename T>
-__device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int64_t m0,
-                                            int64_t n0, const Frag& f) {
+__device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
+                                            const Frag& f, char* smem) {
   const EpiParams& e = p.ep;
   const T* bias = static_cast<const T*>(e.bias);
   T* dS = static_cast<T*>(e.dS);
@@ -209,39 +213,69 @@ __device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int6
   for (int ni = 0; ni < NI; ++ni) {
     const int64_t n = n0 + f.col(ni);
     const bool nv = n < p.N;
-    const int64_t tok = e.tok0 + n;
+    const int64_t tok = e.tok0 + (nv ? n : 0);
     tgt[ni] = nv ? e.targets[tok] : -1;
     gv[ni] = nv ? e.g[tok] : 0.0f;
     rv[ni] = nv && tgt[ni] >= 0 && tgt[ni] < p.M && gv[ni] != 0.0f;
     gs[ni] = gv[ni] * inv;
     l2[ni] = nv ? e.lse[tok] * kLog2e : 0.0f;
   }
+  // softmax part in place of the logits (0 past V / past the chunk)
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t v = m0 + f.row(mi, r);
-      if (v >= p.M) continue;
-      const float bv = (bias != nullptr) ? ld_f32(bias, v) : 0.0f;
+      const bool vv = v < p.M;
+      const float bv = (bias != nullptr) ? ld_f32(bias, vv ? v : 0) : 0.0f;
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
-        if (n >= p.N) continue;
         const float z = acc[mi][ni][r] + bv;
         const float pr = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -l2[ni]));
         float d = 0.0f;  // +0 for a row that takes no part
-        if (rv[ni]) {
-          if (v == tgt[ni]) {
-            e.tcoef[e.tok0 + n] = fmaf(-gv[ni], pr, gv[ni]);  // g (1 - p_t), exact part
-          } else {
+        if (rv[ni] && vv) {
+          if (v == tgt[ni])
+            e.tcoef[e.tok0 + n] = fmaf(-gv[ni], pr, gv[ni]);  // g (1 - p_t), the exact part
+          else
             d = -gs[ni] * pr;
-          }
         }
-        const T dt = (T)d;
-        if (dS != nullptr) dS[n * e.ldS + v] = dt;
-        if (dSt != nullptr) dSt[v * e.ldSt + n] = dt;
+        acc[mi][ni][r] = d;
+        if (dSt != nullptr && vv && n < p.N) dSt[v * e.ldSt + n] = (T)d;
       }
     }
+  }
+  if (dS == nullptr) return;
+  // token-major copy through LDS: [rows of tokens][256 vocab + pad], in passes
+  constexpr int kPad = 16 / (int)sizeof(T);
+  constexpr int kPitchE = kTileM + kPad;  // elements
+  constexpr int kPassRows = (kTileN * kPitchE * (int)sizeof(T) <= kLdsBytes) ? kTileN : kTileN / 2;
+  T* st = reinterpret_cast<T*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < kTileN / kPassRows; ++pass) {
+    const int nb = pass * kPassRows;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int nl = f.col(ni) - nb;
+          if (nl < 0 || nl >= kPassRows) continue;
+          T* q = st + nl * kPitchE + f.row(mi, rg * 4);  // 4 consecutive vocab rows
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = (T)acc[mi][ni][rg * 4 + i];
+        }
+    __syncthreads();
+    constexpr int kChunksPerRow = kTileM * (int)sizeof(T) / 16;
+    constexpr int per16 = ET<T>::per16;
+    for (int c = threadIdx.x; c < kPassRows * kChunksPerRow; c += kThreads) {
+      const int nl = c / kChunksPerRow, vc = (c % kChunksPerRow) * per16;
+      const int64_t n = n0 + nb + nl, v = m0 + vc;
+      if (n < p.N && v < p.M)
+        *reinterpret_cast<u32x4*>(dS + n * e.ldS + v) = *reinterpret_cast<const u32x4*>(st + nl * kPitchE + vc);
+    }
+    __syncthreads();
   }
 }
 
@@ -250,89 +284,116 @@ __device__ __forceinline__ bool token_valid(const EpiParams& e, int64_t tok, int
   return t >= 0 && t < e.V && e.g[tok] != 0.0f;
 }
 
-// dH rows of the chunk: out[m, :] = s C[m, :] + tcoef[m] W[t_m, :].
+// dH rows of the chunk: out[m, :] = s C[m, :] + tcoef[m] W[t_m, :]. The
+// tile's per-token (target, coefficient) pairs are staged in LDS first.
 template <typename T>
-__device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_t m0,
-                                          int64_t n0, const Frag& f) {
+__device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
+                                          const Frag& f, char* smem) {
   const EpiParams& e = p.ep;
   T* out = static_cast<T*>(e.out);
   const T* W = static_cast<const T*>(e.W);
   const float sc = e.scales[e.chunk].x;
+  int32_t* ts = reinterpret_cast<int32_t*>(smem);
+  float* cs = reinterpret_cast<float*>(smem + kTileM * sizeof(int32_t));
+  for (int i = threadIdx.x; i < kTileM; i += kThreads) {
+    const int64_t m = m0 + i;
+    int64_t t = -1;
+    const bool valid = m < p.M && token_valid(e, e.tok0 + m, t);
+    ts[i] = valid ? (int32_t)t : -1;
+    cs[i] = valid ? e.tcoef[e.tok0 + m] : 0.0f;
+  }
+  __syncthreads();
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t m = m0 + f.row(mi, r);
-      if (m >= p.M) continue;
-      int64_t t;
-      const bool valid = token_valid(e, e.tok0 + m, t);
-      const float c = valid ? e.tcoef[e.tok0 + m] : 0.0f;
-      const T* wrow = W + (valid ? t : 0) * e.ldW;
+      const int rl = f.row(mi, r);
+      const int64_t m = m0 + rl;
+      const int32_t tr = ts[rl];
+      const T* wrow = W + (int64_t)(tr >= 0 ? tr : 0) * e.ldW;  // row 0 stands in; its value is not used
+      const float c = cs[rl];
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
-        if (n < p.N) {
-          float val = acc[mi][ni][r] * sc;
-          if (valid) val = fmaf(c, ld_f32(wrow, n), val);
-          out[m * e.ldo + n] = (T)val;
-        }
+        const float base = acc[mi][ni][r] * sc;
+        const float withw = fmaf(c, ld_f32(wrow, n < p.N ? n : 0), base);
+        if (m < p.M && n < p.N) out[m * e.ldo + n] = (T)(tr >= 0 ? withw : base);
       }
     }
 }
 
 // dW rows: table[v, :] += s C[v, :] + sum, in token order, of tcoef[n] h[n, :]
-// over the chunk's valid tokens with target v.
+// over the chunk's valid tokens with target v. The tile's 256 list heads are
+// loaded and validated once into LDS (entries of targets absent from the
+// chunk are stale), so a row without targets costs one LDS read.
 template <typename T, typename TT>
-__device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int64_t m0,
-                                            int64_t n0, const Frag& f) {
+__device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
+                                            const Frag& f, char* smem) {
   const EpiParams& e = p.ep;
   TT* tab = static_cast<TT*>(e.out);
   const T* h = static_cast<const T*>(e.h);
   const float sc = e.scales[e.chunk].x;
+  int32_t* hs = reinterpret_cast<int32_t*>(smem);
+  for (int i = threadIdx.x; i < kTileM; i += kThreads) {
+    const int64_t m = m0 + i;
+    int32_t j = m < p.M ? e.head[m] : -1;
+    int64_t t;
+    if (!(j >= 0 && j < e.ntok && token_valid(e, e.tok0 + j, t) && t == m)) j = -1;
+    hs[i] = j;
+  }
+  __syncthreads();
+  TT* __restrict__ tb = tab;
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+  for (int mi = 0; mi < MI; ++mi) {
+    // per block of 16 rows: load every old table value first, then add and store
+    float val[16][NI];
+    TT old[16][NI];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t m = m0 + f.row(mi, r);
-      if (m >= p.M) continue;
-      float val[NI];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) val[ni] = acc[mi][ni][r] * sc;
-      // head entries of targets absent from this chunk are stale: accept only
-      // an index of this chunk whose token is valid and has target m
-      int32_t j = e.head[m];
-      int64_t t;
-      if (j >= 0 && j < e.ntok && token_valid(e, e.tok0 + j, t) && t == m) {
-        // at most ntok steps: the walk ends even if the list were malformed
-        for (int64_t it = 0; it < e.ntok && j >= 0 && j < e.ntok; ++it) {
-          const float c = e.tcoef[e.tok0 + j];
-          const T* hrow = h + (e.tok0 + j) * e.ldh;
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            const int64_t n = n0 + f.col(ni);
-            if (n < p.N) val[ni] = fmaf(c, ld_f32(hrow, n), val[ni]);
-          }
-          j = e.next[j];
-        }
-      }
+      const int64_t mc = m < p.M ? m : p.M - 1;  // in-bounds stand-in, not stored
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
-        if (n < p.N) {
-          TT* q = tab + m * e.ldo + n;
-          *q = (TT)((float)*q + val[ni]);
-        }
+        old[r][ni] = tb[mc * e.ldo + (n < p.N ? n : p.N - 1)];
+        val[r][ni] = acc[mi][ni][r] * sc;
       }
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = f.row(mi, r);
+      int32_t j = hs[rl];
+      // at most ntok steps: the walk ends even if the list were malformed
+      for (int64_t it = 0; it < e.ntok && j >= 0 && j < e.ntok; ++it) {
+        const float c = e.tcoef[e.tok0 + j];
+        const T* hrow = h + (e.tok0 + j) * e.ldh;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int64_t n = n0 + f.col(ni);
+          if (n < p.N) val[r][ni] = fmaf(c, ld_f32(hrow, n), val[r][ni]);
+        }
+        j = e.next[j];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t m = m0 + f.row(mi, r);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int64_t n = n0 + f.col(ni);
+        if (m < p.M && n < p.N) tb[m * e.ldo + n] = (TT)((float)old[r][ni] + val[r][ni]);
+      }
+    }
+  }
 }
 
 template <typename T>
 __device__ __forceinline__ void epi_accum(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
-                          const Frag& f) {
+                          const Frag& f, char* smem) {
   if (p.ep.out_dt == DT_F32)
-    epi_accum_t<T, float>(p, acc, m0, n0, f);
+    epi_accum_t<T, float>(p, acc, m0, n0, f, smem);
   else
-    epi_accum_t<T, T>(p, acc, m0, n0, f);
+    epi_accum_t<T, T>(p, acc, m0, n0, f, smem);
 }
 
 // ---------------------------------------------------------------- main loop
@@ -463,9 +524,9 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* sme
     mainloop<T, false>(p, m0, n0, f, smem, acc);
 
   if constexpr (E == EPI_LSE_PARTIAL) epi_lse_partial<T>(p, acc, tm, m0, n0, f);
-  if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f);
-  if constexpr (E == EPI_STORE) epi_store<T>(p, acc, m0, n0, f);
-  if constexpr (E == EPI_ACCUM) epi_accum<T>(p, acc, m0, n0, f);
+  if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f, smem);
+  if constexpr (E == EPI_STORE) epi_store<T>(p, acc, m0, n0, f, smem);
+  if constexpr (E == EPI_ACCUM) epi_accum<T>(p, acc, m0, n0, f, smem);
 }
 
 template <typename T, int E0, int E1>
