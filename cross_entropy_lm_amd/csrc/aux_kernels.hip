@@ -51,9 +51,11 @@ __global__ void transpose_kernel(const T* __restrict__ src, int64_t rows, int64_
     if (r < rows && c < cols) tile[i][tx] = src[r * lds + c];
   }
   __syncthreads();
+  const int64_t rpad = (rows + 7) & ~int64_t(7);
   for (int i = ty; i < 64; i += 4) {
     const int64_t c = c0 + i, r = r0 + tx;
     if (c < cols && r < rows) dst[c * ldd + r] = tile[tx][i];
+    else if (c < cols && r < rpad) dst[c * ldd + r] = (T)0;
   }
 }
 

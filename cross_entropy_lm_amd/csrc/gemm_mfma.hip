@@ -35,6 +35,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace llp {
 namespace {
 
@@ -56,6 +58,23 @@ constexpr int kWaveRowsM = 32 * MI;
 constexpr int kWaveColsN = 32 * NI;
 static_assert(kTileM == kTileN, "loader assumes square tiles");
 typedef f32x16 Acc[MI][NI];
+
+// Direct-to-LDS pipeline (operands 16-byte aligned, see mainloop_dma): five
+// operand slots, each one 128-byte K slice (one cache line per row) of the A or
+// the B tile (32 KiB, rows XOR-swizzled in 16-byte units, no padding), filled
+// by buffer_load ... lds. The slots are distinct LDS objects so the compiler
+// can tell reads of one slot from in-flight DMA into another.
+constexpr int kSB = 128;            // K bytes of a slot row
+constexpr int kOpB = kTileM * kSB;  // one slot
+constexpr int kNS = 5;              // slots
+constexpr int kStageArr = kOpB;
+static_assert(kNS * kStageArr <= 160 * 1024, "gfx950 LDS per workgroup");
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS handed to the epilogues: four regions of kOpB bytes.
+struct EpiLds {
+  char* a[4];
+};
 
 template <typename T> struct ET;
 template <> struct ET<__bf16> { static constexpr int per16 = 8; };
@@ -200,7 +219,7 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, 
 // accumulator layout, where 32 lanes hold 32 consecutive tokens of one row.
 template <typename T>
 __device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
-                                            const Frag& f, char* smem) {
+                                            const Frag& f, const EpiLds& L) {
   const EpiParams& e = p.ep;
   const T* bias = static_cast<const T*>(e.bias);
   T* dS = static_cast<T*>(e.dS);
@@ -241,18 +260,27 @@ __device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int6
             d = -gs[ni] * pr;
         }
         acc[mi][ni][r] = d;
-        if (dSt != nullptr && vv && n < p.N) dSt[v * e.ldSt + n] = (T)d;
+        // columns [N, round8(N)) get +0: a 16-byte K chunk that straddles the
+        // chunk's end then contributes nothing to the dW contraction
+        if (dSt != nullptr && vv && n < ((p.N + 7) & ~int64_t(7))) dSt[v * e.ldSt + n] = (T)d;
       }
     }
   }
   if (dS == nullptr) return;
-  // token-major copy through LDS: [rows of tokens][256 vocab + pad], in passes
+  // token-major copy through LDS, in passes of kPassRows tokens x 256 vocab
+  // (+ a 16-byte pad per row), each pass in one of the four LDS regions
   constexpr int kPad = 16 / (int)sizeof(T);
   constexpr int kPitchE = kTileM + kPad;  // elements
-  constexpr int kPassRows = (kTileN * kPitchE * (int)sizeof(T) <= kLdsBytes) ? kTileN : kTileN / 2;
-  T* st = reinterpret_cast<T*>(smem);
+  constexpr int kRegion = kOpB;  // bytes of each LDS region
+  constexpr int kPassRows = (kRegion / (kPitchE * (int)sizeof(T))) >= 64   ? 64
+                            : (kRegion / (kPitchE * (int)sizeof(T))) >= 32 ? 32
+                                                                          : 16;
+  constexpr int kPasses = kTileN / kPassRows;
+  constexpr int kChunksPerRow = kTileM * (int)sizeof(T) / 16;
+  constexpr int per16 = ET<T>::per16;
 #pragma unroll
-  for (int pass = 0; pass < kTileN / kPassRows; ++pass) {
+  for (int pass = 0; pass < kPasses; ++pass) {
+    T* st = reinterpret_cast<T*>(L.a[pass % 4]);
     const int nb = pass * kPassRows;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -267,8 +295,6 @@ __device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int6
           for (int i = 0; i < 4; ++i) q[i] = (T)acc[mi][ni][rg * 4 + i];
         }
     __syncthreads();
-    constexpr int kChunksPerRow = kTileM * (int)sizeof(T) / 16;
-    constexpr int per16 = ET<T>::per16;
     for (int c = threadIdx.x; c < kPassRows * kChunksPerRow; c += kThreads) {
       const int nl = c / kChunksPerRow, vc = (c % kChunksPerRow) * per16;
       const int64_t n = n0 + nb + nl, v = m0 + vc;
@@ -288,7 +314,8 @@ __device__ __forceinline__ bool token_valid(const EpiParams& e, int64_t tok, int
 // tile's per-token (target, coefficient) pairs are staged in LDS first.
 template <typename T>
 __device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
-                                          const Frag& f, char* smem) {
+                                          const Frag& f, const EpiLds& L) {
+  char* smem = L.a[0];
   const EpiParams& e = p.ep;
   T* out = static_cast<T*>(e.out);
   const T* W = static_cast<const T*>(e.W);
@@ -328,7 +355,8 @@ __device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_
 // chunk are stale), so a row without targets costs one LDS read.
 template <typename T, typename TT>
 __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
-                                            const Frag& f, char* smem) {
+                                            const Frag& f, const EpiLds& L) {
+  char* smem = L.a[0];
   const EpiParams& e = p.ep;
   TT* tab = static_cast<TT*>(e.out);
   const T* h = static_cast<const T*>(e.h);
@@ -389,11 +417,11 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
 
 template <typename T>
 __device__ __forceinline__ void epi_accum(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
-                          const Frag& f, char* smem) {
+                          const Frag& f, const EpiLds& L) {
   if (p.ep.out_dt == DT_F32)
-    epi_accum_t<T, float>(p, acc, m0, n0, f, smem);
+    epi_accum_t<T, float>(p, acc, m0, n0, f, L);
   else
-    epi_accum_t<T, T>(p, acc, m0, n0, f, smem);
+    epi_accum_t<T, T>(p, acc, m0, n0, f, L);
 }
 
 // ---------------------------------------------------------------- main loop
@@ -498,17 +526,163 @@ __device__ __forceinline__ void mainloop(const GemmProblem& p, int64_t m0, int64
   }
 }
 
-template <typename T, int E>
-__device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* smem) {
+// ---------------------------------------------------------------- direct-to-LDS main loop
+// Raw workgroup barrier: the memory clobber keeps the compiler from moving
+// LDS accesses across it, and no vmcnt(0) is implied (the DMA of later
+// stages stays in flight); each wave waits for exactly the loads it needs.
+#define LLP_BARRIER()                       \
+  do {                                      \
+    __builtin_amdgcn_sched_barrier(0);      \
+    asm volatile("s_barrier" ::: "memory"); \
+    __builtin_amdgcn_sched_barrier(0);      \
+  } while (0)
+// s_waitcnt vmcnt(N) through the builtin, so the compiler's own wait
+// insertion knows which DMA has landed (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14; expcnt 7 and lgkmcnt 15 mean no wait on those counters)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Stage k covers 128 bytes of K (four MFMA steps). Its A tile is unit 2k and
+// its B tile unit 2k + 1; unit u lives in slot u % 5. Every wave moves a
+// quarter-column of 8-row pieces of every unit from global memory to LDS by
+// DMA (buffer_load ... lds): no wave stages operands through registers or
+// writes them to LDS itself, and each row piece is one whole 128-byte line, so
+// every L1 miss fetches a full line. While stage k multiplies, stage k + 1 is
+// landing and the A tile of stage k + 2 is in flight; the barrier that ends
+// stage k makes stage k + 1 visible and frees stage k's two slots, which then
+// receive the B tile of stage k + 2 and the A tile of stage k + 3. Fragments
+// of step j + 1 are read from LDS while step j multiplies.
+// K chunks at or past K read as 0 (offset past the buffer's end); a chunk that
+// straddles K relies on the operand's padding columns being +0, which the
+// host guarantees when it enables this path.
+template <typename T>
+__device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, int64_t n0, const Frag& f,
+                                             char* const (&buf)[kNS], Acc& acc) {
+  static_assert(kTileM == kTileN, "A and B slots have one shape");
+  constexpr int per16 = ET<T>::per16;
+  constexpr int BKE = kSB / (int)sizeof(T);                    // K elements per stage
+  constexpr int kRowsPerLoad = 64 * 16 / kSB;                  // rows one wave instruction covers
+  constexpr int kLoads = kTileM / kRowsPerLoad / (kThreads / 64);  // instructions per wave per unit
+  static_assert(kLoads * kRowsPerLoad * (kThreads / 64) == kTileM, "the waves cover a slot");
+  constexpr int kSteps = kSB / 32;  // MFMA steps per stage: a step takes 32 bytes of K per row
+  const int lane = f.lane;
+  const int wave = f.wm * kWaveN + f.wn;
+  auto rsrc_of = [](const void* base, int64_t rows, int64_t ld) {
+    const int64_t bytes = rows * ld * (int64_t)sizeof(T);
+    const int nrec = bytes < 0x7FFFFFF0LL ? (int)bytes : 0x7FFFFFF0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t rsA = rsrc_of(static_cast<const T*>(p.A) + m0 * p.lda, p.M - m0, p.lda);
+  const __amdgpu_buffer_rsrc_t rsB = rsrc_of(static_cast<const T*>(p.B) + n0 * p.ldb, p.N - n0, p.ldb);
+  uint32_t voA[kLoads], voB[kLoads];
+  int kel[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int row = (wave * kLoads + j) * kRowsPerLoad + (lane >> 3);
+    const int c = (lane & 7) ^ (row & 7);  // LDS chunk lane & 7 holds global chunk c
+    voA[j] = (uint32_t)(row * p.lda * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
+    voB[j] = (uint32_t)(row * p.ldb * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
+    kel[j] = c * per16;
+  }
+  const int lds_off = wave * kLoads * kRowsPerLoad * kSB;
+  const int64_t nst = (p.K + BKE - 1) / BKE;
+
+  // unit (stage s, operand O) into `slot`
+  auto issue = [&](char* slot, int64_t s, auto Ov) {
+    constexpr int O = decltype(Ov)::value;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const uint32_t vo = O ? voB[j] : voA[j];
+      const uint32_t off = (s * BKE + kel[j] < p.K) ? vo + (uint32_t)(s * kSB) : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(O ? rsB : rsA,
+                                               (lds_void_t*)(slot + lds_off + j * kRowsPerLoad * kSB), 16, off,
+                                               0, 0, 0);
+    }
+  };
+  // fragments of step j of the stage held in slots (sa, sb)
+  auto read_step = [&](const char* sa, const char* sb, int j, u32x4 (&fa)[MI], u32x4 (&fb)[NI]) {
+    const int c = 2 * j + (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = f.wm * kWaveRowsM + mi * 32 + (lane & 31);
+      fa[mi] = *reinterpret_cast<const u32x4*>(sa + row * kSB + ((c ^ (row & 7)) * 16));
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int row = f.wn * kWaveColsN + ni * 32 + (lane & 31);
+      fb[ni] = *reinterpret_cast<const u32x4*>(sb + row * kSB + ((c ^ (row & 7)) * 16));
+    }
+  };
+  auto mma = [&](const u32x4 (&fa)[MI], const u32x4 (&fb)[NI]) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma_step((T*)nullptr, fa[mi], fb[ni], acc[mi][ni]);
+  };
+  using O_A = std::integral_constant<int, 0>;
+  using O_B = std::integral_constant<int, 1>;
+  u32x4 fa[2][MI], fb[2][NI];  // by step parity
+
+  auto stage = [&](int64_t k, auto Iv) {
+    constexpr int I = decltype(Iv)::value;  // k % kNS
+    char* const sa = buf[(2 * I) % kNS];
+    char* const sb = buf[(2 * I + 1) % kNS];
+    if (k >= nst) return;  // uniform over the workgroup
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      if (j + 1 < kSteps) read_step(sa, sb, j + 1, fa[(j + 1) & 1], fb[(j + 1) & 1]);
+      mma(fa[j & 1], fb[j & 1]);
+    }
+    // this wave's pieces of stage k + 1 have landed; only the A tile of stage
+    // k + 2 may remain in flight
+    if (k + 2 < nst) wait_vm<kLoads>();
+    else wait_vm<0>();
+    LLP_BARRIER();
+    if (k + 1 < nst) read_step(buf[(2 * I + 2) % kNS], buf[(2 * I + 3) % kNS], 0, fa[0], fb[0]);
+    if (k + 2 < nst) issue(sa, k + 2, O_B{});  // unit 2k + 5 goes to slot (2k) % 5
+    if (k + 3 < nst) issue(sb, k + 3, O_A{});  // unit 2k + 6 goes to slot (2k + 1) % 5
+  };
+
+  // units 0 .. 4: stages 0 and 1 and the A tile of stage 2
+  issue(buf[0], 0, O_A{});
+  issue(buf[1], 0, O_B{});
+  if (nst > 1) {
+    issue(buf[2], 1, O_A{});
+    issue(buf[3], 1, O_B{});
+  }
+  if (nst > 2) issue(buf[4], 2, O_A{});
+  if (nst > 2) wait_vm<3 * kLoads>();  // stage 0 landed
+  else if (nst > 1) wait_vm<2 * kLoads>();
+  else wait_vm<0>();
+  LLP_BARRIER();
+  read_step(buf[0], buf[1], 0, fa[0], fb[0]);
+  static_assert(kSteps % 2 == 0, "step parity restarts with every stage");
+  for (int64_t kb = 0; kb < nst; kb += kNS) {
+    stage(kb + 0, std::integral_constant<int, 0>{});
+    stage(kb + 1, std::integral_constant<int, 1>{});
+    stage(kb + 2, std::integral_constant<int, 2>{});
+    stage(kb + 3, std::integral_constant<int, 3>{});
+    stage(kb + 4, std::integral_constant<int, 4>{});
+  }
+}
+
+template <typename T, int E, bool kDma>
+__device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* const (&buf)[kNS]) {
   int tm, tn;
   tile_coords(id, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * kTileM;
   const int64_t n0 = (int64_t)tn * kTileN;
   const int tid = threadIdx.x;
+  // the wave index is uniform per wave; readfirstlane tells the compiler so,
+  // which keeps per-wave addresses and buffer descriptors in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   Frag f;
   f.lane = tid & 63;
-  f.wm = (tid >> 6) / kWaveN;
-  f.wn = (tid >> 6) % kWaveN;
+  f.wm = wave / kWaveN;
+  f.wn = wave % kWaveN;
 
   Acc acc;
 #pragma unroll
@@ -518,26 +692,51 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* sme
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  if (p.a_vec && p.b_vec)
-    mainloop<T, true>(p, m0, n0, f, smem, acc);
-  else
-    mainloop<T, false>(p, m0, n0, f, smem, acc);
+  if constexpr (kDma) {
+    mainloop_dma<T>(p, m0, n0, f, buf, acc);
+  } else {
+    if (p.a_vec && p.b_vec)
+      mainloop<T, true>(p, m0, n0, f, buf[0], acc);
+    else
+      mainloop<T, false>(p, m0, n0, f, buf[0], acc);
+  }
+  const EpiLds L = {{buf[0], buf[1], buf[2], buf[3]}};
 
   if constexpr (E == EPI_LSE_PARTIAL) epi_lse_partial<T>(p, acc, tm, m0, n0, f);
-  if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f, smem);
-  if constexpr (E == EPI_STORE) epi_store<T>(p, acc, m0, n0, f, smem);
-  if constexpr (E == EPI_ACCUM) epi_accum<T>(p, acc, m0, n0, f, smem);
+  if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f, L);
+  if constexpr (E == EPI_STORE) epi_store<T>(p, acc, m0, n0, f, L);
+  if constexpr (E == EPI_ACCUM) epi_accum<T>(p, acc, m0, n0, f, L);
 }
 
-template <typename T, int E0, int E1>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmProblem p1, int ntiles0) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+template <typename T, int E0, int E1, bool kDma>
+__device__ __forceinline__ void gemm_dispatch(const GemmProblem& p0, const GemmProblem& p1, int ntiles0,
+                                              char* const (&buf)[kNS]) {
   const int bid = blockIdx.x;
   if (bid < ntiles0) {
-    tile_run<T, E0>(p0, xcd_remap(bid, ntiles0), smem);
+    tile_run<T, E0, kDma>(p0, xcd_remap(bid, ntiles0), buf);
   } else {
     const int b1 = bid - ntiles0;
-    if constexpr (E1 != EPI_NONE) tile_run<T, E1>(p1, xcd_remap(b1, (int)gridDim.x - ntiles0), smem);
+    if constexpr (E1 != EPI_NONE) tile_run<T, E1, kDma>(p1, xcd_remap(b1, (int)gridDim.x - ntiles0), buf);
+  }
+}
+
+template <typename T, int E0, int E1, bool kDma>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmProblem p1, int ntiles0) {
+  if constexpr (kDma) {
+    // distinct LDS objects per slot (see kNS)
+    __shared__ __attribute__((aligned(16))) char st0[kStageArr];
+    __shared__ __attribute__((aligned(16))) char st1[kStageArr];
+    __shared__ __attribute__((aligned(16))) char st2[kStageArr];
+    __shared__ __attribute__((aligned(16))) char st3[kStageArr];
+    __shared__ __attribute__((aligned(16))) char st4[kStageArr];
+    char* const buf[kNS] = {st0, st1, st2, st3, st4};
+    gemm_dispatch<T, E0, E1, true>(p0, p1, ntiles0, buf);
+  } else {
+    static_assert(kLdsBytes >= 4 * kOpB, "epilogue regions fit in the staged buffer");
+    __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+    // the epilogues use the first four regions; the fifth is never touched
+    char* const buf[kNS] = {smem, smem + kOpB, smem + 2 * kOpB, smem + 3 * kOpB, smem};
+    gemm_dispatch<T, E0, E1, false>(p0, p1, ntiles0, buf);
   }
 }
 
@@ -552,12 +751,16 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
   const int e0 = p0 ? p0->epi : EPI_NONE;
   const int e1 = p1 ? p1->epi : EPI_NONE;
   dim3 grid(nt0 + nt1), block(kThreads);
+  const bool dma = (p0 == nullptr || p0->dma) && (p1 == nullptr || p1->dma);
   if (e0 == EPI_LSE_PARTIAL && e1 == EPI_NONE) {
-    gemm_kernel<T, EPI_LSE_PARTIAL, EPI_NONE><<<grid, block, 0, s>>>(a, b, nt0);
+    if (dma) gemm_kernel<T, EPI_LSE_PARTIAL, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
+    else gemm_kernel<T, EPI_LSE_PARTIAL, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
   } else if (e0 == EPI_DLOGITS && e1 == EPI_NONE) {
-    gemm_kernel<T, EPI_DLOGITS, EPI_NONE><<<grid, block, 0, s>>>(a, b, nt0);
+    if (dma) gemm_kernel<T, EPI_DLOGITS, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
+    else gemm_kernel<T, EPI_DLOGITS, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
   } else if ((e0 == EPI_STORE || e0 == EPI_NONE) && (e1 == EPI_ACCUM || e1 == EPI_NONE)) {
-    gemm_kernel<T, EPI_STORE, EPI_ACCUM><<<grid, block, 0, s>>>(a, b, nt0);
+    if (dma) gemm_kernel<T, EPI_STORE, EPI_ACCUM, true><<<grid, block, 0, s>>>(a, b, nt0);
+    else gemm_kernel<T, EPI_STORE, EPI_ACCUM, false><<<grid, block, 0, s>>>(a, b, nt0);
   } else {
     return hipErrorInvalidValue;
   }

@@ -70,6 +70,9 @@ struct GemmProblem {
   int64_t lda, ldb;
   int64_t M, N, K;
   int a_vec, b_vec;  // 1: rows may be read with 16-byte vector loads
+  int dma;           // 1: direct-to-LDS pipeline allowed (both operands 16-byte aligned, a 256-row
+                     //    tile spans < 2 GiB, and K % (16 / esize) == 0 or the padding columns
+                     //    up to the next multiple of 8 are +0)
   int tiles_m, tiles_n;
   int epi;
   EpiParams ep;
@@ -84,7 +87,8 @@ hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, co
                               const int64_t* targets, int64_t V, int64_t N, float* logp,
                               float* lse, hipStream_t s);
 
-// dst[c][r] = src[r][c] for r < rows, c < cols (element size from dt).
+// dst[c][r] = src[r][c] for r < rows, c < cols (element size from dt); the
+// padding columns r in [rows, round8(rows)) of each dst row are set to +0.
 hipError_t launch_transpose(int dt, const void* src, int64_t rows, int64_t cols, int64_t lds,
                             void* dst, int64_t ldd, hipStream_t s);
 

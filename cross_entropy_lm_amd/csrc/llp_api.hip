@@ -15,6 +15,16 @@ inline char* at(void* base, int64_t off) { return static_cast<char*>(base) + off
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Direct-to-LDS pipeline eligibility (see GemmProblem::dma): both operands
+// aligned for vector loads and a 256-row tile of each spanning < 2 GiB.
+// `kpad_zero`: the operands' padding columns up to round8(K) hold +0.
+inline int dma_ok(const GemmProblem& p, int64_t e, bool kpad_zero) {
+  const int64_t lim = 0x7FFFFFF0LL;
+  const bool span = kTile * p.lda * e < lim && kTile * p.ldb * e < lim;
+  const bool ktail = (p.K % (16 / e)) == 0 || kpad_zero;
+  return (p.a_vec && p.b_vec && span && ktail) ? 1 : 0;
+}
+
 #define LLP_TRY(expr)                      \
   do {                                     \
     const hipError_t e_ = (expr);          \
@@ -82,6 +92,7 @@ GemmProblem logits_problem(int64_t tok0, int64_t n, int64_t D, int64_t V, int dt
   p.b_vec = (D % per16 == 0) && aligned16(p.B);
   p.tiles_m = (int)ceil_div(V, kTile);
   p.tiles_n = (int)ceil_div(n, kTile);
+  p.dma = dma_ok(p, e, false);
   return p;
 }
 
@@ -246,6 +257,7 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
       ph.N = D;
       ph.K = V;
       ph.a_vec = ph.b_vec = 1;
+      ph.dma = dma_ok(ph, e, true);  // dS and W^T padding columns are written +0
       ph.tiles_m = (int)ceil_div(Ck, kTile);
       ph.tiles_n = (int)ceil_div(D, kTile);
       ph.epi = EPI_STORE;
@@ -271,6 +283,7 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
       pw.N = D;
       pw.K = Ck;
       pw.a_vec = pw.b_vec = 1;
+      pw.dma = dma_ok(pw, e, true);  // dlogits^T and h^T padding columns are written +0
       pw.tiles_m = (int)ceil_div(V, kTile);
       pw.tiles_n = (int)ceil_div(D, kTile);
       pw.epi = EPI_ACCUM;
