@@ -552,9 +552,11 @@ __device__ __forceinline__ void wait_vm() {
 // writes them to LDS itself, and each row piece is one whole 128-byte line, so
 // every L1 miss fetches a full line. While stage k multiplies, stage k + 1 is
 // landing and the A tile of stage k + 2 is in flight; the barrier that ends
-// stage k makes stage k + 1 visible and frees stage k's two slots, which then
-// receive the B tile of stage k + 2 and the A tile of stage k + 3. Fragments
-// of step j + 1 are read from LDS while step j multiplies.
+// stage k makes stage k + 1 visible and frees stage k's two slots. The B tile
+// of stage k + 2 is issued right after that barrier into the first of them;
+// the A tile of stage k + 3 goes into the second during the first two steps
+// of stage k + 1. Fragments of step j + 1 are read from LDS while step j
+// multiplies.
 // K chunks at or past K read as 0 (offset past the buffer's end); a chunk that
 // straddles K relies on the operand's padding columns being +0, which the
 // host guarantees when it enables this path.
@@ -590,11 +592,12 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
   const int lds_off = wave * kLoads * kRowsPerLoad * kSB;
   const int64_t nst = (p.K + BKE - 1) / BKE;
 
-  // unit (stage s, operand O) into `slot`
-  auto issue = [&](char* slot, int64_t s, auto Ov) {
+  // pieces [j0, j1) of unit (stage s, operand O) into `slot`
+  auto issue = [&](char* slot, int64_t s, auto Ov, int j0 = 0, int j1 = kLoads) {
     constexpr int O = decltype(Ov)::value;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
+      if (j < j0 || j >= j1) continue;
       const uint32_t vo = O ? voB[j] : voA[j];
       const uint32_t off = (s * BKE + kel[j] < p.K) ? vo + (uint32_t)(s * kSB) : 0xFFFFFFF0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(O ? rsB : rsA,
@@ -635,6 +638,11 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
     for (int j = 0; j < kSteps; ++j) {
       if (j + 1 < kSteps) read_step(sa, sb, j + 1, fa[(j + 1) & 1], fb[(j + 1) & 1]);
       mma(fa[j & 1], fb[j & 1]);
+      // the A tile of stage k + 2 goes, half after each of the first two
+      // steps, into the slot that held stage k - 1's B tile: spreading the
+      // DMA keeps the address queues from filling at the barrier
+      constexpr int kHalf = kLoads / 2;
+      if (j < 2 && k >= 1 && k + 2 < nst) issue(buf[(2 * I + 4) % kNS], k + 2, O_A{}, j * kHalf, (j + 1) * kHalf);
     }
     // this wave's pieces of stage k + 1 have landed; only the A tile of stage
     // k + 2 may remain in flight
@@ -643,7 +651,6 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
     LLP_BARRIER();
     if (k + 1 < nst) read_step(buf[(2 * I + 2) % kNS], buf[(2 * I + 3) % kNS], 0, fa[0], fb[0]);
     if (k + 2 < nst) issue(sa, k + 2, O_B{});  // unit 2k + 5 goes to slot (2k) % 5
-    if (k + 3 < nst) issue(sb, k + 3, O_A{});  // unit 2k + 6 goes to slot (2k + 1) % 5
   };
 
   // units 0 .. 4: stages 0 and 1 and the A tile of stage 2

@@ -9,7 +9,7 @@
 #define LLP_WAVES_N 4  // waves along N
 #endif
 #ifndef LLP_GROUP_M
-#define LLP_GROUP_M 8  // tiles along M per scheduling group (operand reuse in L2)
+#define LLP_GROUP_M 4  // tiles along M per scheduling group (operand reuse in L2)
 #endif
 
 namespace llp {
