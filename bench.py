@@ -71,6 +71,62 @@ def traffic_from_profiles(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+# rocprofv3 kernel names -> the launch-trace kinds of the library
+PMC_KERNELS = {"dh_dw": ("Li3ELi4E",), "dlogits": ("Li2ELi0E",), "fwd_lse": ("Li1ELi0E", "gemm_kernel<bool _Accum")}
+COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
+
+
+def pmc_per_dispatch(path: str, match) -> tuple[float, int]:
+    """Mean per dispatch of one rocprofv3 counter CSV's value over the
+    dispatches whose kernel name matches; rows of one dispatch are summed."""
+    import csv
+    import collections
+
+    per = collections.defaultdict(float)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if match(r["Kernel_Name"]):
+                per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no matching dispatch in {path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_pmc(args):
+    """profiles/pmc_<kernel>_<workload>.json from four rocprofv3 --pmc CSVs:
+    FETCH_SIZE and WRITE_SIZE of the bench run, and of --copy-calibration runs
+    (a plain device copy of COPY_BYTES), whose readings give the scale from the
+    counters' units to bytes."""
+    fetch, write, cfetch, cwrite = args.summarize_pmc
+    pats = PMC_KERNELS[args.pmc_kernel]
+    is_k = lambda n: "gemm_kernel" in n and any(x in n for x in pats)  # noqa: E731
+    is_copy = lambda n: "copyBuffer" in n or "copy_kernel" in n  # noqa: E731
+    f_val, f_n = pmc_per_dispatch(fetch, is_k)
+    w_val, w_n = pmc_per_dispatch(write, is_k)
+    cf_val, _ = pmc_per_dispatch(cfetch, is_copy)
+    cw_val, _ = pmc_per_dispatch(cwrite, is_copy)
+    kf, kw = COPY_BYTES / cf_val, COPY_BYTES / cw_val
+    out = {
+        "kernel": args.pmc_kernel, "workload": args.workload, "source_hash": kernel_source_hash(),
+        "fetch_size_per_dispatch": f_val, "write_size_per_dispatch": w_val, "dispatches": [f_n, w_n],
+        "copy_calibration": {"bytes": COPY_BYTES, "fetch_size": cf_val, "write_size": cw_val,
+                             "bytes_per_fetch_unit": kf, "bytes_per_write_unit": kw},
+        "hbm_read_bytes_per_launch": f_val * kf, "hbm_write_bytes_per_launch": w_val * kw,
+        "hbm_bytes_per_launch": f_val * kf + w_val * kw,
+    }
+    print(json.dumps(out, indent=1))
+
+
+def copy_calibration(torch):
+    """One plain device copy of COPY_BYTES (a reference for the PMC byte counters)."""
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -289,7 +345,15 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gate", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run one plain device copy of 1 GiB (reference for PMC byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the HBM traffic summary of --pmc-kernel from rocprofv3 counter CSVs")
+    ap.add_argument("--pmc-kernel", default="dh_dw", choices=sorted(PMC_KERNELS))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a "
               "design note, not a measured path.", file=sys.stderr)
@@ -301,6 +365,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     llp.lib()  # fail loudly if the HIP library is missing
     w = WORKLOADS[args.workload]
     if isinstance(w, synth.LogitsWorkload):
