@@ -10,15 +10,20 @@ namespace llp {
 namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
 
 // Per token: merge the per-tile (m, s) partials in increasing tile order
 // (m in log2 units, s = sum of 2^(y - m)), then lse = (M + log2 S) ln 2 and
 // logp = z[t] - lse for a target in [0, V), else +0 (RL-Kernel PR #495,
 // "Behavior changes").
+// With g and tcoef (fused forward + backward) it also writes the one-hot
+// part tcoef[n] = g (1 - p_t), p_t = 2^(z_t log2 e - lse log2 e), for a valid
+// token (0 <= t < V, g != 0), else +0.
 __global__ void lse_combine_kernel(const float2* __restrict__ partials, int64_t P, int64_t ldp,
                                    const float* __restrict__ zt, const int64_t* __restrict__ targets,
                                    int64_t V, int64_t N, float* __restrict__ logp,
-                                   float* __restrict__ lse) {
+                                   float* __restrict__ lse, const float* __restrict__ g,
+                                   float* __restrict__ tcoef) {
   const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
   float M = -INFINITY, S = 0.0f;
@@ -34,9 +39,63 @@ __global__ void lse_combine_kernel(const float2* __restrict__ partials, int64_t 
   }
   const float l = (M + __builtin_amdgcn_logf(S)) * kLn2;
   if (lse != nullptr) lse[n] = l;
-  if (logp != nullptr) {
-    const int64_t t = targets[n];
-    logp[n] = (t >= 0 && t < V) ? zt[n] - l : 0.0f;
+  const int64_t t = targets[n];
+  if (logp != nullptr) logp[n] = (t >= 0 && t < V) ? zt[n] - l : 0.0f;
+  if (tcoef != nullptr) {
+    const float gv = g[n];
+    const float pt = (t >= 0 && t < V) ? __builtin_amdgcn_exp2f(fmaf(zt[n], kLog2e, -(l * kLog2e))) : 0.0f;
+    tcoef[n] = (t >= 0 && t < V && gv != 0.0f) ? fmaf(-gv, pt, gv) : 0.0f;
+  }
+}
+
+// Fused forward + backward, one chunk of C tokens: from the stored numerators
+// q [v][n] (vocab-major, q = 2^(z log2 e - m_b) with m_b the max of the 128-row
+// vocab block b = v / 128 of token n, the first member of partials[b][n]),
+// the softmax part of dlogits divided by the chunk's scale,
+//     d[v][n] = -(g_n / s) q 2^(m_b - lse_n log2 e)   for a valid token n, v != t_n,
+//     d[v][n] = +0                                      otherwise,
+// written in place over q and, transposed, into dS [n][v] (token-major, +0 in
+// the columns [V, round8(V))). 64 x 64 tiles, 256 threads.
+template <typename T>
+__global__ void softmax_grad_kernel(T* __restrict__ qt, int64_t ldq, const float2* __restrict__ partials,
+                                    int64_t ldp, const float* __restrict__ lse, const float* __restrict__ g,
+                                    const int64_t* __restrict__ targets, const float2* __restrict__ scales,
+                                    int chunk, int64_t V, int64_t C, T* __restrict__ dS, int64_t ldS) {
+  __shared__ T tile[64][65];
+  const int64_t v0 = (int64_t)blockIdx.x * 64, n0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  // column n = n0 + tx: the token's factor; 64-row tiles never straddle a 128-row block
+  const int64_t n = n0 + tx;
+  float coef = 0.0f;  // -(g / s) 2^(m_b - lse log2 e), or 0 for a row that takes no part
+  int64_t t = -1;
+  if (n < C) {
+    t = targets[n];
+    const float gv = g[n];
+    if (t >= 0 && t < V && gv != 0.0f) {
+      const float m2 = partials[(v0 >> 7) * ldp + n].x;
+      const float f = (m2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m2 - lse[n] * kLog2e);
+      coef = -(gv * scales[chunk].y) * f;
+    } else {
+      t = -1;
+    }
+  }
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t v = v0 + i;
+    if (v < V && n < C) {
+      T* q = qt + v * ldq + n;
+      const float d = (t >= 0 && v != t) ? coef * (float)*q : 0.0f;
+      *q = (T)d;
+      tile[i][tx] = (T)d;
+    } else {
+      tile[i][tx] = (T)0;
+    }
+  }
+  if (dS == nullptr) return;  // uniform
+  __syncthreads();
+  const int64_t vpad = (V + 7) & ~int64_t(7);
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t nn = n0 + i, v = v0 + tx;
+    if (nn < C && v < vpad) dS[nn * ldS + v] = tile[tx][i];
   }
 }
 
@@ -192,10 +251,35 @@ hipError_t db_t(const void* dSt, int64_t ldSt, int64_t V, int64_t C, const float
 
 hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,
                               const int64_t* targets, int64_t V, int64_t N, float* logp,
-                              float* lse, hipStream_t s) {
+                              float* lse, const float* g, float* tcoef, hipStream_t s) {
   if (N == 0) return hipSuccess;
   lse_combine_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(partials, P, ldp, zt, targets, V, N,
-                                                                 logp, lse);
+                                                                 logp, lse, g, tcoef);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_grad(int dt, void* qt, int64_t ldq, const float2* partials, int64_t ldp,
+                               const float* lse, const float* g, const int64_t* targets,
+                               const float2* scales, int chunk, int64_t V, int64_t C, void* dS,
+                               int64_t ldS, hipStream_t s) {
+  if (V == 0 || C == 0) return hipSuccess;
+  dim3 grid((unsigned)((V + 63) / 64), (unsigned)((C + 63) / 64));  // C <= 2^31 - 1 (validated)
+  switch (dt) {
+    case DT_F32:
+      softmax_grad_kernel<float><<<grid, 256, 0, s>>>(static_cast<float*>(qt), ldq, partials, ldp, lse, g,
+                                                      targets, scales, chunk, V, C, static_cast<float*>(dS), ldS);
+      break;
+    case DT_BF16:
+      softmax_grad_kernel<__bf16><<<grid, 256, 0, s>>>(static_cast<__bf16*>(qt), ldq, partials, ldp, lse, g,
+                                                       targets, scales, chunk, V, C, static_cast<__bf16*>(dS), ldS);
+      break;
+    case DT_F16:
+      softmax_grad_kernel<_Float16><<<grid, 256, 0, s>>>(static_cast<_Float16*>(qt), ldq, partials, ldp, lse, g,
+                                                         targets, scales, chunk, V, C,
+                                                         static_cast<_Float16*>(dS), ldS);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

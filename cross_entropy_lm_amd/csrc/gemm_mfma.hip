@@ -160,7 +160,13 @@ struct Frag {
 };
 
 // ---------------------------------------------------------------- epilogues
-template <typename T>
+// Forward tile: per token (column) and wave-row block of 128 vocab rows, the
+// partial (m log2 e, sum of 2^(z log2 e - m log2 e)) and, for the row holding
+// the token's target, the target logit. With kQ (the fused forward + backward)
+// each summand q = 2^(z log2 e - m log2 e), in (0, 1], is also stored
+// vocab-major in the operand dtype, so that the softmax gradient can be
+// formed once the token's lse is known.
+template <typename T, bool kQ>
 __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, int tm, int64_t m0,
                                 int64_t n0, const Frag& f) {
   const EpiParams& e = p.ep;
@@ -196,13 +202,41 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, 
     m2[ni] = mx[ni] * kLog2e;
     s[ni] = 0.0f;
   }
+  if constexpr (!kQ) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        s[ni] += __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2[ni]));
+        for (int ni = 0; ni < NI; ++ni)
+          s[ni] += __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2[ni]));
+  } else {
+    const int64_t npad = (p.N + 7) & ~int64_t(7);
+    T* col[NI];     // this lane's column of the tile in the vocab-major buffer
+    bool keep[NI];  // the column lies in [0, round8(N)); past N it stores +0
+    bool live[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int64_t n = n0 + f.col(ni);
+      col[ni] = static_cast<T*>(e.dSt) + n;
+      keep[ni] = n < npad;
+      live[ni] = n < p.N;
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t v = m0 + f.row(mi, r);
+        const int64_t off = v * e.ldSt;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          // a block whose rows all lie past V has m = -inf; its rows are not stored
+          const float q = __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2[ni]));
+          s[ni] += q;
+          if (v < p.M && keep[ni]) col[ni][off] = (T)(live[ni] ? q : 0.0f);
+        }
+      }
+  }
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     float sv = s[ni] + __shfl_xor(s[ni], 32);
@@ -709,7 +743,8 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* con
   }
   const EpiLds L = {{buf[0], buf[1], buf[2], buf[3]}};
 
-  if constexpr (E == EPI_LSE_PARTIAL) epi_lse_partial<T>(p, acc, tm, m0, n0, f);
+  if constexpr (E == EPI_LSE_PARTIAL) epi_lse_partial<T, false>(p, acc, tm, m0, n0, f);
+  if constexpr (E == EPI_LSE_Q) epi_lse_partial<T, true>(p, acc, tm, m0, n0, f);
   if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f, L);
   if constexpr (E == EPI_STORE) epi_store<T>(p, acc, m0, n0, f, L);
   if constexpr (E == EPI_ACCUM) epi_accum<T>(p, acc, m0, n0, f, L);
@@ -762,6 +797,9 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
   if (e0 == EPI_LSE_PARTIAL && e1 == EPI_NONE) {
     if (dma) gemm_kernel<T, EPI_LSE_PARTIAL, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
     else gemm_kernel<T, EPI_LSE_PARTIAL, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
+  } else if (e0 == EPI_LSE_Q && e1 == EPI_NONE) {
+    if (dma) gemm_kernel<T, EPI_LSE_Q, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
+    else gemm_kernel<T, EPI_LSE_Q, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
   } else if (e0 == EPI_DLOGITS && e1 == EPI_NONE) {
     if (dma) gemm_kernel<T, EPI_DLOGITS, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
     else gemm_kernel<T, EPI_DLOGITS, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);

@@ -20,7 +20,8 @@ enum Epi : int {
   EPI_LSE_PARTIAL = 1,  // logits tile -> per-token (max, sum-exp) partials + target logit
   EPI_DLOGITS = 2,      // logits tile -> dlogits / scale, stored token-major and/or vocab-major
   EPI_STORE = 3,        // out[m, n] = scale * C, rounded to the operand dtype (dH)
-  EPI_ACCUM = 4         // table[m, n] += scale * C (dW, fp32 or operand-dtype table)
+  EPI_ACCUM = 4,        // table[m, n] += scale * C (dW, fp32 or operand-dtype table)
+  EPI_LSE_Q = 5         // EPI_LSE_PARTIAL, plus the tile's exp2(z log2 e - m) stored vocab-major
 };
 
 // dlogits = g (onehot(t) - softmax(z)) is split into its softmax part
@@ -39,6 +40,8 @@ struct EpiParams {
   float2* partials;        // [kWaveM * tiles_m][ldp]: (max * log2 e, sum exp2) per wave-row block
   int64_t ldp;
   float* zt;               // [tokens] target logit
+  // EPI_LSE_Q also stores q = exp2(z log2 e - m) (m: the wave-row block's max, the
+  // partial's first member) into dSt [V][ldSt], +0 in columns [N, round8(N))
   // EPI_DLOGITS (M = vocab, N = chunk tokens)
   const float* lse;        // [tokens]
   void* dS;                // [N][ldS] token-major softmax part / s, or null
@@ -85,7 +88,15 @@ hipError_t launch_gemm(int dt, const GemmProblem* p0, const GemmProblem* p1, hip
 // partials [P][N] + zt -> logp, lse (one thread per token, fixed order over P).
 hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,
                               const int64_t* targets, int64_t V, int64_t N, float* logp,
-                              float* lse, hipStream_t s);
+                              float* lse, const float* g, float* tcoef, hipStream_t s);
+
+// Fused forward + backward: softmax part of one chunk's dlogits from the stored
+// numerators, in place (vocab-major) and transposed into dS (token-major; dS may
+// be null when only the vocab-major copy is needed).
+hipError_t launch_softmax_grad(int dt, void* qt, int64_t ldq, const float2* partials, int64_t ldp,
+                               const float* lse, const float* g, const int64_t* targets,
+                               const float2* scales, int chunk, int64_t V, int64_t C, void* dS,
+                               int64_t ldS, hipStream_t s);
 
 // dst[c][r] = src[r][c] for r < rows, c < cols (element size from dt); the
 // padding columns r in [rows, round8(rows)) of each dst row are set to +0.

@@ -112,7 +112,7 @@ int run_forward(int64_t N, int64_t D, int64_t V, int dtype, const void* h, const
   p.ep.ldp = N;
   p.ep.zt = zt;
   LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &p, nullptr, s));
-  LLP_LAUNCH(LLP_K_COMBINE, launch_lse_combine(partials, fp.P, N, zt, targets, V, N, logp, lse, s));
+  LLP_LAUNCH(LLP_K_COMBINE, launch_lse_combine(partials, fp.P, N, zt, targets, V, N, logp, lse, nullptr, nullptr, s));
   return LLP_OK;
 }
 
@@ -177,13 +177,23 @@ int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, i
   return LLP_OK;
 }
 
-int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, const void* h,
-                    const void* W, const void* b, const int64_t* targets, const float* g,
-                    const float* lse, void* dH, void* dW, int dW_dtype, void* db, int accumulate,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+namespace llp {
+namespace {
+// The backward, and with `fused` the forward + backward of linear_logp_fwd_bwd:
+// there each chunk's logits tile yields the chunk's lse partials and softmax
+// numerators, the combine gives logp / lse / the one-hot part, and the
+// softmax gradient is formed from the numerators; the logits are not
+// recomputed. Everything after that is shared.
+int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, const void* h,
+                  const void* W, const void* b, const int64_t* targets, const float* g,
+                  const float* lse, float* logp_out, float* lse_out, void* dH, void* dW, int dW_dtype,
+                  void* db, int accumulate, void* workspace, size_t workspace_bytes, void* stream,
+                  bool fused) {
   const bool want_dH = dH != nullptr, want_dW = dW != nullptr, want_db = db != nullptr;
   BwdPlan bp;
-  int st = plan_bwd(N, D, V, dtype, chunk, want_dH, want_dW, want_db, lse != nullptr, &bp);
+  const bool have_lse = fused ? lse_out != nullptr : lse != nullptr;
+  int st = plan_bwd(N, D, V, dtype, chunk, want_dH, want_dW, want_db, have_lse, &bp, fused ? 1 : 0);
   if (st != LLP_OK) return st;
   if (accumulate != 0 && accumulate != 1) return LLP_EINVAL;
   if ((want_dW || want_db) && !(dW_dtype == LLP_F32 || dW_dtype == dtype)) return LLP_EINVAL;
@@ -191,6 +201,7 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
   if (N > 0 && (want_dH || want_dW || want_db) &&
       (h == nullptr || W == nullptr || targets == nullptr || g == nullptr))
     return LLP_EINVAL;
+  if (fused && N > 0 && logp_out == nullptr) return LLP_EINVAL;
   if ((size_t)bp.bytes > workspace_bytes || (bp.bytes > 0 && workspace == nullptr)) return LLP_EWORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -205,7 +216,11 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
   float2* scales = reinterpret_cast<float2*>(at(workspace, bp.off_scales));
   LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, bp.C, bp.K, dtype == LLP_F16 ? 15 : 0, scales, s));
   const float* lse_use = lse;
-  if (lse == nullptr) {
+  float* lse_fused = nullptr;  // where the fused path writes lse
+  if (fused) {
+    lse_fused = lse_out != nullptr ? lse_out : reinterpret_cast<float*>(at(workspace, bp.off_lse));
+    lse_use = lse_fused;
+  } else if (lse == nullptr) {
     float* lse_ws = reinterpret_cast<float*>(at(workspace, bp.off_lse));
     void* fws = at(workspace, bp.off_fwd);
     st = run_forward(N, D, V, dtype, h, W, b, targets, nullptr, lse_ws, fws, bp.fwd, s);
@@ -214,7 +229,9 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
   }
   void* Wt = want_dH ? at(workspace, bp.off_Wt) : nullptr;
   void* dS = want_dH ? at(workspace, bp.off_dS) : nullptr;
-  void* dSt = (want_dW || want_db) ? at(workspace, bp.off_dSt) : nullptr;
+  void* dSt = (want_dW || want_db || fused) ? at(workspace, bp.off_dSt) : nullptr;
+  float2* part = fused ? reinterpret_cast<float2*>(at(workspace, bp.off_part)) : nullptr;
+  float* zt = fused ? reinterpret_cast<float*>(at(workspace, bp.off_zt)) : nullptr;
   void* ht = want_dW ? at(workspace, bp.off_ht) : nullptr;
   float* tcoef = reinterpret_cast<float*>(at(workspace, bp.off_tcoef));
   int32_t* head = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_head)) : nullptr;
@@ -224,23 +241,38 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
   for (int64_t k = 0; k < bp.K; ++k) {
     const int64_t c0 = k * bp.C;
     const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
-    // dlogits of the chunk, recomputed from the logits tile and the saved lse
     GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
-    p.epi = EPI_DLOGITS;
     p.ep.bias = b;
     p.ep.targets = targets;
     p.ep.tok0 = c0;
     p.ep.V = V;
-    p.ep.g = g;
-    p.ep.lse = lse_use;
-    p.ep.tcoef = tcoef;
-    p.ep.dS = dS;
-    p.ep.ldS = bp.ldS;
-    p.ep.dSt = dSt;
-    p.ep.ldSt = bp.ldSt;
-    p.ep.scales = scales;
-    p.ep.chunk = (int)k;
-    LLP_LAUNCH(LLP_K_DLOGITS, launch_gemm(dtype, &p, nullptr, s));
+    if (fused) {
+      // the chunk's logits tile: lse partials, target logits, softmax numerators
+      p.epi = EPI_LSE_Q;
+      p.ep.partials = part;
+      p.ep.ldp = bp.C;
+      p.ep.zt = zt;
+      p.ep.dSt = dSt;
+      p.ep.ldSt = bp.ldSt;
+      LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &p, nullptr, s));
+      LLP_LAUNCH(LLP_K_COMBINE, launch_lse_combine(part, bp.P, bp.C, zt + c0, targets + c0, V, Ck, logp_out + c0,
+                                                   lse_fused + c0, g + c0, tcoef + c0, s));
+      LLP_LAUNCH(LLP_K_DLOGITS, launch_softmax_grad(dtype, dSt, bp.ldSt, part, bp.C, lse_fused + c0, g + c0,
+                                                    targets + c0, scales, (int)k, V, Ck, dS, bp.ldS, s));
+    } else {
+      // dlogits of the chunk, recomputed from the logits tile and the saved lse
+      p.epi = EPI_DLOGITS;
+      p.ep.g = g;
+      p.ep.lse = lse_use;
+      p.ep.tcoef = tcoef;
+      p.ep.dS = dS;
+      p.ep.ldS = bp.ldS;
+      p.ep.dSt = (want_dW || want_db) ? dSt : nullptr;
+      p.ep.ldSt = bp.ldSt;
+      p.ep.scales = scales;
+      p.ep.chunk = (int)k;
+      LLP_LAUNCH(LLP_K_DLOGITS, launch_gemm(dtype, &p, nullptr, s));
+    }
     if (want_dW)
       LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, static_cast<const char*>(h) + c0 * D * e, Ck, D, D, ht, bp.ldSt, s));
     if (want_dW || want_db) LLP_LAUNCH(LLP_K_SMALL, launch_target_lists(targets, g, c0, Ck, V, head, next, s));
@@ -307,6 +339,45 @@ int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, c
       LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, want_dH ? &ph : nullptr, want_dW ? &pw : nullptr, s));
   }
   return LLP_OK;
+}
+
+}  // namespace
+}  // namespace llp
+
+extern "C" {
+
+int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, const void* h,
+                    const void* W, const void* b, const int64_t* targets, const float* g,
+                    const float* lse, void* dH, void* dW, int dW_dtype, void* db, int accumulate,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(N, D, V, dtype, chunk, h, W, b, targets, g, lse, nullptr, nullptr, dH, dW, dW_dtype, db,
+                       accumulate, workspace, workspace_bytes, stream, false);
+}
+
+int linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
+                                       int want_dH, int want_dW, int want_db, int have_lse,
+                                       size_t* bytes) {
+  if (bytes == nullptr) return LLP_EINVAL;
+  if (!(want_dH || want_dW || want_db)) return linear_logp_fwd_workspace_size(N, D, V, dtype, bytes);
+  BwdPlan bp;
+  const int st = plan_bwd(N, D, V, dtype, chunk, want_dH, want_dW, want_db, have_lse, &bp, 1);
+  if (st != LLP_OK) return st;
+  *bytes = (size_t)bp.bytes;
+  return LLP_OK;
+}
+
+int linear_logp_fwd_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, const void* h,
+                        const void* W, const void* b, const int64_t* targets, const float* g,
+                        float* logp, float* lse, void* dH, void* dW, int dW_dtype, void* db,
+                        int accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dH == nullptr && dW == nullptr && db == nullptr) {
+    // nothing to differentiate: the forward alone
+    const int st = linear_logp_fwd(N, D, V, dtype, h, W, b, targets, logp, lse, workspace, workspace_bytes, stream);
+    if (st != LLP_OK) return st;
+    return (accumulate == 0 || accumulate == 1) ? LLP_OK : LLP_EINVAL;
+  }
+  return backward_impl(N, D, V, dtype, chunk, h, W, b, targets, g, nullptr, logp, lse, dH, dW, dW_dtype, db,
+                       accumulate, workspace, workspace_bytes, stream, true);
 }
 
 int logp_fwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t* targets, float* logp,

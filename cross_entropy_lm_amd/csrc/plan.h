@@ -110,11 +110,19 @@ struct BwdPlan {
   int64_t off_tcoef = -1;                // float [N]: one-hot part g (1 - p_t) per token
   int64_t off_head = -1;                 // int32 [V]: first chunk token per target   (dW or db)
   int64_t off_next = -1;                 // int32 [C]: next chunk token, same target (dW or db)
+  // fused forward + backward only
+  int64_t P = 0;                         // partial rows per token: kWaveM per vocab tile
+  int64_t off_part = -1;                 // float2 [P][C]: one chunk's forward partials
+  int64_t off_zt = -1;                   // float [N]: target logits
   int64_t bytes = 0;
 };
 
+// fused = 1: the layout of linear_logp_fwd_bwd, where each chunk's forward
+// runs first: the chunk's partials, the target logits and (when the caller
+// passes no lse) an lse buffer are added; the vocab-major buffer always exists
+// (it first holds the chunk's softmax numerators); no separate forward.
 inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, int want_dH,
-                    int want_dW, int want_db, int have_lse, BwdPlan* p) {
+                    int want_dW, int want_db, int have_lse, BwdPlan* p, int fused = 0) {
   int st = check_linear_shapes(N, D, V, dtype);
   if (st != LLP_OK) return st;
   *p = BwdPlan();
@@ -130,9 +138,17 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   p->off_scales = L.add(p->K * 8);
   if (!have_lse) {
     p->off_lse = L.add(N * 4);
-    st = plan_fwd(N, D, V, dtype, &p->fwd);
-    if (st != LLP_OK) return st;
-    p->off_fwd = L.add(p->fwd.bytes);
+    if (!fused) {
+      st = plan_fwd(N, D, V, dtype, &p->fwd);
+      if (st != LLP_OK) return st;
+      p->off_fwd = L.add(p->fwd.bytes);
+    }
+  }
+  if (fused) {
+    p->P = kWaveM * ceil_div(V, kTile);
+    if (!mul_ok(p->P, p->C, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
+    p->off_part = L.add(n);
+    p->off_zt = L.add(N * 4);
   }
   if (want_dH) {
     if (!mul_ok(D, p->ldWt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
@@ -140,7 +156,7 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     if (!mul_ok(p->C, p->ldS, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_dS = L.add(n);
   }
-  if (want_dW || want_db) {
+  if (want_dW || want_db || fused) {
     if (!mul_ok(V, p->ldSt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_dSt = L.add(n);
   }

@@ -34,6 +34,10 @@ SIGNATURES = {
                                               ctypes.POINTER(_sz)]),
     "linear_logp_bwd": (_int, [_i64, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _int, _vp, _int, _vp, _sz, _vp]),
+    "linear_logp_fwd_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int, _i64, _int, _int, _int, _int,
+                                                  ctypes.POINTER(_sz)]),
+    "linear_logp_fwd_bwd": (_int, [_i64, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _int, _vp, _int, _vp, _sz, _vp]),
     "logp_fwd": (_int, [_i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "logp_bwd": (_int, [_i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "llp_trace_enable": (_int, [_int]),
@@ -193,6 +197,51 @@ def linear_logp_bwd(h, W, b, targets, g, lse=None, want_dH=True, want_dW=True, w
                                _stream(stream))
     _check(st, "linear_logp_bwd")
     return dH, dW, db
+
+
+def linear_logp_fwd_bwd_workspace_size(N, D, V, dtype, chunk=0, want_dH=True, want_dW=True,
+                                       want_db=False, have_lse=True) -> int:
+    out = _sz(0)
+    _check(lib().linear_logp_fwd_bwd_workspace_size(N, D, V, dtype, chunk, int(want_dH), int(want_dW),
+                                                    int(want_db), int(have_lse), ctypes.byref(out)),
+           "linear_logp_fwd_bwd_workspace_size")
+    return out.value
+
+
+def linear_logp_fwd_bwd(h, W, b, targets, g, want_dH=True, want_dW=True, want_db=False, dW_dtype=None,
+                        chunk=0, accumulate=False, logp=None, lse=None, want_lse=True, dH=None, dW=None,
+                        db=None, workspace=None, stream=None):
+    """(logp, lse, dH, dW, db) in one call, for an upstream g known before the forward."""
+    torch = _torch()
+    for t, n in ((h, "h"), (W, "W"), (b, "b"), (targets, "targets"), (g, "g")):
+        _contig(t, n)
+    N, D = h.shape
+    V = W.shape[0]
+    dt = dtype_code(h.dtype)
+    tdt = torch.float32 if dW_dtype is None else dW_dtype
+    if logp is None:
+        logp = torch.empty(N, dtype=torch.float32, device=h.device)
+    if lse is None and want_lse:
+        lse = torch.empty(N, dtype=torch.float32, device=h.device)
+    if want_dH and dH is None:
+        dH = torch.empty((N, D), dtype=h.dtype, device=h.device)
+    if want_dW and dW is None:
+        dW = (torch.zeros if accumulate else torch.empty)((V, D), dtype=tdt, device=h.device)
+    if want_db and db is None:
+        db = (torch.zeros if accumulate else torch.empty)((V,), dtype=tdt, device=h.device)
+    if dW is not None:
+        tdt = dW.dtype
+    elif db is not None:
+        tdt = db.dtype
+    nbytes = linear_logp_fwd_bwd_workspace_size(N, D, V, dt, chunk, dH is not None, dW is not None,
+                                                db is not None, lse is not None)
+    ws = _workspace(nbytes, workspace, h.device)
+    st = lib().linear_logp_fwd_bwd(N, D, V, dt, chunk, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(g),
+                                   _ptr(logp), _ptr(lse), _ptr(dH), _ptr(dW), dtype_code(tdt), _ptr(db),
+                                   int(bool(accumulate)), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream))
+    _check(st, "linear_logp_fwd_bwd")
+    return logp, lse, dH, dW, db
 
 
 def logp_fwd(logits, targets, logp=None, lse=None, want_lse=True, stream=None):

@@ -138,6 +138,36 @@ LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t 
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward and backward in one call, for a caller that knows the upstream
+ * gradient g of logp before the forward runs (for example a mean or sum
+ * negative log-likelihood, g = -1/N or -1). Same inputs, outputs and
+ * conventions as linear_logp_fwd followed by linear_logp_bwd with the
+ * forward's lse: logp [N] (required), lse [N] (NULL to skip), dH, dW, db,
+ * dW_dtype, accumulate and chunk as in linear_logp_bwd. The difference is the
+ * schedule: each chunk's logits tile is computed once, and its softmax
+ * numerators exp(z - m) (m: the maximum over the tile's 128-row vocab block)
+ * are kept in the chunk workspace in the operand dtype until the chunk's lse
+ * is known, instead of recomputing the logits in the backward: three N x V x D
+ * contractions instead of four. This follows from g being fixed once the loss
+ * reduction is fixed; the fused linear cross-entropy is measured as one
+ * complete forward + backward training operation (Liger-Kernel PR #1324,
+ * "Benchmark results", "Methodology").
+ * logp and lse are bit-identical to linear_logp_fwd's. The gradients round
+ * the softmax part twice (the stored numerator, then the gradient), so they
+ * match linear_logp_bwd's to within that rounding, not bitwise.
+ * With dH, dW and db all NULL this is linear_logp_fwd (and the workspace
+ * query returns the forward's size). Deterministic.
+ */
+LLP_API int linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
+                                       int want_dH, int want_dW, int want_db, int have_lse,
+                                       size_t* bytes);
+LLP_API int linear_logp_fwd_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
+                        const void* h, const void* W, const void* b, const int64_t* targets,
+                        const float* g, float* logp, float* lse,
+                        void* dH, void* dW, int dW_dtype, void* db, int accumulate,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Logits-only forward (RL-Kernel PR #495): logits [N, V] of dtype ->
  * logp [N] (required), lse [N] (NULL to skip). One read of the logits.
  */
@@ -169,9 +199,9 @@ LLP_API int logp_bwd(int64_t N, int64_t V, int dtype, const void* logits, const 
  */
 #define LLP_TRACE_MAX 65536
 typedef enum {
-  LLP_K_FWD_LSE = 0,    /* forward logits tile + online max/sum-exp partials */
+  LLP_K_FWD_LSE = 0,    /* forward logits tile + online max/sum-exp partials (fused: per chunk) */
   LLP_K_COMBINE = 1,    /* per-token merge of partials -> logp, lse */
-  LLP_K_DLOGITS = 2,    /* backward logits recompute -> dlogits of a chunk */
+  LLP_K_DLOGITS = 2,    /* dlogits of a chunk: logits recompute, or (fused) from the numerators */
   LLP_K_DH_DW = 3,      /* dH and/or dW contractions of a chunk (one grid) */
   LLP_K_TRANSPOSE = 4,  /* W^T and per-chunk h^T operand copies */
   LLP_K_SMALL = 5,      /* chunk scales, target lists, db, zero fill */

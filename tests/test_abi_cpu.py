@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 12
+    assert len(names) == 14
     L = llp.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -126,6 +126,41 @@ def test_bwd_argument_errors():
     assert _bwd(nbytes=need - 1) == llp.LLP_EWORKSPACE
     assert _bwd(ws=None, nbytes=need) == llp.LLP_EWORKSPACE
     assert _bwd(N=1 << 31) == llp.LLP_EOVERFLOW
+
+
+def _fused(N=256, D=128, V=1024, dt=F32, chunk=64, h=FAKE, W=FAKE, b=FAKE, t=FAKE, g=FAKE, logp=FAKE,
+           lse=FAKE, dH=FAKE, dW=FAKE, tdt=F32, db=FAKE, acc=0, ws=FAKE, nbytes=1 << 40):
+    return llp.lib().linear_logp_fwd_bwd(N, D, V, dt, chunk, h, W, b, t, g, logp, lse, dH, dW, tdt, db, acc,
+                                         ws, nbytes, None)
+
+
+def test_fused_argument_errors_and_workspace():
+    E = llp.LLP_EINVAL
+    assert _fused(N=-1) == E
+    assert _fused(D=0) == E
+    assert _fused(dt=3) == E
+    assert _fused(acc=2) == E
+    assert _fused(tdt=F16) == E
+    assert _fused(b=None) == E         # db requested without a bias
+    assert _fused(h=None) == E
+    assert _fused(g=None) == E
+    assert _fused(logp=None) == E      # logp is required, as in linear_logp_fwd
+    fq = llp.linear_logp_fwd_bwd_workspace_size
+    need = fq(256, 128, 1024, F32, 64, True, True, True, True)
+    assert _fused(nbytes=need - 1) == llp.LLP_EWORKSPACE
+    assert _fused(ws=None, nbytes=need) == llp.LLP_EWORKSPACE
+    assert _fused(N=1 << 31) == llp.LLP_EOVERFLOW
+    # the fused layout adds the chunk's forward partials and target logits, and
+    # always holds the vocab-major buffer; without lse it also holds one
+    bq = llp.linear_logp_bwd_workspace_size
+    assert need > bq(256, 128, 1024, F32, 64, True, True, True, True)
+    assert fq(256, 128, 1024, F32, 64, True, True, True, False) >= need + 256 * 4
+    # no gradient requested: the forward's workspace
+    assert fq(256, 128, 1024, F32, 64, False, False, False, True) == llp.linear_logp_fwd_workspace_size(
+        256, 128, 1024, F32)
+    # N = 0 with accumulate: nothing to do, null pointers allowed
+    assert llp.lib().linear_logp_fwd_bwd(0, 128, 1024, F32, 0, None, None, None, None, None, None, None, None,
+                                         None, F32, None, 1, None, 0, None) == llp.LLP_OK
 
 
 def test_header_documents_each_entry_point():

@@ -1,0 +1,277 @@
+"""GPU parity of the single-call forward + backward (linear_logp_fwd_bwd)
+against the FP64 oracle through the C ABI: the small ragged shapes of the
+split path, the edge cases, the bitwise properties (logp / lse equal to the
+forward's, repeats, requested subsets, lse given or not, exact power-of-two
+scaling), closeness to the split path's gradients, and the headline workloads
+at full size on sampled outputs."""
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import linear_logp as O
+
+from gpu_common import TOL, assert_close, bits_equal, norm_err, say, torch_dtype
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# the fused gradients round the softmax part twice (stored numerator, then the
+# gradient); their distance to the split path's, relative to its largest entry
+SPLIT_CLOSE = {"bf16": 2.0 ** -6, "f16": 2.0 ** -9, "f32": 1e-5}
+
+
+def llp():
+    from cross_entropy_lm_amd import llp as m
+
+    return m
+
+
+def fused(w, d, want=(True, True, True), tdt=None, chunk=None, g=None, want_lse=True, t=None, **kw):
+    say(f"fused {w.name} N={w.N} D={w.D} V={w.V} {w.dtype} chunk={w.chunk if chunk is None else chunk} want={want}")
+    out = llp().linear_logp_fwd_bwd(d["h"], d["W"], d["b"], d["t"] if t is None else t,
+                                    d["g"] if g is None else g, want[0], want[1], want[2] and w.bias,
+                                    dW_dtype=tdt, chunk=w.chunk if chunk is None else chunk,
+                                    want_lse=want_lse, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def split(w, d, tdt=None, chunk=None):
+    L = llp()
+    logp, lse = L.linear_logp_fwd(d["h"], d["W"], d["b"], d["t"])
+    dH, dW, db = L.linear_logp_bwd(d["h"], d["W"], d["b"], d["t"], d["g"], lse, True, True, w.bias,
+                                   dW_dtype=tdt, chunk=w.chunk if chunk is None else chunk)
+    torch.cuda.synchronize()
+    return logp, lse, dH, dW, db
+
+
+SMALL = [
+    synth.LinearWorkload("ragged_bf16", 300, 136, 1031, "bf16", True, 128, "normal"),
+    synth.LinearWorkload("ragged_f16", 300, 136, 1031, "f16", True, 128, "normal"),
+    synth.LinearWorkload("ragged_f32", 300, 136, 1031, "f32", True, 128, "normal"),
+    synth.LinearWorkload("oddD_bf16", 130, 99, 515, "bf16", True, 64, "normal"),
+    synth.LinearWorkload("oddD_f32", 130, 99, 515, "f32", False, 50, "normal"),
+    synth.LinearWorkload("v255_bf16", 77, 64, 255, "bf16", False, 7, "normal"),
+    synth.LinearWorkload("v1_f32", 33, 32, 1, "f32", True, 16, "normal"),
+    synth.TINY,
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_fused_matches_oracle_and_the_split_path(w):
+    d = synth.make_linear_t(w, DEV)
+    logp, lse, dH, dW, db = fused(w, d)
+    host = synth.make_linear_np(w)
+    rlogp, rlse = O.linear_logp_fwd(host["h64"], host["W64"], host["b64"], host["t"])
+    rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True, True,
+                                      w.bias)
+    tl, tg = TOL[w.dtype]["logp"], TOL[w.dtype]["grad"]
+    assert_close(logp, rlogp, *tl, "logp")
+    assert_close(lse, rlse, *tl, "lse")
+    assert_close(dH, rdH, *tg, "dH")
+    assert_close(dW, rdW, *tg, "dW")
+    if w.bias:
+        assert_close(db, rdb, *tg, "db")
+    s_logp, s_lse, s_dH, s_dW, s_db = split(w, d)
+    # the forward is the same arithmetic: bitwise
+    assert bits_equal(logp, s_logp) and bits_equal(lse, s_lse)
+    for x, y, n in ((dH, s_dH, "dH"), (dW, s_dW, "dW"), (db, s_db, "db")):
+        if x is None:
+            continue
+        e = norm_err(x, y.double().cpu().numpy())
+        assert e <= SPLIT_CLOSE[w.dtype], f"{n}: fused vs split {e:.2e}"
+
+
+def test_fused_repeat_subsets_and_lse_are_bitwise():
+    w = SMALL[0]
+    d = synth.make_linear_t(w, DEV)
+    full = fused(w, d)
+    again = fused(w, d)
+    for x, y in zip(full, again):
+        assert bits_equal(x, y)
+    no_lse = fused(w, d, want_lse=False)
+    assert no_lse[1] is None
+    for i in (0, 2, 3, 4):
+        assert bits_equal(full[i], no_lse[i])
+    only_dh = fused(w, d, want=(True, False, False))
+    only_dw = fused(w, d, want=(False, True, False))
+    only_db = fused(w, d, want=(False, False, True))
+    assert bits_equal(full[2], only_dh[2]) and only_dh[3] is None and only_dh[4] is None
+    assert bits_equal(full[3], only_dw[3]) and only_dw[2] is None and only_dw[4] is None
+    assert bits_equal(full[4], only_db[4]) and only_db[2] is None and only_db[3] is None
+    for o in (only_dh, only_dw, only_db):
+        assert bits_equal(full[0], o[0]) and bits_equal(full[1], o[1])
+    # nothing to differentiate: the forward alone
+    fwd_only = fused(w, d, want=(False, False, False))
+    assert bits_equal(full[0], fwd_only[0]) and bits_equal(full[1], fwd_only[1])
+    assert fwd_only[2] is None and fwd_only[3] is None and fwd_only[4] is None
+
+
+def test_fused_logp_and_dH_do_not_depend_on_the_chunk():
+    w = SMALL[0]
+    d = synth.make_linear_t(w, DEV)
+    ref = fused(w, d, chunk=300)
+    for c in (1, 7, 64, 128, 0):
+        r = fused(w, d, chunk=c)
+        assert bits_equal(ref[0], r[0]) and bits_equal(ref[1], r[1]), c
+        assert bits_equal(ref[2], r[2]), c
+
+
+def test_fused_power_of_two_upstream_scales_exactly():
+    w = SMALL[0]
+    d = synth.make_linear_t(w, DEV)
+    a = fused(w, d)
+    b = fused(w, d, g=d["g"] * 2.0 ** -14)
+    assert bits_equal(a[0], b[0]) and bits_equal(a[1], b[1])
+    for x, y in zip(a[2:], b[2:]):
+        assert bits_equal(x.float() * 2.0 ** -14, y.float()) if x.dtype == torch.float32 else \
+            bits_equal((x.float() * 2.0 ** -14).to(x.dtype), y)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+def test_fused_zero_upstream_gives_positive_zeros(dt):
+    w = synth.LinearWorkload(f"g0_{dt}", 300, 136, 1031, dt, True, 128, "normal")
+    d = synth.make_linear_t(w, DEV)
+    for g0 in (0.0, -0.0):
+        g = torch.full((w.N,), g0, dtype=torch.float32, device=DEV)
+        _, _, dH, dW, db = fused(w, d, g=g)
+        for x in (dH, dW, db):
+            xf = x.float()
+            assert bool((xf == 0).all()), "nonzero gradient for g = 0"
+            assert not bool(torch.signbit(xf).any()), "negative zero for g = 0"
+
+
+def test_fused_out_of_range_targets():
+    w = synth.LinearWorkload("oor_bf16", 300, 136, 1031, "bf16", True, 128, "normal")
+    d = synth.make_linear_t(w, DEV)
+    t = d["t"].clone()
+    bad = torch.tensor([1, 150, 299])
+    t[bad] = torch.tensor([-100, w.V, w.V + 5], device=DEV)
+    logp, lse, dH, dW, db = fused(w, d, t=t)
+    lp = logp.cpu()
+    assert bool((lp[bad] == 0).all()) and not bool(torch.signbit(lp[bad]).any())
+    dHf = dH.float().cpu()
+    assert bool((dHf[bad] == 0).all()) and not bool(torch.signbit(dHf[bad]).any())
+    host = synth.make_linear_np(w)
+    tt = host["t"].copy()
+    tt[bad.numpy()] = [-100, w.V, w.V + 5]
+    rlogp, rlse = O.linear_logp_fwd(host["h64"], host["W64"], host["b64"], tt)
+    rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], tt, host["g64"], True, True, True)
+    tl, tg = TOL["bf16"]["logp"], TOL["bf16"]["grad"]
+    assert_close(logp, rlogp, *tl, "logp")
+    assert_close(lse, rlse, *tl, "lse")
+    assert_close(dH, rdH, *tg, "dH")
+    assert_close(dW, rdW, *tg, "dW")
+    assert_close(db, rdb, *tg, "db")
+
+
+def test_fused_empty_batch_and_accumulate():
+    L = llp()
+    say("fused N = 0")
+    D, V = 64, 300
+    h = torch.empty((0, D), dtype=torch.bfloat16, device=DEV)
+    W = torch.randn((V, D), device=DEV).to(torch.bfloat16)
+    b = torch.randn(V, device=DEV).to(torch.bfloat16)
+    t = torch.empty(0, dtype=torch.int64, device=DEV)
+    g = torch.empty(0, dtype=torch.float32, device=DEV)
+    dW0 = torch.full((V, D), float("nan"), device=DEV)
+    db0 = torch.full((V,), float("nan"), device=DEV)
+    logp, lse, dH, dW, db = L.linear_logp_fwd_bwd(h, W, b, t, g, True, True, True, dW=dW0, db=db0)
+    torch.cuda.synchronize()
+    assert logp.shape == (0,) and dH.shape == (0, D)
+    for x in (dW, db):
+        assert bool((x == 0).all()) and not bool(torch.signbit(x).any())
+    # accumulate into the caller's tables
+    w = synth.LinearWorkload("acc_f32", 200, 72, 600, "f32", True, 64, "normal")
+    d = synth.make_linear_t(w, DEV)
+    gen = torch.Generator().manual_seed(5)
+    a0 = torch.randn((w.V, w.D), generator=gen).to(DEV)
+    b0 = torch.randn((w.V,), generator=gen).to(DEV)
+    _, _, _, dW, db = fused(w, d, want=(False, True, True), accumulate=True, dW=a0.clone(), db=b0.clone())
+    host = synth.make_linear_np(w)
+    _, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], False,
+                                    True, True, dW0=a0.cpu().double().numpy(), db0=b0.cpu().double().numpy())
+    assert_close(dW, rdW, 1e-5, 5e-4, "dW accumulate")
+    assert_close(db, rdb, 1e-5, 5e-4, "db accumulate")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_fused_operand_dtype_table(dt):
+    w = synth.LinearWorkload(f"optable_{dt}", 300, 136, 1031, dt, True, 128, "normal")
+    d = synth.make_linear_t(w, DEV)
+    _, _, _, dW, db = fused(w, d, tdt=torch_dtype(dt))
+    assert dW.dtype == torch_dtype(dt)
+    _, _, _, sdW, sdb = split(w, d, tdt=torch_dtype(dt))
+    # both round the table once per chunk; the fused path also rounds the softmax part twice
+    for x, y, n in ((dW, sdW, "dW"), (db, sdb, "db")):
+        e = norm_err(x, y.double().cpu().numpy())
+        assert e <= 2 * SPLIT_CLOSE[dt], f"{n}: fused vs split {e:.2e}"
+
+
+# ----------------------------------------------------------------------------- full size
+def sample_tokens(N, C):
+    s = {0, 1, N - 1, N // 2, C - 1, min(C, N - 1), N - 2}
+    s |= set(int(x) for x in np.random.default_rng(N).integers(0, N, 6))
+    return np.array(sorted(x for x in s if 0 <= x < N))
+
+
+def sample_vocab(V, t_host):
+    s = {0, V - 1, V // 2} | set(int(x) for x in t_host[:4])
+    s |= set(int(x) for x in np.random.default_rng(V).integers(0, V, 6))
+    vals, cnt = np.unique(t_host, return_counts=True)
+    if (cnt > 1).any():
+        s.add(int(vals[np.argmax(cnt)]))
+    return np.array(sorted(s))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_fused_flce_full_size(dt):
+    w = {"bf16": synth.FLCE, "f16": synth.FLCE_F16}[dt]
+    d = synth.make_linear_t(w, DEV)
+    logp, lse, dH, dW, _ = fused(w, d, want=(True, True, False))
+    g1 = torch.full((w.N,), -1.0, device=DEV)
+    _, _, dH1, dW1, _ = fused(w, d, want=(True, True, False), g=g1)
+    # g = -1 is exactly 2^14 x the mean-loss upstream; the results scale exactly
+    # unless the small one falls into fp16's subnormal range (dH at g = -2^-14)
+    assert bits_equal(dW1, dW * 16384.0)
+    if dt == "bf16":
+        assert bits_equal(dH1, (dH.float() * 16384.0).to(dH1.dtype))
+    L = llp()
+    flogp, flse = L.linear_logp_fwd(d["h"], d["W"], d["b"], d["t"])
+    torch.cuda.synchronize()
+    assert bits_equal(logp, flogp) and bits_equal(lse, flse)
+    host = synth.make_linear_np(w)
+    tok = sample_tokens(w.N, w.chunk)
+    vr = sample_vocab(w.V, host["t"])
+    tl, tg = TOL[dt]["logp"], TOL[dt]["grad"]
+    g64 = -np.ones(w.N)
+    rl, rs, rh = O.linear_logp_token_rows(host["h64"][tok], host["W64"], host["b64"], host["t"][tok], g64[tok])
+    assert_close(logp[tok], rl, *tl, "logp")
+    assert_close(lse[tok], rs, *tl, "lse")
+    assert_close(dH1[tok], rh, *tg, "dH (g = -1)")
+    say(f"fused {dt} dH normalised error {norm_err(dH1[tok], rh):.2e}")
+    rw, _ = O.linear_logp_vocab_rows(host["h64"], host["W64"], host["b64"], host["t"], g64, vr)
+    assert_close(dW1[vr], rw, *tg, "dW (g = -1)")
+    say(f"fused {dt} dW normalised error {norm_err(dW1[vr], rw):.2e}")
+
+
+def test_fused_bias_big_vocab_default_chunk():
+    w = synth.BIAS_BIGV
+    d = synth.make_linear_t(w, DEV)
+    logp, lse, dH, dW, db = fused(w, d, chunk=0)
+    L = llp()
+    flogp, flse = L.linear_logp_fwd(d["h"], d["W"], d["b"], d["t"])
+    torch.cuda.synchronize()
+    assert bits_equal(logp, flogp) and bits_equal(lse, flse)
+    host = synth.make_linear_np(w)
+    tok = sample_tokens(w.N, 110)
+    vr = sample_vocab(w.V, host["t"])
+    tg = TOL["bf16"]["grad"]
+    _, _, rh = O.linear_logp_token_rows(host["h64"][tok], host["W64"], host["b64"], host["t"][tok], host["g64"][tok])
+    assert_close(dH[tok], rh, *tg, "dH")
+    rw, rb = O.linear_logp_vocab_rows(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], vr)
+    assert_close(dW[vr], rw, *tg, "dW")
+    assert_close(db[vr], rb, *tg, "db")
