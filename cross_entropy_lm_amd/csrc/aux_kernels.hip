@@ -12,31 +12,43 @@ namespace {
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Per token: merge the per-tile (m, s) partials in increasing tile order
-// (m in log2 units, s = sum of 2^(y - m)), then lse = (M + log2 S) ln 2 and
-// logp = z[t] - lse for a target in [0, V), else +0 (RL-Kernel PR #495,
-// "Behavior changes").
+// Per token: merge the per-block (m, s) partials (m in log2 units, s = sum of
+// 2^(y - m)), then lse = (M + log2 S) ln 2 and logp = z[t] - lse for a target
+// in [0, V), else +0 (RL-Kernel PR #495, "Behavior changes"). A block of 1024
+// threads takes 64 tokens; the 16 threads of a token merge the partials
+// i = j, j + 16, ... in increasing i, then the 16 results are merged in
+// increasing j: a fixed order that depends on neither the batch size nor the
+// chunking. Loads are coalesced over the 64 consecutive tokens.
 // With g and tcoef (fused forward + backward) it also writes the one-hot
 // part tcoef[n] = g (1 - p_t), p_t = 2^(z_t log2 e - lse log2 e), for a valid
 // token (0 <= t < V, g != 0), else +0.
-__global__ void lse_combine_kernel(const float2* __restrict__ partials, int64_t P, int64_t ldp,
-                                   const float* __restrict__ zt, const int64_t* __restrict__ targets,
-                                   int64_t V, int64_t N, float* __restrict__ logp,
-                                   float* __restrict__ lse, const float* __restrict__ g,
-                                   float* __restrict__ tcoef) {
-  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
-  float M = -INFINITY, S = 0.0f;
-  for (int64_t i = 0; i < P; ++i) {
-    const float2 q = partials[i * ldp + n];
-    if (q.x == -INFINITY) continue;
-    if (q.x > M) {
-      S = S * __builtin_amdgcn_exp2f(M - q.x) + q.y;
-      M = q.x;
-    } else {
-      S += q.y * __builtin_amdgcn_exp2f(q.x - M);
-    }
+constexpr int kCombTok = 64, kCombSl = 16;
+__device__ __forceinline__ void lse_merge(float& M, float& S, float m, float s) {
+  if (m == -INFINITY) return;
+  if (m > M) {
+    S = S * __builtin_amdgcn_exp2f(M - m) + s;
+    M = m;
+  } else {
+    S += s * __builtin_amdgcn_exp2f(m - M);
   }
+}
+__global__ __launch_bounds__(kCombTok * kCombSl) void lse_combine_kernel(
+    const float2* __restrict__ partials, int64_t P, int64_t ldp, const float* __restrict__ zt,
+    const int64_t* __restrict__ targets, int64_t V, int64_t N, float* __restrict__ logp,
+    float* __restrict__ lse, const float* __restrict__ g, float* __restrict__ tcoef) {
+  __shared__ float2 part[kCombSl][kCombTok];
+  const int tk = threadIdx.x % kCombTok, sl = threadIdx.x / kCombTok;
+  const int64_t n = (int64_t)blockIdx.x * kCombTok + tk;
+  float M = -INFINITY, S = 0.0f;
+  if (n < N)
+    for (int64_t i = sl; i < P; i += kCombSl) {
+      const float2 q = partials[i * ldp + n];
+      lse_merge(M, S, q.x, q.y);
+    }
+  part[sl][tk] = make_float2(M, S);
+  __syncthreads();
+  if (sl != 0 || n >= N) return;
+  for (int j = 1; j < kCombSl; ++j) lse_merge(M, S, part[j][tk].x, part[j][tk].y);
   const float l = (M + __builtin_amdgcn_logf(S)) * kLn2;
   if (lse != nullptr) lse[n] = l;
   const int64_t t = targets[n];
@@ -55,47 +67,90 @@ __global__ void lse_combine_kernel(const float2* __restrict__ partials, int64_t 
 //     d[v][n] = -(g_n / s) q 2^(m_b - lse_n log2 e)   for a valid token n, v != t_n,
 //     d[v][n] = +0                                      otherwise,
 // written in place over q and, transposed, into dS [n][v] (token-major, +0 in
-// the columns [V, round8(V))). 64 x 64 tiles, 256 threads.
+// the columns [V, round8(V)); skipped when dS is null). 64 x 64 tiles, 256
+// threads, 16-byte accesses along rows where the tile is complete.
 template <typename T>
-__global__ void softmax_grad_kernel(T* __restrict__ qt, int64_t ldq, const float2* __restrict__ partials,
-                                    int64_t ldp, const float* __restrict__ lse, const float* __restrict__ g,
-                                    const int64_t* __restrict__ targets, const float2* __restrict__ scales,
-                                    int chunk, int64_t V, int64_t C, T* __restrict__ dS, int64_t ldS) {
-  __shared__ T tile[64][65];
+__global__ __launch_bounds__(256) void softmax_grad_kernel(
+    T* __restrict__ qt, int64_t ldq, const float2* __restrict__ partials, int64_t ldp,
+    const float* __restrict__ lse, const float* __restrict__ g, const int64_t* __restrict__ targets,
+    const float2* __restrict__ scales, int chunk, int64_t V, int64_t C, T* __restrict__ dS, int64_t ldS) {
+  constexpr int kVec = 16 / (int)sizeof(T);  // elements per 16 bytes
+  constexpr int kCpr = 64 / kVec;            // 16-byte chunks per 64-element row
+  constexpr int kRpp = 256 / kCpr;           // rows per pass
+  typedef __attribute__((__vector_size__(16))) unsigned int u32x4;
+  __shared__ T tile[64][64 + kVec];
+  __shared__ float coef_s[64];
+  __shared__ int32_t t_s[64];
   const int64_t v0 = (int64_t)blockIdx.x * 64, n0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  // column n = n0 + tx: the token's factor; 64-row tiles never straddle a 128-row block
-  const int64_t n = n0 + tx;
-  float coef = 0.0f;  // -(g / s) 2^(m_b - lse log2 e), or 0 for a row that takes no part
-  int64_t t = -1;
-  if (n < C) {
-    t = targets[n];
-    const float gv = g[n];
-    if (t >= 0 && t < V && gv != 0.0f) {
-      const float m2 = partials[(v0 >> 7) * ldp + n].x;
-      const float f = (m2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m2 - lse[n] * kLog2e);
-      coef = -(gv * scales[chunk].y) * f;
-    } else {
-      t = -1;
+  if (threadIdx.x < 64) {
+    // column n: the token's factor -(g / s) 2^(m_b - lse log2 e); 64-row tiles lie in one 128-row block
+    const int64_t n = n0 + threadIdx.x;
+    float coef = 0.0f;
+    int32_t t = -1;
+    if (n < C) {
+      const int64_t tt = targets[n];
+      const float gv = g[n];
+      if (tt >= 0 && tt < V && gv != 0.0f) {
+        const float m2 = partials[(v0 >> 7) * ldp + n].x;
+        const float f = (m2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m2 - lse[n] * kLog2e);
+        coef = -(gv * scales[chunk].y) * f;
+        t = (int32_t)tt;
+      }
     }
+    coef_s[threadIdx.x] = coef;
+    t_s[threadIdx.x] = t;
   }
-  for (int i = ty; i < 64; i += 4) {
+  __syncthreads();
+  const int c = threadIdx.x % kCpr;
+  const bool full_n = n0 + (c + 1) * kVec <= C;
+  for (int i = threadIdx.x / kCpr; i < 64; i += kRpp) {
     const int64_t v = v0 + i;
-    if (v < V && n < C) {
-      T* q = qt + v * ldq + n;
-      const float d = (t >= 0 && v != t) ? coef * (float)*q : 0.0f;
-      *q = (T)d;
-      tile[i][tx] = (T)d;
+    T val[kVec];
+    if (v < V && full_n) {
+      T* q = qt + v * ldq + n0 + c * kVec;
+      *reinterpret_cast<u32x4*>(val) = *reinterpret_cast<const u32x4*>(q);
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const int nl = c * kVec + j;
+        const int32_t t = t_s[nl];
+        val[j] = (T)((t >= 0 && v != t) ? coef_s[nl] * (float)val[j] : 0.0f);
+      }
+      *reinterpret_cast<u32x4*>(q) = *reinterpret_cast<const u32x4*>(val);
     } else {
-      tile[i][tx] = (T)0;
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const int nl = c * kVec + j;
+        const int64_t n = n0 + nl;
+        val[j] = (T)0;
+        if (v < V && n < C) {
+          T* q = qt + v * ldq + n;
+          const int32_t t = t_s[nl];
+          val[j] = (T)((t >= 0 && v != t) ? coef_s[nl] * (float)*q : 0.0f);
+          *q = val[j];
+        }
+      }
     }
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) tile[i][c * kVec + j] = val[j];
   }
   if (dS == nullptr) return;  // uniform
   __syncthreads();
   const int64_t vpad = (V + 7) & ~int64_t(7);
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t nn = n0 + i, v = v0 + tx;
-    if (nn < C && v < vpad) dS[nn * ldS + v] = tile[tx][i];
+  const int64_t vs = v0 + c * kVec;  // this thread's kVec vocab columns of dS
+  for (int i = threadIdx.x / kCpr; i < 64; i += kRpp) {
+    const int64_t n = n0 + i;
+    if (n >= C || vs >= vpad) continue;
+    T val[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) val[j] = tile[c * kVec + j][i];
+    T* o = dS + n * ldS + vs;
+    if (vs + kVec <= vpad) {
+      *reinterpret_cast<u32x4*>(o) = *reinterpret_cast<const u32x4*>(val);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j)
+        if (vs + j < vpad) o[j] = val[j];
+    }
   }
 }
 
@@ -253,8 +308,8 @@ hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, co
                               const int64_t* targets, int64_t V, int64_t N, float* logp,
                               float* lse, const float* g, float* tcoef, hipStream_t s) {
   if (N == 0) return hipSuccess;
-  lse_combine_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(partials, P, ldp, zt, targets, V, N,
-                                                                 logp, lse, g, tcoef);
+  lse_combine_kernel<<<(unsigned)((N + kCombTok - 1) / kCombTok), kCombTok * kCombSl, 0, s>>>(
+      partials, P, ldp, zt, targets, V, N, logp, lse, g, tcoef);
   return hipGetLastError();
 }
 
