@@ -4,10 +4,13 @@
 Default workload: linear_logp forward + backward at N = 16384 tokens, D = 4096,
 V = 32000, bf16 operands, 2048-token chunks, FP32 dW table, no bias, mean-loss
 upstream g = -1/N (the fused linear cross-entropy benchmark of Liger-Kernel
-PR #1324, "Benchmark results"). A step is one linear_logp_fwd + one
-linear_logp_bwd (dH and dW, including the table's zero fill) through the C ABI
-on synthetic device-resident inputs. Other workloads (--workload) are
-parity-test shapes and the logits-only log-prob.
+PR #1324, "Benchmark results": one complete forward + backward training
+operation). A step is one forward + backward producing logp, lse, dH and dW
+(including the table's zero fill) through the C ABI on synthetic
+device-resident inputs. Both paths are gated against the oracle and timed:
+`fused` (linear_logp_fwd_bwd, one call, reported as `value` by default) and
+`split` (linear_logp_fwd then linear_logp_bwd, reported beside it). Other
+workloads (--workload) are parity-test shapes and the logits-only log-prob.
 
 Prints ONE JSON line (throughput, roofline of the dominant kernel from live
 per-kernel HIP-event timing, and the FP64 oracle timed on a bounded sample on
@@ -138,6 +141,40 @@ def blas_threads() -> int:
 
 
 # ----------------------------------------------------------------------------- linear
+PATHS = {
+    "fused": "linear_logp_fwd_bwd: one call, upstream g known at forward time (3 N x V x D contractions)",
+    "split": "linear_logp_fwd then linear_logp_bwd with the forward's lse (4 N x V x D contractions)",
+}
+
+
+def time_steps(step, args, torch, llp, stream):
+    """W untimed steps, then K steps bracketed by HIP events on the launch
+    stream; returns (ms per step, {kind: (total ms, launches)})."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    llp.llp_trace_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    llp.llp_trace_enable(False)
+    return e0.elapsed_time(e1) / args.steps, llp.llp_trace_read()
+
+
+def kernel_table(tr, steps, per_launch_flops):
+    kernels = {}
+    for k, (tms, cnt) in tr.items():
+        if cnt == 0:
+            continue
+        kernels[k] = {"ms_per_step": tms / steps, "launches_per_step": cnt / steps, "avg_launch_ms": tms / cnt}
+        if per_launch_flops.get(k):
+            kernels[k]["tflops"] = per_launch_flops[k] / (tms / cnt * 1e-3) / 1e12
+    return kernels
+
+
 def run_linear(w, args, torch, llp):
     dev = torch.device("cuda:0")
     chunk = args.chunk if args.chunk is not None else w.chunk
@@ -157,64 +194,57 @@ def run_linear(w, args, torch, llp):
     ws_f = torch.empty(max(1, llp.linear_logp_fwd_workspace_size(N, D, V, op_dt)), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(max(1, llp.linear_logp_bwd_workspace_size(N, D, V, op_dt, chunk, True, True, w.bias, True)),
                        dtype=torch.uint8, device=dev)
+    ws_x = torch.empty(max(1, llp.linear_logp_fwd_bwd_workspace_size(N, D, V, op_dt, chunk, True, True, w.bias,
+                                                                     True)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def split_step():
         llp.linear_logp_fwd(d["h"], d["W"], d["b"], d["t"], logp=logp, lse=lse, workspace=ws_f)
         llp.linear_logp_bwd(d["h"], d["W"], d["b"], d["t"], d["g"], lse, True, True, w.bias, chunk=chunk,
                             dH=dH, dW=dW, db=db, workspace=ws_b)
 
-    step()
-    torch.cuda.synchronize()
+    def fused_step():
+        llp.linear_logp_fwd_bwd(d["h"], d["W"], d["b"], d["t"], d["g"], True, True, w.bias, chunk=chunk,
+                                logp=logp, lse=lse, dH=dH, dW=dW, db=db, workspace=ws_x)
 
-    # correctness gate before timing (and the CPU baseline on the same sample)
+    # correctness gate before timing (and the CPU baseline on the same sample), for both paths
     cpu = None
-    if not args.no_gate or not args.no_cpu_baseline:
-        cpu = oracle_sample(w, args, logp, dH)
-
-    log(f"warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
-    for _ in range(args.warmup):
+    for name, step in (("split", split_step), ("fused", fused_step)):
         step()
-    torch.cuda.synchronize()
-    llp.llp_trace_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    llp.llp_trace_enable(False)
-    tr = llp.llp_trace_read()
-    ms = e0.elapsed_time(e1) / args.steps
+        torch.cuda.synchronize()
+        if not args.no_gate or not args.no_cpu_baseline:
+            cpu = oracle_sample(w, args, logp, dH, cpu, name)
 
     flops = A.linear_fwd_bwd_flops(N, D, V)
-    per_launch_flops = {
-        "fwd_lse": 2 * N * V * D,
-        "dlogits": 2 * N * V * D / K,
-        "dh_dw": 4 * N * V * D / K,
-    }
-    kernels = {}
-    for k, (tms, cnt) in tr.items():
-        if cnt == 0:
-            continue
-        kernels[k] = {"ms_per_step": tms / args.steps, "launches_per_step": cnt / args.steps,
-                      "avg_launch_ms": tms / cnt}
-        if k in per_launch_flops:
-            kernels[k]["tflops"] = per_launch_flops[k] / (tms / cnt * 1e-3) / 1e12
-    mfma = {k: v for k, v in kernels.items() if k in per_launch_flops}
-    dom = max(mfma, key=lambda k: mfma[k]["ms_per_step"])
+    model_flops = A.linear_model_flops(N, D, V)
     peak = PEAK_TFLOPS[w.dtype]
-    achieved = mfma[dom]["tflops"]
-    traffic = traffic_from_profiles(dom, w.name)
-    tokens_s = A.tokens_per_s(N, ms)
-    out = {
+    results = {}
+    for name, step, plf in (
+            ("split", split_step, {"fwd_lse": 2 * N * V * D, "dlogits": 2 * N * V * D / K,
+                                   "dh_dw": 4 * N * V * D / K}),
+            ("fused", fused_step, {"fwd_lse": 2 * N * V * D / K, "dh_dw": 4 * N * V * D / K})):
+        log(f"{name}: warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
+        ms, tr = time_steps(step, args, torch, llp, stream)
+        kernels = kernel_table(tr, args.steps, plf)
+        mfma = {k: v for k, v in kernels.items() if "tflops" in v}
+        results[name] = {
+            "ms_per_step": ms, "tokens_per_s": A.tokens_per_s(N, ms),
+            "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / (peak * 1e12),
+            "pct_mfma_peak_model_flops": 100.0 * model_flops / (ms * 1e-3) / (peak * 1e12),
+            "dominant": max(mfma, key=lambda k: mfma[k]["ms_per_step"]), "kernels": kernels}
+    main = results[args.path]
+    other = "split" if args.path == "fused" else "fused"
+    dom = main["dominant"]
+    achieved = main["kernels"][dom]["tflops"]
+    tokens_s = main["tokens_per_s"]
+    return {
         "metric": METRIC if w.name == "flce_bf16" else f"fwd+bwd tokens/s linear_logp {w.name}",
         "value": tokens_s,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": main["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": tokens_s / PAGES_TOKENS_PER_S if w.name == "flce_bf16" and args.table == "f32" else None,
@@ -223,32 +253,40 @@ def run_linear(w, args, torch, llp):
         "data": "synthetic (seeded counter-based generator; random-init weights)",
         "config": {"workload": w.name, "N": N, "D": D, "V": V, "chunk": C, "chunks": K,
                    "bias": w.bias, "g": w.g, "dW_table": args.table, "outputs": "logp,lse,dH,dW" +
-                   (",db" if w.bias else "")},
-        "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / (peak * 1e12),
-        "pct_mfma_peak_model_flops": 100.0 * A.linear_model_flops(N, D, V) / (ms * 1e-3) / (peak * 1e12),
+                   (",db" if w.bias else ""), "path": PATHS[args.path]},
+        "pct_mfma_peak": main["pct_mfma_peak"],
+        "pct_mfma_peak_model_flops": main["pct_mfma_peak_model_flops"],
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic},
-        "kernels": kernels,
+                     "frac": achieved / peak, "traffic": traffic_from_profiles(dom, w.name)},
+        "kernels": main["kernels"],
+        other: {"path": PATHS[other], **results[other]},
+        **({"cpu_baseline": {k: v for k, v in cpu.items() if not k.startswith("_")}}
+           if cpu is not None and not args.no_cpu_baseline else {}),
     }
-    if cpu is not None and not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu
-    return out
 
 
-def oracle_sample(w, args, logp, dH):
+def oracle_sample(w, args, logp, dH, prev=None, label=""):
     """FP64 oracle forward + backward (logp, dH, dW) on the first S tokens,
-    timed on the host cores; the GPU's logp and dH rows are gated against it."""
+    timed on the host cores once; each path's logp and dH rows are gated
+    against it."""
     from oracle import linear_logp as O
 
     S = min(args.cpu_sample_tokens, w.N)
-    rows = np.arange(S)
-    log(f"oracle sample: {S} tokens (host generation first)")
-    host = synth.make_linear_np(w, rows=rows)
-    t0 = time.perf_counter()
-    rlogp, _ = O.linear_logp_fwd(host["h64"], host["W64"], host["b64"], host["t"])
-    rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True, True,
-                                      w.bias)
-    dt = time.perf_counter() - t0
+    if prev is None:
+        rows = np.arange(S)
+        log(f"oracle sample: {S} tokens (host generation first)")
+        host = synth.make_linear_np(w, rows=rows)
+        t0 = time.perf_counter()
+        rlogp, _ = O.linear_logp_fwd(host["h64"], host["W64"], host["b64"], host["t"])
+        rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True,
+                                          True, w.bias)
+        dt = time.perf_counter() - t0
+        log(f"oracle {dt:.1f} s")
+        prev = {"value": S / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"first {S} tokens of {w.name}: FP64 numpy oracle forward + backward (logp, dH, dW)"
+                          f"{' + db' if w.bias else ''}, {dt:.2f} s",
+                "_ref": (rlogp, rdH)}
+    rlogp, rdH = prev["_ref"]
     gl = logp[:S].double().cpu().numpy()
     gh = dH[:S].double().cpu().numpy()
     tl = {"f32": (1e-5, 5e-4)}.get(w.dtype, (5e-3, 5e-2))
@@ -256,11 +294,9 @@ def oracle_sample(w, args, logp, dH):
     ok_l = np.all(np.abs(gl - rlogp) <= tl[0] + tl[1] * np.abs(rlogp))
     ok_h = np.all(np.abs(gh - rdH) <= tg[0] + tg[1] * np.abs(rdH))
     if not args.no_gate and not (ok_l and ok_h):
-        raise SystemExit(f"correctness gate failed: logp ok={ok_l} dH ok={ok_h}")
-    log(f"gate ok (logp, dH on {S} tokens); oracle {dt:.1f} s")
-    return {"value": S / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"first {S} tokens of {w.name}: FP64 numpy oracle forward + backward (logp, dH, dW)"
-                      f"{' + db' if w.bias else ''}, {dt:.2f} s"}
+        raise SystemExit(f"correctness gate failed ({label}): logp ok={ok_l} dH ok={ok_h}")
+    log(f"gate ok ({label}: logp, dH on {S} tokens)")
+    return prev
 
 
 # ----------------------------------------------------------------------------- logits only
@@ -342,6 +378,8 @@ def main():
     ap.add_argument("--workload", default="flce_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--chunk", type=int, default=None, help="tokens per backward chunk (default: the workload's)")
     ap.add_argument("--table", default="f32", choices=["f32", "op"], help="dW table dtype")
+    ap.add_argument("--path", default="fused", choices=["fused", "split"],
+                    help="path reported as `value` (the other is timed too and reported beside it)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gate", action="store_true")
