@@ -154,22 +154,47 @@ __global__ __launch_bounds__(256) void softmax_grad_kernel(
   }
 }
 
+// dst[c][r] = src[r][c] for r < rows, c < cols, and +0 in the padding columns
+// r in [rows, round8(rows)) of dst. 64 x 64 tiles through LDS, 256 threads;
+// 16-byte row segments on both sides where the tile is complete and aligned.
 template <typename T>
-__global__ void transpose_kernel(const T* __restrict__ src, int64_t rows, int64_t cols, int64_t lds,
-                                 T* __restrict__ dst, int64_t ldd) {
-  __shared__ T tile[64][65];
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
+                                                        int64_t lds, T* __restrict__ dst, int64_t ldd, int vec) {
+  constexpr int kVec = 16 / (int)sizeof(T);  // elements per 16 bytes
+  constexpr int kCpr = 64 / kVec;            // 16-byte chunks per 64-element row
+  constexpr int kRpp = 256 / kCpr;           // rows per pass
+  typedef __attribute__((__vector_size__(16))) unsigned int u32x4;
+  __shared__ T tile[64][64 + 2];
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    if (r < rows && c < cols) tile[i][tx] = src[r * lds + c];
+  const int ch = threadIdx.x % kCpr;
+  for (int i = threadIdx.x / kCpr; i < 64; i += kRpp) {
+    const int64_t r = r0 + i, c = c0 + ch * kVec;
+    T v[kVec];
+    if (vec && r < rows && c + kVec <= cols) {
+      *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(src + r * lds + c);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) v[j] = (r < rows && c + j < cols) ? src[r * lds + c + j] : (T)0;
+    }
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) tile[i][ch * kVec + j] = v[j];
   }
   __syncthreads();
   const int64_t rpad = (rows + 7) & ~int64_t(7);
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) dst[c * ldd + r] = tile[tx][i];
-    else if (c < cols && r < rpad) dst[c * ldd + r] = (T)0;
+  for (int i = threadIdx.x / kCpr; i < 64; i += kRpp) {
+    const int64_t c = c0 + i, r = r0 + ch * kVec;
+    if (c >= cols || r >= rpad) continue;
+    T v[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) v[j] = tile[ch * kVec + j][i];  // +0 past rows
+    T* o = dst + c * ldd + r;
+    if (vec && r + kVec <= rpad) {
+      *reinterpret_cast<u32x4*>(o) = *reinterpret_cast<const u32x4*>(v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j)
+        if (r + j < rpad) o[j] = v[j];
+    }
   }
 }
 
@@ -282,8 +307,12 @@ hipError_t transpose_t(const void* src, int64_t rows, int64_t cols, int64_t lds,
                        int64_t ldd, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
   dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((cols + 63) / 64));  // cols <= 2^22 (validated)
+  // 16-byte segments need 16-byte aligned bases and leading dimensions in whole segments
+  constexpr int64_t kVec = 16 / (int64_t)sizeof(T);
+  const int vec = (reinterpret_cast<uintptr_t>(src) % 16 == 0) && (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
+                  (lds % kVec == 0) && (ldd % kVec == 0);
   transpose_kernel<T><<<grid, 256, 0, s>>>(static_cast<const T*>(src), rows, cols, lds,
-                                           static_cast<T*>(dst), ldd);
+                                           static_cast<T*>(dst), ldd, vec);
   return hipGetLastError();
 }
 
