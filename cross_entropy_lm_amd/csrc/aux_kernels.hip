@@ -154,6 +154,35 @@ __global__ __launch_bounds__(256) void softmax_grad_kernel(
   }
 }
 
+// Vocabulary-parallel merge: per token, the P shares' (lse_r, zt_r) (zt_r =
+// -inf unless share r holds the target) in increasing r:
+// lse = M + log sum_r exp(lse_r - M), M = max_r lse_r; logp = zt_owner - lse
+// for a target in [0, Vt), else +0. A share with no finite lse (every logit
+// -inf) adds nothing.
+__global__ void shard_combine_kernel(const float* __restrict__ lse_sh, const float* __restrict__ zt_sh,
+                                     int64_t P, int64_t N, const int64_t* __restrict__ targets, int64_t Vt,
+                                     float* __restrict__ logp, float* __restrict__ lse) {
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float M = -INFINITY;
+  float zt = -INFINITY;
+  for (int64_t r = 0; r < P; ++r) {
+    M = fmaxf(M, lse_sh[r * N + n]);
+    const float z = zt_sh[r * N + n];
+    if (z != -INFINITY) zt = z;
+  }
+  float S = 0.0f;
+  if (M != -INFINITY)
+    for (int64_t r = 0; r < P; ++r) {
+      const float l = lse_sh[r * N + n];
+      if (l != -INFINITY) S += __builtin_amdgcn_exp2f((l - M) * kLog2e);
+    }
+  const float l = M + __builtin_amdgcn_logf(S) * kLn2;
+  if (lse != nullptr) lse[n] = l;
+  const int64_t t = targets[n];
+  if (logp != nullptr) logp[n] = (t >= 0 && t < Vt) ? zt - l : 0.0f;
+}
+
 // dst[c][r] = src[r][c] for r < rows, c < cols, and +0 in the padding columns
 // r in [rows, round8(rows)) of dst. 64 x 64 tiles through LDS, 256 threads;
 // 16-byte row segments on both sides where the tile is complete and aligned.
@@ -225,10 +254,13 @@ __global__ void chunk_scales_kernel(const float* __restrict__ g, int64_t N, int6
   }
 }
 
+// A token that takes part (0 <= t < Vt, g != 0) and whose target lies in the
+// vocabulary share [v0, v0 + V); t is returned as the local row.
 __device__ __forceinline__ bool tok_valid(const int64_t* targets, const float* g, int64_t tok,
-                                          int64_t V, int64_t& t) {
-  t = targets[tok];
-  return t >= 0 && t < V && g[tok] != 0.0f;
+                                          int64_t V, int64_t v0, int64_t Vt, int64_t& t) {
+  const int64_t tg = targets[tok];
+  t = tg - v0;
+  return tg >= 0 && tg < Vt && t >= 0 && t < V && g[tok] != 0.0f;
 }
 
 template <typename T, typename TT>
@@ -236,7 +268,8 @@ __global__ void db_accum_kernel(const T* __restrict__ dSt, int64_t ldSt, int64_t
                                 const float2* __restrict__ scales, int chunk,
                                 const int32_t* __restrict__ head, const int32_t* __restrict__ next,
                                 const int64_t* __restrict__ targets, const float* __restrict__ g,
-                                const float* __restrict__ tcoef, int64_t tok0, TT* __restrict__ db) {
+                                const float* __restrict__ tcoef, int64_t tok0, int64_t v0, int64_t Vt,
+                                TT* __restrict__ db) {
   const int lane = threadIdx.x & 63;
   const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (v >= V) return;  // uniform per wave
@@ -247,7 +280,7 @@ __global__ void db_accum_kernel(const T* __restrict__ dSt, int64_t ldSt, int64_t
     float val = s * scales[chunk].x;
     int32_t j = head[v];
     int64_t t;
-    if (j >= 0 && j < C && tok_valid(targets, g, tok0 + j, V, t) && t == v) {
+    if (j >= 0 && j < C && tok_valid(targets, g, tok0 + j, V, v0, Vt, t) && t == v) {
       for (int64_t it = 0; it < C && j >= 0 && j < C; ++it) {
         val += tcoef[tok0 + j];
         j = next[j];
@@ -262,18 +295,18 @@ __global__ void db_accum_kernel(const T* __restrict__ dSt, int64_t ldSt, int64_t
 // head[t], and every valid token writes next[n] (the first later valid token
 // with the same target, or -1). No atomics: the lists are in token order.
 __global__ void target_lists_kernel(const int64_t* __restrict__ targets, const float* __restrict__ g,
-                                    int64_t tok0, int64_t C, int64_t V, int32_t* __restrict__ head,
-                                    int32_t* __restrict__ next) {
+                                    int64_t tok0, int64_t C, int64_t V, int64_t v0, int64_t Vt,
+                                    int32_t* __restrict__ head, int32_t* __restrict__ next) {
   const int lane = threadIdx.x & 63;
   const int64_t n = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (n >= C) return;  // uniform per wave
   int64_t t;
-  if (!tok_valid(targets, g, tok0 + n, V, t)) return;
+  if (!tok_valid(targets, g, tok0 + n, V, v0, Vt, t)) return;
   bool earlier = false;
   int64_t nxt = INT64_MAX;
   for (int64_t j = lane; j < C; j += 64) {
     int64_t tj;
-    if (j != n && tok_valid(targets, g, tok0 + j, V, tj) && tj == t) {
+    if (j != n && tok_valid(targets, g, tok0 + j, V, v0, Vt, tj) && tj == t) {
       if (j < n) earlier = true;
       else if (j < nxt) nxt = j;
     }
@@ -292,9 +325,9 @@ __global__ void target_lists_kernel(const int64_t* __restrict__ targets, const f
   }
 }
 
-__global__ void zero_kernel(uint32_t* __restrict__ p, int64_t nwords) {
+__global__ void fill_kernel(uint32_t* __restrict__ p, int64_t nwords, uint32_t word) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) p[i] = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) p[i] = word;
 }
 
 __global__ void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n) {
@@ -319,15 +352,15 @@ hipError_t transpose_t(const void* src, int64_t rows, int64_t cols, int64_t lds,
 template <typename T>
 hipError_t db_t(const void* dSt, int64_t ldSt, int64_t V, int64_t C, const float2* scales, int chunk,
                 const int32_t* head, const int32_t* next, const int64_t* targets, const float* g,
-                const float* tcoef, int64_t tok0, void* db, int tdt, hipStream_t s) {
+                const float* tcoef, int64_t tok0, int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s) {
   dim3 grid((unsigned)((V + 3) / 4));
   if (tdt == DT_F32)
     db_accum_kernel<T, float><<<grid, 256, 0, s>>>(static_cast<const T*>(dSt), ldSt, V, C, scales, chunk,
-                                                   head, next, targets, g, tcoef, tok0,
+                                                   head, next, targets, g, tcoef, tok0, v0, Vt,
                                                    static_cast<float*>(db));
   else
     db_accum_kernel<T, T><<<grid, 256, 0, s>>>(static_cast<const T*>(dSt), ldSt, V, C, scales, chunk,
-                                               head, next, targets, g, tcoef, tok0, static_cast<T*>(db));
+                                               head, next, targets, g, tcoef, tok0, v0, Vt, static_cast<T*>(db));
   return hipGetLastError();
 }
 
@@ -339,6 +372,13 @@ hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, co
   if (N == 0) return hipSuccess;
   lse_combine_kernel<<<(unsigned)((N + kCombTok - 1) / kCombTok), kCombTok * kCombSl, 0, s>>>(
       partials, P, ldp, zt, targets, V, N, logp, lse, g, tcoef);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_combine(const float* lse_sh, const float* zt_sh, int64_t P, int64_t N,
+                                const int64_t* targets, int64_t Vt, float* logp, float* lse, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  shard_combine_kernel<<<(unsigned)((N + 255) / 256), 256, 0, s>>>(lse_sh, zt_sh, P, N, targets, Vt, logp, lse);
   return hipGetLastError();
 }
 
@@ -387,22 +427,23 @@ hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, 
 hipError_t launch_db_accum(int dt, const void* dSt, int64_t ldSt, int64_t V, int64_t C,
                            const float2* scales, int chunk, const int32_t* head, const int32_t* next,
                            const int64_t* targets, const float* g, const float* tcoef, int64_t tok0,
-                           void* db, int tdt, hipStream_t s) {
+                           int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s) {
   switch (dt) {
     case DT_F32:
-      return db_t<float>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, db, tdt, s);
+      return db_t<float>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, v0, Vt, db, tdt, s);
     case DT_BF16:
-      return db_t<__bf16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, db, tdt, s);
+      return db_t<__bf16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, v0, Vt, db, tdt, s);
     case DT_F16:
-      return db_t<_Float16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, db, tdt, s);
+      return db_t<_Float16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, v0, Vt, db, tdt,
+                            s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_target_lists(const int64_t* targets, const float* g, int64_t tok0, int64_t C,
-                               int64_t V, int32_t* head, int32_t* next, hipStream_t s) {
+                               int64_t V, int64_t v0, int64_t Vt, int32_t* head, int32_t* next, hipStream_t s) {
   if (C == 0) return hipSuccess;
-  target_lists_kernel<<<(unsigned)((C + 3) / 4), 256, 0, s>>>(targets, g, tok0, C, V, head, next);
+  target_lists_kernel<<<(unsigned)((C + 3) / 4), 256, 0, s>>>(targets, g, tok0, C, V, v0, Vt, head, next);
   return hipGetLastError();
 }
 
@@ -412,12 +453,19 @@ hipError_t launch_zero(void* p, int64_t n, int esize, hipStream_t s) {
   if (bytes % 4 == 0 && (reinterpret_cast<uintptr_t>(p) & 3) == 0) {
     const int64_t words = bytes / 4;
     const unsigned blocks = (unsigned)std::min<int64_t>((words + 255) / 256, 65536);
-    zero_kernel<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words);
+    fill_kernel<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), words, 0u);
   } else {
     const int64_t halves = bytes / 2;
     const unsigned blocks = (unsigned)std::min<int64_t>((halves + 255) / 256, 65536);
     zero_u16_kernel<<<blocks, 256, 0, s>>>(static_cast<uint16_t*>(p), halves);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill32(uint32_t* p, int64_t n, uint32_t word, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 65536);
+  fill_kernel<<<blocks, 256, 0, s>>>(p, n, word);
   return hipGetLastError();
 }
 

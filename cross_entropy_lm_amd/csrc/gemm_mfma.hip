@@ -176,7 +176,7 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, 
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     const int64_t n = n0 + f.col(ni);
-    tgt[ni] = (n < p.N) ? e.targets[e.tok0 + n] : -1;
+    tgt[ni] = (n < p.N) ? e.targets[e.tok0 + n] - e.v0 : -1;  // local row; matches only in this share
     mx[ni] = -INFINITY;
   }
 #pragma unroll
@@ -267,9 +267,10 @@ __device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int6
     const int64_t n = n0 + f.col(ni);
     const bool nv = n < p.N;
     const int64_t tok = e.tok0 + (nv ? n : 0);
-    tgt[ni] = nv ? e.targets[tok] : -1;
+    const int64_t tg = nv ? e.targets[tok] : -1;
+    tgt[ni] = tg - e.v0;  // local row of the target; matches only in the share holding it
     gv[ni] = nv ? e.g[tok] : 0.0f;
-    rv[ni] = nv && tgt[ni] >= 0 && tgt[ni] < p.M && gv[ni] != 0.0f;
+    rv[ni] = nv && tg >= 0 && tg < e.Vt && gv[ni] != 0.0f;
     gs[ni] = gv[ni] * inv;
     l2[ni] = nv ? e.lse[tok] * kLog2e : 0.0f;
   }
@@ -339,9 +340,12 @@ __device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int6
   }
 }
 
+// A token that takes part (0 <= t < Vt, g != 0) and whose target row lies in
+// this problem's share; t is returned as the local row.
 __device__ __forceinline__ bool token_valid(const EpiParams& e, int64_t tok, int64_t& t) {
-  t = e.targets[tok];
-  return t >= 0 && t < e.V && e.g[tok] != 0.0f;
+  const int64_t tg = e.targets[tok];
+  t = tg - e.v0;
+  return tg >= 0 && tg < e.Vt && t >= 0 && t < e.V && e.g[tok] != 0.0f;
 }
 
 // dH rows of the chunk: out[m, :] = s C[m, :] + tcoef[m] W[t_m, :]. The
@@ -352,6 +356,8 @@ __device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_
   char* smem = L.a[0];
   const EpiParams& e = p.ep;
   T* out = static_cast<T*>(e.out);
+  float* out32 = static_cast<float*>(e.out);  // out_dt == DT_F32: a share's partial dH
+  const bool f32 = e.out_dt == DT_F32 && !std::is_same<T, float>::value;
   const T* W = static_cast<const T*>(e.W);
   const float sc = e.scales[e.chunk].x;
   int32_t* ts = reinterpret_cast<int32_t*>(smem);
@@ -378,7 +384,11 @@ __device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_
         const int64_t n = n0 + f.col(ni);
         const float base = acc[mi][ni][r] * sc;
         const float withw = fmaf(c, ld_f32(wrow, n < p.N ? n : 0), base);
-        if (m < p.M && n < p.N) out[m * e.ldo + n] = (T)(tr >= 0 ? withw : base);
+        if (m < p.M && n < p.N) {
+          const float o = tr >= 0 ? withw : base;
+          if (f32) out32[m * e.ldo + n] = o;
+          else out[m * e.ldo + n] = (T)o;
+        }
       }
     }
 }

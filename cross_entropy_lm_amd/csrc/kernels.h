@@ -35,7 +35,12 @@ struct EpiParams {
   const int64_t* targets;  // [tokens], indexed tok0 + local token
   const float* g;          // [tokens] upstream gradient
   int64_t tok0;            // first token of this problem
-  int64_t V;
+  int64_t V;               // vocabulary rows of this problem (a share's rows when sharded)
+  // Vocabulary share: this problem's rows are [v0, v0 + V) of a vocabulary of
+  // Vt rows (unsharded: v0 = 0, Vt = V). A token takes part when 0 <= t < Vt
+  // and g != 0; its one-hot terms belong to the share holding t.
+  int64_t v0;
+  int64_t Vt;
   // EPI_LSE_PARTIAL (M = vocab, N = tokens)
   float2* partials;        // [kWaveM * tiles_m][ldp]: (max * log2 e, sum exp2) per wave-row block
   int64_t ldp;
@@ -113,16 +118,21 @@ hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, 
 hipError_t launch_db_accum(int dt, const void* dSt, int64_t ldSt, int64_t V, int64_t C,
                            const float2* scales, int chunk, const int32_t* head, const int32_t* next,
                            const int64_t* targets, const float* g, const float* tcoef, int64_t tok0,
-                           void* db, int tdt, hipStream_t s);
+                           int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s);
 
 // Per chunk [tok0, tok0 + C): head[t] = first valid token with target t and
 // next[n] = the following one (-1 at the end), local indices, in token order.
 // Only head entries of targets present in the chunk are written.
 hipError_t launch_target_lists(const int64_t* targets, const float* g, int64_t tok0, int64_t C,
-                               int64_t V, int32_t* head, int32_t* next, hipStream_t s);
+                               int64_t V, int64_t v0, int64_t Vt, int32_t* head, int32_t* next, hipStream_t s);
+// Merge of P vocabulary shares' (lse, target logit) per token -> logp, lse.
+hipError_t launch_shard_combine(const float* lse_sh, const float* zt_sh, int64_t P, int64_t N,
+                                const int64_t* targets, int64_t Vt, float* logp, float* lse, hipStream_t s);
 
 // Fill n elements of size esize with +0.
 hipError_t launch_zero(void* p, int64_t n, int esize, hipStream_t s);
+// Fill n 4-byte words (p 4-byte aligned) with the bit pattern `word`.
+hipError_t launch_fill32(uint32_t* p, int64_t n, uint32_t word, hipStream_t s);
 
 // Logits-only rows.
 hipError_t launch_rows_fwd(int dt, const void* logits, int64_t N, int64_t V,

@@ -93,6 +93,9 @@ GemmProblem logits_problem(int64_t tok0, int64_t n, int64_t D, int64_t V, int dt
   p.tiles_m = (int)ceil_div(V, kTile);
   p.tiles_n = (int)ceil_div(n, kTile);
   p.dma = dma_ok(p, e, false);
+  p.ep.V = V;
+  p.ep.v0 = 0;  // the whole vocabulary unless the caller names a share
+  p.ep.Vt = V;
   return p;
 }
 
@@ -189,7 +192,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
                   const void* W, const void* b, const int64_t* targets, const float* g,
                   const float* lse, float* logp_out, float* lse_out, void* dH, void* dW, int dW_dtype,
                   void* db, int accumulate, void* workspace, size_t workspace_bytes, void* stream,
-                  bool fused) {
+                  bool fused, int64_t v0 = 0, int64_t Vt = -1, int dH_dtype = -1) {
+  if (Vt < 0) Vt = V;
+  if (dH_dtype < 0) dH_dtype = dtype;
   const bool want_dH = dH != nullptr, want_dW = dW != nullptr, want_db = db != nullptr;
   BwdPlan bp;
   const bool have_lse = fused ? lse_out != nullptr : lse != nullptr;
@@ -197,6 +202,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   if (st != LLP_OK) return st;
   if (accumulate != 0 && accumulate != 1) return LLP_EINVAL;
   if ((want_dW || want_db) && !(dW_dtype == LLP_F32 || dW_dtype == dtype)) return LLP_EINVAL;
+  if (want_dH && !(dH_dtype == LLP_F32 || dH_dtype == dtype)) return LLP_EINVAL;
   if (want_db && b == nullptr) return LLP_EINVAL;
   if (N > 0 && (want_dH || want_dW || want_db) &&
       (h == nullptr || W == nullptr || targets == nullptr || g == nullptr))
@@ -245,7 +251,8 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     p.ep.bias = b;
     p.ep.targets = targets;
     p.ep.tok0 = c0;
-    p.ep.V = V;
+    p.ep.v0 = v0;
+    p.ep.Vt = Vt;
     if (fused) {
       // the chunk's logits tile: lse partials, target logits, softmax numerators
       p.epi = EPI_LSE_Q;
@@ -275,10 +282,10 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     }
     if (want_dW)
       LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, static_cast<const char*>(h) + c0 * D * e, Ck, D, D, ht, bp.ldSt, s));
-    if (want_dW || want_db) LLP_LAUNCH(LLP_K_SMALL, launch_target_lists(targets, g, c0, Ck, V, head, next, s));
+    if (want_dW || want_db) LLP_LAUNCH(LLP_K_SMALL, launch_target_lists(targets, g, c0, Ck, V, v0, Vt, head, next, s));
     if (want_db)
       LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, bp.ldSt, V, Ck, scales, (int)k, head, next, targets, g, tcoef,
-                              c0, db, dW_dtype, s));
+                              c0, v0, Vt, db, dW_dtype, s));
     GemmProblem ph = {}, pw = {};
     if (want_dH) {
       ph.A = dS;
@@ -293,13 +300,15 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       ph.tiles_m = (int)ceil_div(Ck, kTile);
       ph.tiles_n = (int)ceil_div(D, kTile);
       ph.epi = EPI_STORE;
-      ph.ep.out = static_cast<char*>(dH) + c0 * D * e;
+      ph.ep.out = static_cast<char*>(dH) + c0 * D * (dH_dtype == LLP_F32 ? 4 : e);
       ph.ep.ldo = D;
-      ph.ep.out_dt = dtype;
+      ph.ep.out_dt = dH_dtype;
       ph.ep.targets = targets;
       ph.ep.g = g;
       ph.ep.tok0 = c0;
       ph.ep.V = V;
+      ph.ep.v0 = v0;
+      ph.ep.Vt = Vt;
       ph.ep.tcoef = tcoef;
       ph.ep.W = W;
       ph.ep.ldW = D;
@@ -326,6 +335,8 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.g = g;
       pw.ep.tok0 = c0;
       pw.ep.V = V;
+      pw.ep.v0 = v0;
+      pw.ep.Vt = Vt;
       pw.ep.tcoef = tcoef;
       pw.ep.h = h;
       pw.ep.ldh = D;
@@ -378,6 +389,61 @@ int linear_logp_fwd_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chun
   }
   return backward_impl(N, D, V, dtype, chunk, h, W, b, targets, g, nullptr, logp, lse, dH, dW, dW_dtype, db,
                        accumulate, workspace, workspace_bytes, stream, true);
+}
+
+int linear_logp_shard_fwd(int64_t N, int64_t D, int64_t Vs, int64_t v0, int64_t Vt, int dtype, const void* h,
+                          const void* W, const void* b, const int64_t* targets, float* lse_shard, float* zt_shard,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  FwdPlan fp;
+  int st = plan_fwd(N, D, Vs, dtype, &fp);
+  if (st != LLP_OK) return st;
+  if (v0 < 0 || Vt < 1 || v0 > Vt - Vs) return LLP_EINVAL;
+  if (N == 0) return LLP_OK;
+  if (h == nullptr || W == nullptr || targets == nullptr || lse_shard == nullptr || zt_shard == nullptr)
+    return LLP_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(zt_shard) & 3) != 0) return LLP_EINVAL;
+  if ((size_t)fp.bytes > workspace_bytes || (fp.bytes > 0 && workspace == nullptr)) return LLP_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float2* partials = reinterpret_cast<float2*>(at(workspace, fp.off_partials));
+  // -inf marks "target not in this share"; the tile holding the target overwrites it
+  LLP_LAUNCH(LLP_K_SMALL, launch_fill32(reinterpret_cast<uint32_t*>(zt_shard), N, 0xFF800000u, s));
+  GemmProblem p = logits_problem(0, N, D, Vs, dtype, h, W);
+  p.epi = EPI_LSE_PARTIAL;
+  p.ep.bias = b;
+  p.ep.targets = targets;
+  p.ep.tok0 = 0;
+  p.ep.v0 = v0;
+  p.ep.Vt = Vt;
+  p.ep.partials = partials;
+  p.ep.ldp = N;
+  p.ep.zt = zt_shard;
+  LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &p, nullptr, s));
+  LLP_LAUNCH(LLP_K_COMBINE,
+             launch_lse_combine(partials, fp.P, N, zt_shard, targets, Vs, N, nullptr, lse_shard, nullptr, nullptr, s));
+  return LLP_OK;
+}
+
+int linear_logp_shard_combine(int64_t N, int64_t P, const float* lse_shards, const float* zt_shards,
+                              const int64_t* targets, int64_t Vt, float* logp, float* lse, void* stream) {
+  if (N < 0 || P < 1 || Vt < 1) return LLP_EINVAL;
+  if (N > (INT64_MAX / 4) / P) return LLP_EOVERFLOW;
+  if (N == 0) return LLP_OK;
+  if (lse_shards == nullptr || zt_shards == nullptr || targets == nullptr || (logp == nullptr && lse == nullptr))
+    return LLP_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LLP_LAUNCH(LLP_K_COMBINE, launch_shard_combine(lse_shards, zt_shards, P, N, targets, Vt, logp, lse, s));
+  return LLP_OK;
+}
+
+int linear_logp_shard_bwd(int64_t N, int64_t D, int64_t Vs, int64_t v0, int64_t Vt, int dtype, int64_t chunk,
+                          const void* h, const void* W, const void* b, const int64_t* targets, const float* g,
+                          const float* lse, void* dH, int dH_dtype, void* dW, int dW_dtype, void* db,
+                          int accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+  if (v0 < 0 || Vs < 1 || Vt < 1 || v0 > Vt - Vs) return LLP_EINVAL;
+  if (N > 0 && lse == nullptr && (dH != nullptr || dW != nullptr || db != nullptr)) return LLP_EINVAL;
+  return backward_impl(N, D, Vs, dtype, chunk, h, W, b, targets, g, lse, nullptr, nullptr, dH, dW, dW_dtype, db,
+                       accumulate, workspace, workspace_bytes, stream, false, v0, Vt,
+                       dH != nullptr ? dH_dtype : dtype);
 }
 
 int logp_fwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t* targets, float* logp,

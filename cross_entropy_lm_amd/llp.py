@@ -38,6 +38,11 @@ SIGNATURES = {
                                                   ctypes.POINTER(_sz)]),
     "linear_logp_fwd_bwd": (_int, [_i64, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _int, _vp, _int, _vp, _sz, _vp]),
+    "linear_logp_shard_fwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _sz, _vp]),
+    "linear_logp_shard_combine": (_int, [_i64, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
+    "linear_logp_shard_bwd": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _int, _vp, _int, _vp, _int, _vp, _sz, _vp]),
     "logp_fwd": (_int, [_i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
     "logp_bwd": (_int, [_i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "llp_trace_enable": (_int, [_int]),
@@ -242,6 +247,86 @@ def linear_logp_fwd_bwd(h, W, b, targets, g, want_dH=True, want_dW=True, want_db
                                    _stream(stream))
     _check(st, "linear_logp_fwd_bwd")
     return logp, lse, dH, dW, db
+
+
+def linear_logp_shard_fwd(h, W_shard, b_shard, targets, v0, Vt, lse_shard=None, zt_shard=None,
+                          workspace=None, stream=None):
+    """(lse_shard [N], zt_shard [N]) of the vocabulary share W_shard = rows [v0, v0 + Vs) of a
+    Vt-row vocabulary; zt_shard is -inf where the share does not hold the target."""
+    torch = _torch()
+    for t, n in ((h, "h"), (W_shard, "W_shard"), (b_shard, "b_shard"), (targets, "targets")):
+        _contig(t, n)
+    N, D = h.shape
+    Vs = W_shard.shape[0]
+    dt = dtype_code(h.dtype)
+    if lse_shard is None:
+        lse_shard = torch.empty(N, dtype=torch.float32, device=h.device)
+    if zt_shard is None:
+        zt_shard = torch.empty(N, dtype=torch.float32, device=h.device)
+    nbytes = linear_logp_fwd_workspace_size(N, D, Vs, dt)
+    ws = _workspace(nbytes, workspace, h.device)
+    st = lib().linear_logp_shard_fwd(N, D, Vs, v0, Vt, dt, _ptr(h), _ptr(W_shard), _ptr(b_shard),
+                                     _ptr(targets), _ptr(lse_shard), _ptr(zt_shard), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "linear_logp_shard_fwd")
+    return lse_shard, zt_shard
+
+
+def linear_logp_shard_combine(lse_shards, zt_shards, targets, Vt, logp=None, lse=None, want_lse=True,
+                              stream=None):
+    """(logp [N], lse [N]) from the shares' [P, N] lse and target-logit rows."""
+    torch = _torch()
+    for t, n in ((lse_shards, "lse_shards"), (zt_shards, "zt_shards"), (targets, "targets")):
+        _contig(t, n)
+    P, N = lse_shards.shape
+    if tuple(zt_shards.shape) != (P, N):
+        raise ValueError("zt_shards must have the shape of lse_shards")
+    dev = lse_shards.device
+    if logp is None:
+        logp = torch.empty(N, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(N, dtype=torch.float32, device=dev)
+    st = lib().linear_logp_shard_combine(N, P, _ptr(lse_shards), _ptr(zt_shards), _ptr(targets), Vt,
+                                         _ptr(logp), _ptr(lse), _stream(stream))
+    _check(st, "linear_logp_shard_combine")
+    return logp, lse
+
+
+def linear_logp_shard_bwd(h, W_shard, b_shard, targets, g, lse, v0, Vt, want_dH=True, want_dW=True,
+                          want_db=False, dH_dtype=None, dW_dtype=None, chunk=0, accumulate=False, dH=None,
+                          dW=None, db=None, workspace=None, stream=None):
+    """(dH partial [N, D], dW_shard [Vs, D], db_shard [Vs]) of one vocabulary share, given the
+    global lse. ``dH_dtype`` is float32 by default (the partials are summed by the caller)."""
+    torch = _torch()
+    for t, n in ((h, "h"), (W_shard, "W_shard"), (b_shard, "b_shard"), (targets, "targets"), (g, "g"),
+                 (lse, "lse")):
+        _contig(t, n)
+    N, D = h.shape
+    Vs = W_shard.shape[0]
+    dt = dtype_code(h.dtype)
+    tdt = torch.float32 if dW_dtype is None else dW_dtype
+    hdt = torch.float32 if dH_dtype is None else dH_dtype
+    if want_dH and dH is None:
+        dH = torch.empty((N, D), dtype=hdt, device=h.device)
+    if dH is not None:
+        hdt = dH.dtype
+    if want_dW and dW is None:
+        dW = (torch.zeros if accumulate else torch.empty)((Vs, D), dtype=tdt, device=h.device)
+    if want_db and db is None:
+        db = (torch.zeros if accumulate else torch.empty)((Vs,), dtype=tdt, device=h.device)
+    if dW is not None:
+        tdt = dW.dtype
+    elif db is not None:
+        tdt = db.dtype
+    nbytes = linear_logp_bwd_workspace_size(N, D, Vs, dt, chunk, dH is not None, dW is not None,
+                                            db is not None, True)
+    ws = _workspace(nbytes, workspace, h.device)
+    st = lib().linear_logp_shard_bwd(N, D, Vs, v0, Vt, dt, chunk, _ptr(h), _ptr(W_shard), _ptr(b_shard),
+                                     _ptr(targets), _ptr(g), _ptr(lse), _ptr(dH), dtype_code(hdt), _ptr(dW),
+                                     dtype_code(tdt), _ptr(db), int(bool(accumulate)), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "linear_logp_shard_bwd")
+    return dH, dW, db
 
 
 def logp_fwd(logits, targets, logp=None, lse=None, want_lse=True, stream=None):

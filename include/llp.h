@@ -168,6 +168,58 @@ LLP_API int linear_logp_fwd_bwd(int64_t N, int64_t D, int64_t V, int dtype, int6
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Vocabulary-parallel share. A vocabulary of Vt rows is split into P
+ * contiguous shares; a share holds rows [v0, v0 + Vs) of W (W_shard [Vs, D],
+ * b_shard [Vs] or NULL) and sees every token. The pages name a tensor-parallel
+ * variant of this operator without describing it (RL-Kernel issue #261,
+ * "Non-goals and overlap"); these calls are the one-device part of it, built
+ * on the associativity of log-sum-exp: lse = log sum_r exp(lse_r) over the
+ * shares' lse_r, and the target logit lives in exactly one share. The
+ * exchange between devices (an all-gather or all-reduce of 8 bytes per token
+ * per share forward, a sum of the dH partials backward) is the caller's.
+ * Targets are global rows: a token takes part when 0 <= t < Vt (else it gets
+ * logp = +0 and zero gradients, as above); v0 >= 0, Vs >= 1, v0 + Vs <= Vt.
+ *
+ * linear_logp_shard_fwd: lse_shard [N] = log sum over the share's rows of
+ * exp(z), and zt_shard [N] = the target logit z[n, t_n] where the share holds
+ * t_n, else -inf (both float32, required). Workspace: the size
+ * linear_logp_fwd_workspace_size(N, D, Vs, dtype) reports.
+ */
+LLP_API int linear_logp_shard_fwd(int64_t N, int64_t D, int64_t Vs, int64_t v0, int64_t Vt, int dtype,
+                          const void* h, const void* W_shard, const void* b_shard,
+                          const int64_t* targets, float* lse_shard, float* zt_shard,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge of P shares' forward results, share-major: lse_shards [P][N] and
+ * zt_shards [P][N] (row r from the share r; any order of shares gives the
+ * same lse up to rounding, a fixed order gives the same bits). lse [N] =
+ * M + log sum_r exp(lse_r - M) with M = max_r lse_r, summed in increasing r;
+ * logp [N] = zt - lse for 0 <= t < Vt (zt: the one finite zt_r), else +0.
+ * Either output may be NULL, not both. No workspace.
+ */
+LLP_API int linear_logp_shard_combine(int64_t N, int64_t P, const float* lse_shards,
+                              const float* zt_shards, const int64_t* targets, int64_t Vt,
+                              float* logp, float* lse, void* stream);
+
+/*
+ * Backward of one share, given the global lse [N] (required, from
+ * linear_logp_shard_combine) and g [N]. dH [N, D] or NULL receives this
+ * share's PARTIAL dH = dlogits[:, v0:v0+Vs] W_shard, of dH_dtype (LLP_F32 or
+ * the operand dtype; float32 keeps the sum over shares exact to float32
+ * rounding); the caller sums the P partials. dW_shard [Vs, D] and db_shard
+ * [Vs] are this share's rows of dW and db, complete (they need no exchange),
+ * with dW_dtype, accumulate and chunk as in linear_logp_bwd. Workspace: the
+ * size linear_logp_bwd_workspace_size(N, D, Vs, dtype, chunk, want_dH,
+ * want_dW, want_db, 1) reports. Deterministic.
+ */
+LLP_API int linear_logp_shard_bwd(int64_t N, int64_t D, int64_t Vs, int64_t v0, int64_t Vt, int dtype,
+                          int64_t chunk, const void* h, const void* W_shard, const void* b_shard,
+                          const int64_t* targets, const float* g, const float* lse,
+                          void* dH, int dH_dtype, void* dW_shard, int dW_dtype, void* db_shard,
+                          int accumulate, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Logits-only forward (RL-Kernel PR #495): logits [N, V] of dtype ->
  * logp [N] (required), lse [N] (NULL to skip). One read of the logits.
  */

@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 17
     L = llp.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -161,6 +161,45 @@ def test_fused_argument_errors_and_workspace():
     # N = 0 with accumulate: nothing to do, null pointers allowed
     assert llp.lib().linear_logp_fwd_bwd(0, 128, 1024, F32, 0, None, None, None, None, None, None, None, None,
                                          None, F32, None, 1, None, 0, None) == llp.LLP_OK
+
+
+def _sfwd(N=256, D=128, Vs=400, v0=400, Vt=1031, dt=F32, h=FAKE, W=FAKE, b=FAKE, t=FAKE, lse=FAKE, zt=FAKE,
+          ws=FAKE, nbytes=1 << 40):
+    return llp.lib().linear_logp_shard_fwd(N, D, Vs, v0, Vt, dt, h, W, b, t, lse, zt, ws, nbytes, None)
+
+
+def _sbwd(N=256, D=128, Vs=400, v0=400, Vt=1031, dt=F32, chunk=64, h=FAKE, W=FAKE, b=FAKE, t=FAKE, g=FAKE,
+          lse=FAKE, dH=FAKE, hdt=F32, dW=FAKE, tdt=F32, db=FAKE, acc=0, ws=FAKE, nbytes=1 << 40):
+    return llp.lib().linear_logp_shard_bwd(N, D, Vs, v0, Vt, dt, chunk, h, W, b, t, g, lse, dH, hdt, dW, tdt, db,
+                                           acc, ws, nbytes, None)
+
+
+def test_shard_argument_errors():
+    E = llp.LLP_EINVAL
+    # the share must lie inside the vocabulary
+    for kw in (dict(v0=-1), dict(v0=632), dict(Vt=0), dict(Vs=0), dict(Vs=1032, v0=0)):
+        assert _sfwd(**kw) == E, kw
+        assert _sbwd(**kw) == E, kw
+    assert _sfwd(lse=None) == E and _sfwd(zt=None) == E and _sfwd(h=None) == E
+    assert _sfwd(zt=FAKE + 2) == E  # zt_shard must be 4-byte aligned
+    need = llp.linear_logp_fwd_workspace_size(256, 128, 400, F32)
+    assert _sfwd(nbytes=need - 1) == llp.LLP_EWORKSPACE
+    assert _sfwd(N=1 << 31) == llp.LLP_EOVERFLOW
+    assert _sbwd(lse=None) == E        # the global lse is required
+    assert _sbwd(hdt=F16) == E         # dH partial: float32 or the operand dtype
+    assert _sbwd(tdt=BF16) == E
+    assert _sbwd(b=None) == E
+    assert _sbwd(acc=2) == E
+    bneed = llp.linear_logp_bwd_workspace_size(256, 128, 400, F32, 64, True, True, True, True)
+    assert _sbwd(nbytes=bneed - 1) == llp.LLP_EWORKSPACE
+    comb = llp.lib().linear_logp_shard_combine
+    assert comb(-1, 2, FAKE, FAKE, FAKE, 1031, FAKE, FAKE, None) == E
+    assert comb(256, 0, FAKE, FAKE, FAKE, 1031, FAKE, FAKE, None) == E
+    assert comb(256, 2, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == E
+    assert comb(256, 2, None, FAKE, FAKE, 1031, FAKE, FAKE, None) == E
+    assert comb(256, 2, FAKE, FAKE, FAKE, 1031, None, None, None) == E
+    assert comb(1 << 60, 8, FAKE, FAKE, FAKE, 1031, FAKE, FAKE, None) == llp.LLP_EOVERFLOW
+    assert comb(0, 3, None, None, None, 1031, None, None, None) == llp.LLP_OK
 
 
 def test_header_documents_each_entry_point():
