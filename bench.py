@@ -355,6 +355,20 @@ def run_logits(w, args, torch, llp):
                           "GBps": nbytes[k] / (tms / cnt * 1e-3) / 1e9}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     total = A.logits_only_bytes(N, V, 2)
+    # the backward for a caller that kept no lse: the row is reduced, then
+    # written (two reads, one write); its dlogits equal the saved-lse ones bit for bit
+    dl2 = torch.empty_like(dl)
+    llp.logp_bwd(d["logits"], d["t"], d["g"], None, dlogits=dl2)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(dl.view(torch.int16), dl2.view(torch.int16)))
+    if not same and not args.no_gate:
+        raise SystemExit("correctness gate failed (logits-only backward without lse)")
+    e0.record(stream)
+    for _ in range(args.steps):
+        llp.logp_bwd(d["logits"], d["t"], d["g"], None, dlogits=dl2)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_nolse = e0.elapsed_time(e1) / args.steps
     return {
         "metric": "fwd+bwd logits-only logp N32768 V151936 bf16; GB/s",
         "value": total / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -365,6 +379,8 @@ def run_logits(w, args, torch, llp):
                      "unit": "GB/s", "frac": kernels[dom]["GBps"] / PEAK_HBM_GBS,
                      "traffic": traffic_from_profiles(dom, w.name)},
         "kernels": kernels,
+        "bwd_without_lse": {"ms": ms_nolse, "GBps": 3 * N * V * 2 / (ms_nolse * 1e-3) / 1e9,
+                            "bytes": "2 reads + 1 write of the logits", "bitwise_equal_to_saved_lse": same},
         "cpu_baseline": {"value": S * V * 3 * 2 / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                          "sample": f"first {S} rows: FP64 numpy oracle logp + dlogits, {dt:.2f} s"},
     }

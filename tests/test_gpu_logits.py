@@ -49,6 +49,8 @@ def test_logits_only_matches_oracle(dt, N, V):
     assert_close(lse, rlse, *tl, "lse")
     assert_close(dl, rd, *tg, "dlogits")
     assert_close(dl2, rd, *tg, "dlogits (lse recomputed)")
+    # the backward that keeps no residual reduces the row exactly as the forward does
+    assert bits_equal(dl, dl2)
 
 
 def test_out_of_range_targets_and_masked_tail():
