@@ -70,10 +70,32 @@ __global__ __launch_bounds__(kCombTok * kCombSl) void lse_combine_kernel(
 // the columns [V, round8(V)); skipped when dS is null). 64 x 64 tiles, 256
 // threads, 16-byte accesses along rows where the tile is complete.
 template <typename T>
-__global__ __launch_bounds__(256) void softmax_grad_kernel(
-    T* __restrict__ qt, int64_t ldq, const float2* __restrict__ partials, int64_t ldp,
-    const float* __restrict__ lse, const float* __restrict__ g, const int64_t* __restrict__ targets,
-    const float2* __restrict__ scales, int chunk, int64_t V, int64_t C, T* __restrict__ dS, int64_t ldS) {
+struct SoftmaxGradArgs {
+  T* qt;
+  int64_t ldq;
+  const float2* partials;
+  int64_t ldp;
+  const float* lse;
+  const float* g;
+  const int64_t* targets;
+  const float2* scales;
+  int chunk;
+  int64_t V, C;
+  T* dS;
+  int64_t ldS;
+};
+
+template <typename T>
+__device__ __forceinline__ void softmax_grad_tile(int64_t bx, int64_t by, const SoftmaxGradArgs<T>& a) {
+  T* __restrict__ qt = a.qt;
+  const int64_t ldq = a.ldq, ldp = a.ldp, V = a.V, C = a.C, ldS = a.ldS;
+  const float2* __restrict__ partials = a.partials;
+  const float* __restrict__ lse = a.lse;
+  const float* __restrict__ g = a.g;
+  const int64_t* __restrict__ targets = a.targets;
+  const float2* __restrict__ scales = a.scales;
+  const int chunk = a.chunk;
+  T* __restrict__ dS = a.dS;
   constexpr int kVec = 16 / (int)sizeof(T);  // elements per 16 bytes
   constexpr int kCpr = 64 / kVec;            // 16-byte chunks per 64-element row
   constexpr int kRpp = 256 / kCpr;           // rows per pass
@@ -81,7 +103,7 @@ __global__ __launch_bounds__(256) void softmax_grad_kernel(
   __shared__ T tile[64][64 + kVec];
   __shared__ float coef_s[64];
   __shared__ int32_t t_s[64];
-  const int64_t v0 = (int64_t)blockIdx.x * 64, n0 = (int64_t)blockIdx.y * 64;
+  const int64_t v0 = bx * 64, n0 = by * 64;
   if (threadIdx.x < 64) {
     // column n: the token's factor -(g / s) 2^(m_b - lse log2 e); 64-row tiles lie in one 128-row block
     const int64_t n = n0 + threadIdx.x;
@@ -154,6 +176,11 @@ __global__ __launch_bounds__(256) void softmax_grad_kernel(
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void softmax_grad_kernel(SoftmaxGradArgs<T> a) {
+  softmax_grad_tile<T>(blockIdx.x, blockIdx.y, a);
+}
+
 // Vocabulary-parallel merge: per token, the P shares' (lse_r, zt_r) (zt_r =
 // -inf unless share r holds the target) in increasing r:
 // lse = M + log sum_r exp(lse_r - M), M = max_r lse_r; logp = zt_owner - lse
@@ -187,14 +214,26 @@ __global__ void shard_combine_kernel(const float* __restrict__ lse_sh, const flo
 // r in [rows, round8(rows)) of dst. 64 x 64 tiles through LDS, 256 threads;
 // 16-byte row segments on both sides where the tile is complete and aligned.
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
-                                                        int64_t lds, T* __restrict__ dst, int64_t ldd, int vec) {
+struct TransposeArgs {
+  const T* src;
+  int64_t rows, cols, lds;
+  T* dst;
+  int64_t ldd;
+  int vec;
+};
+
+template <typename T>
+__device__ __forceinline__ void transpose_tile(int64_t bx, int64_t by, const TransposeArgs<T>& a) {
+  const T* __restrict__ src = a.src;
+  T* __restrict__ dst = a.dst;
+  const int64_t rows = a.rows, cols = a.cols, lds = a.lds, ldd = a.ldd;
+  const int vec = a.vec;
   constexpr int kVec = 16 / (int)sizeof(T);  // elements per 16 bytes
   constexpr int kCpr = 64 / kVec;            // 16-byte chunks per 64-element row
   constexpr int kRpp = 256 / kCpr;           // rows per pass
   typedef __attribute__((__vector_size__(16))) unsigned int u32x4;
   __shared__ T tile[64][64 + 2];
-  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int64_t r0 = bx * 64, c0 = by * 64;
   const int ch = threadIdx.x % kCpr;
   for (int i = threadIdx.x / kCpr; i < 64; i += kRpp) {
     const int64_t r = r0 + i, c = c0 + ch * kVec;
@@ -225,6 +264,11 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
         if (r + j < rpad) o[j] = v[j];
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs<T> a) {
+  transpose_tile<T>(blockIdx.x, blockIdx.y, a);
 }
 
 // s = smallest power of two >= max |g| over the chunk (1 if that maximum is 0
@@ -294,11 +338,22 @@ __global__ void db_accum_kernel(const T* __restrict__ dSt, int64_t ldSt, int64_t
 // a valid token with no earlier valid token of the same target writes
 // head[t], and every valid token writes next[n] (the first later valid token
 // with the same target, or -1). No atomics: the lists are in token order.
-__global__ void target_lists_kernel(const int64_t* __restrict__ targets, const float* __restrict__ g,
-                                    int64_t tok0, int64_t C, int64_t V, int64_t v0, int64_t Vt,
-                                    int32_t* __restrict__ head, int32_t* __restrict__ next) {
+struct ListArgs {
+  const int64_t* targets;
+  const float* g;
+  int64_t tok0, C, V, v0, Vt;
+  int32_t* head;
+  int32_t* next;
+};
+
+__device__ __forceinline__ void target_lists_block(int64_t bx, const ListArgs& a) {
+  const int64_t* __restrict__ targets = a.targets;
+  const float* __restrict__ g = a.g;
+  const int64_t tok0 = a.tok0, C = a.C, V = a.V, v0 = a.v0, Vt = a.Vt;
+  int32_t* __restrict__ head = a.head;
+  int32_t* __restrict__ next = a.next;
   const int lane = threadIdx.x & 63;
-  const int64_t n = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int64_t n = bx * 4 + (threadIdx.x >> 6);  // 256 threads: four tokens
   if (n >= C) return;  // uniform per wave
   int64_t t;
   if (!tok_valid(targets, g, tok0 + n, V, v0, Vt, t)) return;
@@ -325,6 +380,29 @@ __global__ void target_lists_kernel(const int64_t* __restrict__ targets, const f
   }
 }
 
+__global__ __launch_bounds__(256) void target_lists_kernel(ListArgs a) { target_lists_block(blockIdx.x, a); }
+
+// The per-chunk preparation before the dH / dW contraction in one launch, so
+// that its independent memory-bound parts overlap instead of queueing: the
+// target lists (blocks [0, nl)), the chunk's h transposed (next nt blocks)
+// and the softmax gradient tiles (next ns blocks). Each part is optional.
+template <typename T>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(ListArgs la, int64_t nl, TransposeArgs<T> ta, int64_t tgx,
+                                                         int64_t nt, SoftmaxGradArgs<T> sa, int64_t sgx) {
+  int64_t b = blockIdx.x;
+  if (b < nl) {
+    target_lists_block(b, la);
+    return;
+  }
+  b -= nl;
+  if (b < nt) {
+    transpose_tile<T>(b % tgx, b / tgx, ta);
+    return;
+  }
+  b -= nt;
+  softmax_grad_tile<T>(b % sgx, b / sgx, sa);
+}
+
 __global__ void fill_kernel(uint32_t* __restrict__ p, int64_t nwords, uint32_t word) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride) p[i] = word;
@@ -344,8 +422,8 @@ hipError_t transpose_t(const void* src, int64_t rows, int64_t cols, int64_t lds,
   constexpr int64_t kVec = 16 / (int64_t)sizeof(T);
   const int vec = (reinterpret_cast<uintptr_t>(src) % 16 == 0) && (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
                   (lds % kVec == 0) && (ldd % kVec == 0);
-  transpose_kernel<T><<<grid, 256, 0, s>>>(static_cast<const T*>(src), rows, cols, lds,
-                                           static_cast<T*>(dst), ldd, vec);
+  transpose_kernel<T><<<grid, 256, 0, s>>>(
+      TransposeArgs<T>{static_cast<const T*>(src), rows, cols, lds, static_cast<T*>(dst), ldd, vec});
   return hipGetLastError();
 }
 
@@ -382,6 +460,14 @@ hipError_t launch_shard_combine(const float* lse_sh, const float* zt_sh, int64_t
   return hipGetLastError();
 }
 
+template <typename T>
+SoftmaxGradArgs<T> sg_args(void* qt, int64_t ldq, const float2* partials, int64_t ldp, const float* lse,
+                           const float* g, const int64_t* targets, const float2* scales, int chunk, int64_t V,
+                           int64_t C, void* dS, int64_t ldS) {
+  return SoftmaxGradArgs<T>{static_cast<T*>(qt), ldq, partials, ldp, lse, g, targets, scales, chunk, V, C,
+                            static_cast<T*>(dS), ldS};
+}
+
 hipError_t launch_softmax_grad(int dt, void* qt, int64_t ldq, const float2* partials, int64_t ldp,
                                const float* lse, const float* g, const int64_t* targets,
                                const float2* scales, int chunk, int64_t V, int64_t C, void* dS,
@@ -390,17 +476,16 @@ hipError_t launch_softmax_grad(int dt, void* qt, int64_t ldq, const float2* part
   dim3 grid((unsigned)((V + 63) / 64), (unsigned)((C + 63) / 64));  // C <= 2^31 - 1 (validated)
   switch (dt) {
     case DT_F32:
-      softmax_grad_kernel<float><<<grid, 256, 0, s>>>(static_cast<float*>(qt), ldq, partials, ldp, lse, g,
-                                                      targets, scales, chunk, V, C, static_cast<float*>(dS), ldS);
+      softmax_grad_kernel<float><<<grid, 256, 0, s>>>(
+          sg_args<float>(qt, ldq, partials, ldp, lse, g, targets, scales, chunk, V, C, dS, ldS));
       break;
     case DT_BF16:
-      softmax_grad_kernel<__bf16><<<grid, 256, 0, s>>>(static_cast<__bf16*>(qt), ldq, partials, ldp, lse, g,
-                                                       targets, scales, chunk, V, C, static_cast<__bf16*>(dS), ldS);
+      softmax_grad_kernel<__bf16><<<grid, 256, 0, s>>>(
+          sg_args<__bf16>(qt, ldq, partials, ldp, lse, g, targets, scales, chunk, V, C, dS, ldS));
       break;
     case DT_F16:
-      softmax_grad_kernel<_Float16><<<grid, 256, 0, s>>>(static_cast<_Float16*>(qt), ldq, partials, ldp, lse, g,
-                                                         targets, scales, chunk, V, C,
-                                                         static_cast<_Float16*>(dS), ldS);
+      softmax_grad_kernel<_Float16><<<grid, 256, 0, s>>>(
+          sg_args<_Float16>(qt, ldq, partials, ldp, lse, g, targets, scales, chunk, V, C, dS, ldS));
       break;
     default: return hipErrorInvalidValue;
   }
@@ -413,6 +498,42 @@ hipError_t launch_transpose(int dt, const void* src, int64_t rows, int64_t cols,
     case DT_F32: return transpose_t<float>(src, rows, cols, lds, dst, ldd, s);
     case DT_BF16:
     case DT_F16: return transpose_t<uint16_t>(src, rows, cols, lds, dst, ldd, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
+  const ListArgs la{c.targets, c.g, c.tok0, c.C, c.V, c.v0, c.Vt, c.head, c.next};
+  const int64_t nl = c.head != nullptr ? (c.C + 3) / 4 : 0;
+  constexpr int64_t kVec = 16 / (int64_t)sizeof(T);
+  const int vec = (reinterpret_cast<uintptr_t>(c.h) % 16 == 0) && (reinterpret_cast<uintptr_t>(c.ht) % 16 == 0) &&
+                  (c.D % kVec == 0) && (c.ldht % kVec == 0);
+  const TransposeArgs<T> ta{static_cast<const T*>(c.h), c.C, c.D, c.D, static_cast<T*>(c.ht), c.ldht, vec};
+  const int64_t tgx = (c.C + 63) / 64;
+  const int64_t nt = c.ht != nullptr ? tgx * ((c.D + 63) / 64) : 0;
+  const SoftmaxGradArgs<T> sa = sg_args<T>(c.qt, c.ldq, c.partials, c.ldp, c.lse, c.gc, c.tc, c.scales, c.chunk, c.V,
+                                           c.C, c.dS, c.ldS);
+  const int64_t sgx = (c.V + 63) / 64;
+  const int64_t ns = c.qt != nullptr ? sgx * ((c.C + 63) / 64) : 0;
+  const int64_t total = nl + nt + ns;
+  if (total == 0) return hipSuccess;
+  if (total > INT32_MAX) {  // one launch per part
+    if (nl) target_lists_kernel<<<(unsigned)nl, 256, 0, s>>>(la);
+    if (nt) transpose_kernel<T><<<dim3((unsigned)tgx, (unsigned)(nt / tgx)), 256, 0, s>>>(ta);
+    if (ns) softmax_grad_kernel<T><<<dim3((unsigned)sgx, (unsigned)(ns / sgx)), 256, 0, s>>>(sa);
+    return hipGetLastError();
+  }
+  chunk_prep_kernel<T><<<(unsigned)total, 256, 0, s>>>(la, nl, ta, tgx, nt, sa, sgx);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_prep(int dt, const ChunkPrep& c, hipStream_t s) {
+  if (c.C == 0) return hipSuccess;
+  switch (dt) {
+    case DT_F32: return chunk_prep_t<float>(c, s);
+    case DT_BF16: return chunk_prep_t<__bf16>(c, s);
+    case DT_F16: return chunk_prep_t<_Float16>(c, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -443,7 +564,7 @@ hipError_t launch_db_accum(int dt, const void* dSt, int64_t ldSt, int64_t V, int
 hipError_t launch_target_lists(const int64_t* targets, const float* g, int64_t tok0, int64_t C,
                                int64_t V, int64_t v0, int64_t Vt, int32_t* head, int32_t* next, hipStream_t s) {
   if (C == 0) return hipSuccess;
-  target_lists_kernel<<<(unsigned)((C + 3) / 4), 256, 0, s>>>(targets, g, tok0, C, V, v0, Vt, head, next);
+  target_lists_kernel<<<(unsigned)((C + 3) / 4), 256, 0, s>>>(ListArgs{targets, g, tok0, C, V, v0, Vt, head, next});
   return hipGetLastError();
 }
 

@@ -394,6 +394,8 @@ __device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_
 }
 
 // dW rows: table[v, :] += s C[v, :] + sum, in token order, of tcoef[n] h[n, :]
+// (the table is read and written once per chunk: non-temporal accesses keep
+// it from displacing the operand panels that other tiles share in L2)
 // over the chunk's valid tokens with target v. The tile's 256 list heads are
 // loaded and validated once into LDS (entries of targets absent from the
 // chunk are stale), so a row without targets costs one LDS read.
@@ -427,7 +429,7 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
-        old[r][ni] = tb[mc * e.ldo + (n < p.N ? n : p.N - 1)];
+        old[r][ni] = __builtin_nontemporal_load(&tb[mc * e.ldo + (n < p.N ? n : p.N - 1)]);
         val[r][ni] = acc[mi][ni][r] * sc;
       }
     }
@@ -453,7 +455,7 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
-        if (m < p.M && n < p.N) tb[m * e.ldo + n] = (TT)((float)old[r][ni] + val[r][ni]);
+        if (m < p.M && n < p.N) __builtin_nontemporal_store((TT)((float)old[r][ni] + val[r][ni]), &tb[m * e.ldo + n]);
       }
     }
   }

@@ -129,6 +129,40 @@ hipError_t launch_target_lists(const int64_t* targets, const float* g, int64_t t
 hipError_t launch_shard_combine(const float* lse_sh, const float* zt_sh, int64_t P, int64_t N,
                                 const int64_t* targets, int64_t Vt, float* logp, float* lse, hipStream_t s);
 
+// The per-chunk preparation of the dH / dW contraction in one launch (its
+// parts are independent): the target lists (when head != null, as
+// launch_target_lists), h rows [tok0, tok0 + C) transposed into ht [D][ldht]
+// (when ht != null, as launch_transpose) and the softmax gradient of the
+// fused path (when qt != null, as launch_softmax_grad, whose per-token
+// arrays lse, gc, tc start at the chunk).
+struct ChunkPrep {
+  int64_t C, V;
+  // target lists
+  const int64_t* targets;
+  const float* g;
+  int64_t tok0, v0, Vt;
+  int32_t* head;
+  int32_t* next;
+  // transpose of the chunk's h rows
+  const void* h;  // first row of the chunk
+  int64_t D;
+  void* ht;
+  int64_t ldht;
+  // softmax gradient
+  void* qt;
+  int64_t ldq;
+  const float2* partials;
+  int64_t ldp;
+  const float* lse;
+  const float* gc;
+  const int64_t* tc;
+  const float2* scales;
+  int chunk;
+  void* dS;
+  int64_t ldS;
+};
+hipError_t launch_chunk_prep(int dt, const ChunkPrep& c, hipStream_t s);
+
 // Fill n elements of size esize with +0.
 hipError_t launch_zero(void* p, int64_t n, int esize, hipStream_t s);
 // Fill n 4-byte words (p 4-byte aligned) with the bit pattern `word`.

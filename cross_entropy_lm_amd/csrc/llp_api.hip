@@ -264,8 +264,6 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &p, nullptr, s));
       LLP_LAUNCH(LLP_K_COMBINE, launch_lse_combine(part, bp.P, bp.C, zt + c0, targets + c0, V, Ck, logp_out + c0,
                                                    lse_fused + c0, g + c0, tcoef + c0, s));
-      LLP_LAUNCH(LLP_K_DLOGITS, launch_softmax_grad(dtype, dSt, bp.ldSt, part, bp.C, lse_fused + c0, g + c0,
-                                                    targets + c0, scales, (int)k, V, Ck, dS, bp.ldS, s));
     } else {
       // dlogits of the chunk, recomputed from the logits tile and the saved lse
       p.epi = EPI_DLOGITS;
@@ -280,9 +278,40 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       p.ep.chunk = (int)k;
       LLP_LAUNCH(LLP_K_DLOGITS, launch_gemm(dtype, &p, nullptr, s));
     }
-    if (want_dW)
-      LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, static_cast<const char*>(h) + c0 * D * e, Ck, D, D, ht, bp.ldSt, s));
-    if (want_dW || want_db) LLP_LAUNCH(LLP_K_SMALL, launch_target_lists(targets, g, c0, Ck, V, v0, Vt, head, next, s));
+    // one launch: target lists, the chunk's h transposed, and (fused) the softmax gradient
+    ChunkPrep cp = {};
+    cp.C = Ck;
+    cp.V = V;
+    if (want_dW || want_db) {
+      cp.targets = targets;
+      cp.g = g;
+      cp.tok0 = c0;
+      cp.v0 = v0;
+      cp.Vt = Vt;
+      cp.head = head;
+      cp.next = next;
+    }
+    if (want_dW) {
+      cp.h = static_cast<const char*>(h) + c0 * D * e;
+      cp.D = D;
+      cp.ht = ht;
+      cp.ldht = bp.ldSt;
+    }
+    if (fused) {
+      cp.qt = dSt;
+      cp.ldq = bp.ldSt;
+      cp.partials = part;
+      cp.ldp = bp.C;
+      cp.lse = lse_fused + c0;
+      cp.gc = g + c0;
+      cp.tc = targets + c0;
+      cp.scales = scales;
+      cp.chunk = (int)k;
+      cp.dS = dS;
+      cp.ldS = bp.ldS;
+    }
+    if (cp.head != nullptr || cp.ht != nullptr || cp.qt != nullptr)
+      LLP_LAUNCH(fused ? LLP_K_DLOGITS : LLP_K_TRANSPOSE, launch_chunk_prep(dtype, cp, s));
     if (want_db)
       LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, bp.ldSt, V, Ck, scales, (int)k, head, next, targets, g, tcoef,
                               c0, v0, Vt, db, dW_dtype, s));
