@@ -86,7 +86,12 @@ struct SoftmaxGradArgs {
 };
 
 template <typename T>
-__device__ __forceinline__ void softmax_grad_tile(int64_t bx, int64_t by, const SoftmaxGradArgs<T>& a) {
+constexpr int softmax_grad_lds() {
+  return 64 * (64 + 16 / (int)sizeof(T)) * (int)sizeof(T) + 64 * 4 + 64 * 4;
+}
+
+template <typename T>
+__device__ __forceinline__ void softmax_grad_tile(int64_t bx, int64_t by, const SoftmaxGradArgs<T>& a, char* smem) {
   T* __restrict__ qt = a.qt;
   const int64_t ldq = a.ldq, ldp = a.ldp, V = a.V, C = a.C, ldS = a.ldS;
   const float2* __restrict__ partials = a.partials;
@@ -100,9 +105,9 @@ __device__ __forceinline__ void softmax_grad_tile(int64_t bx, int64_t by, const 
   constexpr int kCpr = 64 / kVec;            // 16-byte chunks per 64-element row
   constexpr int kRpp = 256 / kCpr;           // rows per pass
   typedef __attribute__((__vector_size__(16))) unsigned int u32x4;
-  __shared__ T tile[64][64 + kVec];
-  __shared__ float coef_s[64];
-  __shared__ int32_t t_s[64];
+  T(*tile)[64 + kVec] = reinterpret_cast<T(*)[64 + kVec]>(smem);  // [64][64 + kVec]
+  float* coef_s = reinterpret_cast<float*>(smem + 64 * (64 + kVec) * sizeof(T));
+  int32_t* t_s = reinterpret_cast<int32_t*>(coef_s + 64);
   const int64_t v0 = bx * 64, n0 = by * 64;
   if (threadIdx.x < 64) {
     // column n: the token's factor -(g / s) 2^(m_b - lse log2 e); 64-row tiles lie in one 128-row block
@@ -178,7 +183,8 @@ __device__ __forceinline__ void softmax_grad_tile(int64_t bx, int64_t by, const 
 
 template <typename T>
 __global__ __launch_bounds__(256) void softmax_grad_kernel(SoftmaxGradArgs<T> a) {
-  softmax_grad_tile<T>(blockIdx.x, blockIdx.y, a);
+  __shared__ __attribute__((aligned(16))) char smem[softmax_grad_lds<T>()];
+  softmax_grad_tile<T>(blockIdx.x, blockIdx.y, a, smem);
 }
 
 // Vocabulary-parallel merge: per token, the P shares' (lse_r, zt_r) (zt_r =
@@ -223,7 +229,12 @@ struct TransposeArgs {
 };
 
 template <typename T>
-__device__ __forceinline__ void transpose_tile(int64_t bx, int64_t by, const TransposeArgs<T>& a) {
+constexpr int transpose_lds() {
+  return 64 * (64 + 2) * (int)sizeof(T);
+}
+
+template <typename T>
+__device__ __forceinline__ void transpose_tile(int64_t bx, int64_t by, const TransposeArgs<T>& a, char* smem) {
   const T* __restrict__ src = a.src;
   T* __restrict__ dst = a.dst;
   const int64_t rows = a.rows, cols = a.cols, lds = a.lds, ldd = a.ldd;
@@ -232,7 +243,7 @@ __device__ __forceinline__ void transpose_tile(int64_t bx, int64_t by, const Tra
   constexpr int kCpr = 64 / kVec;            // 16-byte chunks per 64-element row
   constexpr int kRpp = 256 / kCpr;           // rows per pass
   typedef __attribute__((__vector_size__(16))) unsigned int u32x4;
-  __shared__ T tile[64][64 + 2];
+  T(*tile)[64 + 2] = reinterpret_cast<T(*)[64 + 2]>(smem);  // [64][66]
   const int64_t r0 = bx * 64, c0 = by * 64;
   const int ch = threadIdx.x % kCpr;
   for (int i = threadIdx.x / kCpr; i < 64; i += kRpp) {
@@ -268,7 +279,8 @@ __device__ __forceinline__ void transpose_tile(int64_t bx, int64_t by, const Tra
 
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs<T> a) {
-  transpose_tile<T>(blockIdx.x, blockIdx.y, a);
+  __shared__ __attribute__((aligned(16))) char smem[transpose_lds<T>()];
+  transpose_tile<T>(blockIdx.x, blockIdx.y, a, smem);
 }
 
 // s = smallest power of two >= max |g| over the chunk (1 if that maximum is 0
@@ -382,25 +394,188 @@ __device__ __forceinline__ void target_lists_block(int64_t bx, const ListArgs& a
 
 __global__ __launch_bounds__(256) void target_lists_kernel(ListArgs a) { target_lists_block(blockIdx.x, a); }
 
-// The per-chunk preparation before the dH / dW contraction in one launch, so
-// that its independent memory-bound parts overlap instead of queueing: the
-// target lists (blocks [0, nl)), the chunk's h transposed (next nt blocks)
-// and the softmax gradient tiles (next ns blocks). Each part is optional.
+// One-hot rows of an FP32 dW table for one chunk: for every vocabulary row t
+// that is the target of valid tokens of the chunk,
+//     table[t, :] += sum over those tokens j, in increasing j, of tcoef[j] h[j, :]
+// (fp32, the sum formed from +0 and added to the table once per batch of up to
+// kOhCap - 2048 tokens, so once for any realistic chunk). The dense part
+// s * (dlogits^T h) is added afterwards by the contraction's epilogue.
+// Block n takes the row of token n's target when n is the first valid token
+// with that target, so every row has one writer and a fixed order of
+// additions; the other blocks return after the scan.
 template <typename T>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(ListArgs la, int64_t nl, TransposeArgs<T> ta, int64_t tgx,
-                                                         int64_t nt, SoftmaxGradArgs<T> sa, int64_t sgx) {
+struct OnehotArgs {
+  const int64_t* targets;  // indexed tok0 + local token, as g and tcoef
+  const float* g;
+  const float* tcoef;
+  int64_t tok0, C, V, v0, Vt;
+  const T* h;  // the chunk's first row
+  int64_t ldh, D;
+  float* table;  // [V][ldt]
+  int64_t ldt;
+  int vec;  // h rows and table rows may be accessed in 16-byte pieces
+};
+constexpr int kOhPer = 8;    // table columns per thread and pass (2048 per pass of 256 threads)
+constexpr int kOhWin = 8;    // 256-token windows whose targets a thread loads at once
+constexpr int kOhGroup = kOhWin * 256;
+constexpr int kOhCap = 2 * kOhGroup;  // list entries (a flush is due once more than kOhCap - kOhGroup)
+constexpr int onehot_lds() { return kOhCap * 4 + kOhWin * 4 * 4; }
+
+template <typename T>
+__device__ __forceinline__ void load_piece(const T* p, float (&x)[kOhPer]) {
+  typedef __attribute__((__vector_size__(16))) unsigned int u32x4;
+  constexpr int kv = 16 / (int)sizeof(T);
+#pragma unroll
+  for (int q = 0; q < kOhPer / kv; ++q) {
+    T v[kv];
+    *reinterpret_cast<u32x4*>(v) = *reinterpret_cast<const u32x4*>(p + q * kv);
+#pragma unroll
+    for (int i = 0; i < kv; ++i) x[q * kv + i] = (float)v[i];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void onehot_rows_block(int64_t n, const OnehotArgs<T>& a, char* smem) {
+  int32_t* lst = reinterpret_cast<int32_t*>(smem);
+  int(*wcnt)[4] = reinterpret_cast<int(*)[4]>(smem + kOhCap * 4);  // [kOhWin][4]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t* __restrict__ targets = a.targets + a.tok0;
+  const float* __restrict__ g = a.g + a.tok0;
+  const int64_t tn = targets[n];
+  const float gn = g[n];
+  const int64_t t = tn - a.v0;
+  const bool valid = tn >= 0 && tn < a.Vt && t >= 0 && t < a.V && gn != 0.0f;
+  float* row = a.table + (valid ? t : 0) * a.ldt;
+  // row += sum over the listed tokens of tcoef h, in list order; the row's old
+  // values are loaded before the h rows, so a pass waits about one round trip
+  auto flush = [&](int count) {
+#pragma unroll 1
+    for (int64_t d = (int64_t)tid * kOhPer; d < a.D; d += 256 * kOhPer) {
+      const bool full = a.vec && d + kOhPer <= a.D;
+      float o[kOhPer], acc[kOhPer];
+      if (full) {
+        load_piece(row + d, o);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kOhPer; ++i) o[i] = (d + i < a.D) ? row[d + i] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < kOhPer; ++i) acc[i] = 0.0f;
+#pragma unroll 1
+      for (int e = 0; e < count; ++e) {
+        const int64_t j = lst[e];
+        const T* hr = a.h + j * a.ldh + d;
+        const float c = a.tcoef[a.tok0 + j];
+        float x[kOhPer];
+        if (full) {
+          load_piece(hr, x);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kOhPer; ++i) x[i] = (d + i < a.D) ? (float)hr[i] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kOhPer; ++i) acc[i] = fmaf(c, x[i], acc[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < kOhPer; ++i) o[i] += acc[i];
+      if (full) {
+        typedef __attribute__((__vector_size__(16))) unsigned int u32x4;
+#pragma unroll
+        for (int q = 0; q < kOhPer / 4; ++q)
+          *reinterpret_cast<u32x4*>(row + d + q * 4) = *reinterpret_cast<const u32x4*>(o + q * 4);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kOhPer; ++i)
+          if (d + i < a.D) row[d + i] = o[i];
+      }
+    }
+  };
+  // scan the chunk in groups of kOhWin x 256 tokens, one round trip each (the
+  // loads use clamped indices, so they are unconditional): a valid token
+  // earlier than n with the same target means another block owns the row; the
+  // tokens j >= n with the target are appended to the list in increasing j
+  int count = 0;  // uniform over the block
+  for (int64_t base = 0; base < a.C; base += kOhGroup) {
+    bool m[kOhWin];
+#pragma unroll
+    for (int w = 0; w < kOhWin; ++w) {
+      const int64_t j = base + w * 256 + tid;
+      const int64_t jc = j < a.C ? j : a.C - 1;
+      const int64_t tj = targets[jc];
+      const float gj = g[jc];
+      m[w] = (j < a.C) & (tj >= 0) & (tj < a.Vt) & (tj - a.v0 == t) & (gj != 0.0f);
+    }
+    if (!valid) return;  // uniform over the block
+    int earlier = 0;
+#pragma unroll
+    for (int w = 0; w < kOhWin; ++w) earlier |= (m[w] & (base + w * 256 + tid < n)) ? 1 : 0;
+    if (__syncthreads_or(earlier)) return;
+    uint64_t bal[kOhWin];
+#pragma unroll
+    for (int w = 0; w < kOhWin; ++w) {
+      m[w] = m[w] & (base + w * 256 + tid >= n);
+      bal[w] = __ballot(m[w]);
+      if (lane == 0) wcnt[w][wave] = __popcll(bal[w]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kOhWin; ++w) {
+      int before = count, total = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        before += (v < wave) ? wcnt[w][v] : 0;
+        total += wcnt[w][v];
+      }
+      // count <= kOhCap - kOhGroup before a group, so every position is < kOhCap
+      if (m[w]) lst[before + __popcll(bal[w] & ((uint64_t(1) << lane) - 1))] = (int32_t)(base + w * 256 + tid);
+      count += total;
+    }
+    __syncthreads();  // the list is complete; wcnt may be rewritten
+    if (count > kOhCap - kOhGroup || base + kOhGroup >= a.C) {
+      if (count > 0) flush(count);
+      count = 0;
+      __syncthreads();  // every thread has read the list before it is rewritten
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void onehot_rows_kernel(OnehotArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char smem[onehot_lds()];
+  onehot_rows_block<T>(blockIdx.x, a, smem);
+}
+
+// The per-chunk preparation before the dH / dW contraction in one launch, so
+// that its independent parts overlap instead of queueing: the one-hot rows of
+// an FP32 dW table (blocks [0, no)), the target lists (next nl blocks), the
+// chunk's h transposed (next nt blocks) and the softmax gradient tiles (next
+// ns blocks). Each part is optional.
+template <typename T>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(OnehotArgs<T> oa, int64_t no, ListArgs la, int64_t nl,
+                                                         TransposeArgs<T> ta, int64_t tgx, int64_t nt,
+                                                         SoftmaxGradArgs<T> sa, int64_t sgx) {
+  // the one-hot blocks come first: they are latency-bound and short, so the
+  // memory-bound parts that follow run beside them
+  // one LDS buffer for whichever part this block runs
+  __shared__ __attribute__((aligned(16))) char smem[std::max(std::max(softmax_grad_lds<T>(), transpose_lds<T>()),
+                                                             onehot_lds())];
   int64_t b = blockIdx.x;
+  if (b < no) {
+    onehot_rows_block<T>(b, oa, smem);
+    return;
+  }
+  b -= no;
   if (b < nl) {
     target_lists_block(b, la);
     return;
   }
   b -= nl;
   if (b < nt) {
-    transpose_tile<T>(b % tgx, b / tgx, ta);
+    transpose_tile<T>(b % tgx, b / tgx, ta, smem);
     return;
   }
   b -= nt;
-  softmax_grad_tile<T>(b % sgx, b / sgx, sa);
+  softmax_grad_tile<T>(b % sgx, b / sgx, sa, smem);
 }
 
 __global__ void fill_kernel(uint32_t* __restrict__ p, int64_t nwords, uint32_t word) {
@@ -507,6 +682,11 @@ hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
   const ListArgs la{c.targets, c.g, c.tok0, c.C, c.V, c.v0, c.Vt, c.head, c.next};
   const int64_t nl = c.head != nullptr ? (c.C + 3) / 4 : 0;
   constexpr int64_t kVec = 16 / (int64_t)sizeof(T);
+  const int ovec = (reinterpret_cast<uintptr_t>(c.h) % 16 == 0) && (reinterpret_cast<uintptr_t>(c.table) % 16 == 0) &&
+                   (c.D % kVec == 0) && (c.ldt % 4 == 0) && (c.D % 4 == 0);  // pieces start at multiples of 16
+  const OnehotArgs<T> oa{c.targets, c.g, c.tcoef, c.tok0, c.C, c.V, c.v0, c.Vt,
+                         static_cast<const T*>(c.h), c.D, c.D, c.table, c.ldt, ovec};
+  const int64_t no = c.table != nullptr ? c.C : 0;
   const int vec = (reinterpret_cast<uintptr_t>(c.h) % 16 == 0) && (reinterpret_cast<uintptr_t>(c.ht) % 16 == 0) &&
                   (c.D % kVec == 0) && (c.ldht % kVec == 0);
   const TransposeArgs<T> ta{static_cast<const T*>(c.h), c.C, c.D, c.D, static_cast<T*>(c.ht), c.ldht, vec};
@@ -516,15 +696,16 @@ hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
                                            c.C, c.dS, c.ldS);
   const int64_t sgx = (c.V + 63) / 64;
   const int64_t ns = c.qt != nullptr ? sgx * ((c.C + 63) / 64) : 0;
-  const int64_t total = nl + nt + ns;
+  const int64_t total = no + nl + nt + ns;
   if (total == 0) return hipSuccess;
   if (total > INT32_MAX) {  // one launch per part
+    if (no) onehot_rows_kernel<T><<<(unsigned)no, 256, 0, s>>>(oa);
     if (nl) target_lists_kernel<<<(unsigned)nl, 256, 0, s>>>(la);
     if (nt) transpose_kernel<T><<<dim3((unsigned)tgx, (unsigned)(nt / tgx)), 256, 0, s>>>(ta);
     if (ns) softmax_grad_kernel<T><<<dim3((unsigned)sgx, (unsigned)(ns / sgx)), 256, 0, s>>>(sa);
     return hipGetLastError();
   }
-  chunk_prep_kernel<T><<<(unsigned)total, 256, 0, s>>>(la, nl, ta, tgx, nt, sa, sgx);
+  chunk_prep_kernel<T><<<(unsigned)total, 256, 0, s>>>(oa, no, la, nl, ta, tgx, nt, sa, sgx);
   return hipGetLastError();
 }
 

@@ -410,7 +410,7 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
   int32_t* hs = reinterpret_cast<int32_t*>(smem);
   for (int i = threadIdx.x; i < kTileM; i += kThreads) {
     const int64_t m = m0 + i;
-    int32_t j = m < p.M ? e.head[m] : -1;
+    int32_t j = (m < p.M && e.head != nullptr) ? e.head[m] : -1;
     int64_t t;
     if (!(j >= 0 && j < e.ntok && token_valid(e, e.tok0 + j, t) && t == m)) j = -1;
     hs[i] = j;
@@ -461,13 +461,113 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
   }
 }
 
+// dW rows of an FP32 table whose one-hot rows were added beforehand:
+// table[v, :] += s C[v, :]. The tile goes through LDS (free once the K loop
+// has ended) in two halves of 128 rows x 256 columns, four 32-row regions
+// each; every thread then reads and writes whole 16-byte pieces of table rows
+// with buffer instructions whose row offsets are scalar. The old values of
+// half 1 are in flight while half 0 is added and stored, so a tile waits for
+// about one table round trip. Requires D % 4 == 0, a 16-byte aligned table
+// and a 256-row tile span below 2 GiB (EpiParams::tab_fast).
+// LDS region layout: row rr, column c at float rr * 256 + (c ^ 32 [bit 2 of rr]),
+// so the two 32-lane row groups of an accumulator write fall on distinct banks.
+__device__ __forceinline__ int tab_swz(int rr) { return ((rr >> 2) & 1) << 5; }
+
+__device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
+                                               const Frag& f, const EpiLds& L) {
+  static_assert(MI == 4 && kWaveM == 2 && kTileN == 256, "two halves of four 32-row regions");
+  constexpr int kRpp = kThreads / 64;  // region rows covered by one pass of all threads (one per wave)
+  constexpr int kPpr = 32 / kRpp;      // pieces of one region per thread
+  static_assert(kPpr * kRpp == 32, "waves divide a region");
+  const EpiParams& e = p.ep;
+  const float sc = e.scales[e.chunk].x;
+  const int tid = threadIdx.x;
+  float* tb0 = static_cast<float*>(e.out) + m0 * e.ldo + n0;
+  const int64_t span = (p.M - m0) * e.ldo * 4;  // bytes from the tile's first row to the table's end
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(tb0, (short)0, span < 0x7FFFFFF0LL ? (int)span : 0x7FFFFFF0, 0x00020000);
+  const int wrow = tid >> 6;             // this wave's row inside a kRpp-row group (wave-uniform)
+  const int c = (tid & 63) * 4;          // this thread's first column inside the tile
+  const bool colok = n0 + c < p.N;       // N % 4 == 0: the whole piece lies in [0, N)
+  const int vbase = (wrow * (int)e.ldo + c) * 4;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  // row (inside the tile, less wrow) of piece i of half h: region q = i / kPpr
+  // holds rows wm = q / 2, mi = 2h + q % 2; rows of a region advance by kRpp
+  auto row_of = [](int h, int i) {
+    const int q = i / kPpr;
+    return (q >> 1) * 128 + (2 * h + (q & 1)) * 32 + kRpp * (i % kPpr);
+  };
+  // quarter k of half h: regions 2k and 2k + 1, pieces [2k kPpr, (2k + 2) kPpr)
+  auto load_q = [&](int h, int k, f32x4 (&o)[2 * kPpr]) {
+#pragma unroll
+    for (int j = 0; j < 2 * kPpr; ++j)
+      o[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, vbase, row_of(h, 2 * kPpr * k + j) * (int)e.ldo * 4, 2 /* nt */));
+  };
+  auto to_lds = [&](int h) {
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh) {
+      // the region pointer is chosen without a runtime index into L.a (which
+      // would place the pointer array in private memory)
+      float* reg = reinterpret_cast<float*>(f.wm ? L.a[2 + mh] : L.a[mh]);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = (r >> 2) * 8 + (f.lane >> 5) * 4 + (r & 3);
+          const int col = f.wn * kWaveColsN + ni * 32 + (f.lane & 31);
+          reg[rr * 256 + (col ^ tab_swz(rr))] = acc[2 * h + mh][ni][r] * sc;
+        }
+    }
+  };
+  auto store_q = [&](int h, int k, const f32x4 (&o)[2 * kPpr]) {
+#pragma unroll
+    for (int j = 0; j < 2 * kPpr; ++j) {
+      const int i = 2 * kPpr * k + j;
+      const int rr = wrow + kRpp * (i % kPpr);
+      const bool odd = (i / kPpr) & 1;
+      const float* reg = reinterpret_cast<const float*>(k ? (odd ? L.a[3] : L.a[2]) : (odd ? L.a[1] : L.a[0]));
+      const f32x4 add = *reinterpret_cast<const f32x4*>(reg + rr * 256 + (c ^ tab_swz(rr)));
+      const int row = row_of(h, i) + wrow;
+      if (colok && m0 + row < p.M)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[j] + add), rs, vbase,
+                                               row_of(h, i) * (int)e.ldo * 4, 2 /* nt */);
+    }
+  };
+  // the scheduling barriers keep the loads of half 1 where they are issued
+  // (the scheduler would otherwise sink them below the barrier, next to
+  // their use, and serialise the two round trips)
+  f32x4 qa[2 * kPpr], qb[2 * kPpr];
+  to_lds(0);
+  load_q(0, 0, qa);
+  load_q(0, 1, qb);
+  __syncthreads();
+  store_q(0, 0, qa);
+  __builtin_amdgcn_sched_barrier(0);
+  load_q(1, 0, qa);
+  __builtin_amdgcn_sched_barrier(0);
+  store_q(0, 1, qb);
+  __builtin_amdgcn_sched_barrier(0);
+  load_q(1, 1, qb);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  to_lds(1);
+  __syncthreads();
+  store_q(1, 0, qa);
+  store_q(1, 1, qb);
+}
+
 template <typename T>
 __device__ __forceinline__ void epi_accum(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
                           const Frag& f, const EpiLds& L) {
-  if (p.ep.out_dt == DT_F32)
-    epi_accum_t<T, float>(p, acc, m0, n0, f, L);
-  else
+  if (p.ep.out_dt == DT_F32) {
+    if (p.ep.tab_fast)
+      epi_accum_fast(p, acc, m0, n0, f, L);
+    else
+      epi_accum_t<T, float>(p, acc, m0, n0, f, L);
+  } else {
     epi_accum_t<T, T>(p, acc, m0, n0, f, L);
+  }
 }
 
 // ---------------------------------------------------------------- main loop

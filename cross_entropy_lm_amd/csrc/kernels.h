@@ -60,9 +60,12 @@ struct EpiParams {
   // EPI_ACCUM (M = V, N = D): table += s C + sum over the chunk's tokens with target m of tcoef h
   const void* h;
   int64_t ldh;
+  // head == null: the one-hot rows were added to the table beforehand (FP32
+  // table, see ChunkPrep) and the epilogue adds s C only
   const int32_t* head;     // [V] first chunk token with target v (entries for absent v are stale)
   const int32_t* next;     // [C] next chunk token with the same target, -1 at the end
   int64_t ntok;            // tokens in the chunk
+  int tab_fast;            // FP32 table without one-hot part, D % 4 == 0, 16-byte aligned, tile span < 2 GiB
   // EPI_STORE and EPI_ACCUM
   void* out;
   int64_t ldo;
@@ -130,20 +133,26 @@ hipError_t launch_shard_combine(const float* lse_sh, const float* zt_sh, int64_t
                                 const int64_t* targets, int64_t Vt, float* logp, float* lse, hipStream_t s);
 
 // The per-chunk preparation of the dH / dW contraction in one launch (its
-// parts are independent): the target lists (when head != null, as
-// launch_target_lists), h rows [tok0, tok0 + C) transposed into ht [D][ldht]
-// (when ht != null, as launch_transpose) and the softmax gradient of the
-// fused path (when qt != null, as launch_softmax_grad, whose per-token
-// arrays lse, gc, tc start at the chunk).
+// parts are independent): the one-hot rows of an FP32 dW table (when table !=
+// null: table[t, :] += sum over the chunk's valid tokens j with target t, in
+// increasing j, of tcoef[j] h[j, :]; the contraction then adds only its dense
+// part), the target lists (when head != null, as launch_target_lists), h rows
+// [tok0, tok0 + C) transposed into ht [D][ldht] (when ht != null, as
+// launch_transpose) and the softmax gradient of the fused path (when qt !=
+// null, as launch_softmax_grad, whose per-token arrays lse, gc, tc start at
+// the chunk).
 struct ChunkPrep {
   int64_t C, V;
-  // target lists
+  // target lists and one-hot rows (targets, g, tcoef indexed tok0 + local token)
   const int64_t* targets;
   const float* g;
   int64_t tok0, v0, Vt;
   int32_t* head;
   int32_t* next;
-  // transpose of the chunk's h rows
+  const float* tcoef;
+  float* table;  // [V][ldt] FP32 dW table, or null
+  int64_t ldt;
+  // transpose of the chunk's h rows (also read by the one-hot rows)
   const void* h;  // first row of the chunk
   int64_t D;
   void* ht;

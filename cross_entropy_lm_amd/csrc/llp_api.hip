@@ -243,6 +243,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   int32_t* head = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_head)) : nullptr;
   int32_t* next = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_next)) : nullptr;
   if (want_dH) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
+  // per-chunk target lists: walked by db and by an operand-dtype dW table's
+  // epilogue (an FP32 table takes its one-hot rows in the chunk preparation)
+  const bool lists = want_db || (want_dW && dW_dtype != LLP_F32);
 
   for (int64_t k = 0; k < bp.K; ++k) {
     const int64_t c0 = k * bp.C;
@@ -288,14 +291,21 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       cp.tok0 = c0;
       cp.v0 = v0;
       cp.Vt = Vt;
-      cp.head = head;
-      cp.next = next;
+      if (lists) {
+        cp.head = head;
+        cp.next = next;
+      }
     }
     if (want_dW) {
       cp.h = static_cast<const char*>(h) + c0 * D * e;
       cp.D = D;
       cp.ht = ht;
       cp.ldht = bp.ldSt;
+      if (dW_dtype == LLP_F32) {  // the one-hot rows go into the table here
+        cp.tcoef = tcoef;
+        cp.table = static_cast<float*>(dW);
+        cp.ldt = D;
+      }
     }
     if (fused) {
       cp.qt = dSt;
@@ -310,7 +320,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       cp.dS = dS;
       cp.ldS = bp.ldS;
     }
-    if (cp.head != nullptr || cp.ht != nullptr || cp.qt != nullptr)
+    if (cp.head != nullptr || cp.ht != nullptr || cp.qt != nullptr || cp.table != nullptr)
       LLP_LAUNCH(fused ? LLP_K_DLOGITS : LLP_K_TRANSPOSE, launch_chunk_prep(dtype, cp, s));
     if (want_db)
       LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, bp.ldSt, V, Ck, scales, (int)k, head, next, targets, g, tcoef,
@@ -369,8 +379,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.tcoef = tcoef;
       pw.ep.h = h;
       pw.ep.ldh = D;
-      pw.ep.head = head;
+      pw.ep.head = dW_dtype == LLP_F32 ? nullptr : head;  // null: one-hot rows already added
       pw.ep.next = next;
+      pw.ep.tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < 0x7FFFFFF0LL;
       pw.ep.ntok = Ck;
       pw.ep.scales = scales;
       pw.ep.chunk = (int)k;

@@ -249,3 +249,42 @@ def test_gradient_tables_sum_to_zero_over_vocab():
     assert col < 1e-4 * dW.double().abs().sum(0).max().item() + 1e-6
     assert abs(db.double().sum().item()) < 1e-5 * db.double().abs().sum().item() + 1e-6
     del host
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["split", "fused"])
+def test_many_tokens_share_a_target(fused):
+    # Half of a 1200-token chunk has one target (several batches of the
+    # one-hot row sum), a seventh has the last vocabulary row (ragged tile),
+    # and some of them have g = 0 (they take no part); FP32 table.
+    w = synth.LinearWorkload("shared_bf16", 1500, 136, 1031, "bf16", True, 1200, "normal")
+    d = synth.make_linear_t(w, DEV)
+    host = synth.make_linear_np(w)
+    i = np.arange(w.N)
+    tt = host["t"].copy()
+    tt[i % 2 == 0] = 5
+    tt[i % 7 == 1] = w.V - 1
+    g64 = host["g64"].copy()
+    g64[i % 11 == 0] = 0.0
+    t = torch.from_numpy(tt).to(DEV)
+    g = torch.from_numpy(g64.astype(np.float32)).to(DEV)
+    L = llp()
+    say(f"shared targets fused={fused}")
+    if fused:
+        logp, lse, dH, dW, db = L.linear_logp_fwd_bwd(d["h"], d["W"], d["b"], t, g, True, True, True,
+                                                      chunk=w.chunk)
+    else:
+        logp, lse = L.linear_logp_fwd(d["h"], d["W"], d["b"], t)
+        dH, dW, db = L.linear_logp_bwd(d["h"], d["W"], d["b"], t, g, lse, True, True, True, chunk=w.chunk)
+    torch.cuda.synchronize()
+    rlogp, _ = O.linear_logp_fwd(host["h64"], host["W64"], host["b64"], tt)
+    rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], tt, g64, True, True, True)
+    tl, tg = TOL["bf16"]["logp"], TOL["bf16"]["grad"]
+    assert_close(logp, rlogp, *tl, "logp")
+    assert_close(dH, rdH, *tg, "dH")
+    assert_close(dW, rdW, *tg, "dW")
+    assert_close(db, rdb, *tg, "db")
+    # the rows of the shared targets carry most of the one-hot mass: check them tighter
+    # than the stated tolerance, relative to their own scale
+    for v in (5, w.V - 1):
+        x = dW[v].double().cpu().numpy()
+        assert np.abs(x - rdW[v]).max() <= 1e-3 * np.abs(rdW[v]).max() + 1e-6, v
