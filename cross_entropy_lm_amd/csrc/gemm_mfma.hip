@@ -690,6 +690,9 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have completed (vmcnt 63 and
+// expcnt 7 mean no wait on those counters)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
 // Stage k covers 128 bytes of K (four MFMA steps). Its A tile is unit 2k and
 // its B tile unit 2k + 1; unit u lives in slot u % 5. Every wave moves a
@@ -783,20 +786,26 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) {
       if (j + 1 < kSteps) read_step(sa, sb, j + 1, fa[(j + 1) & 1], fb[(j + 1) & 1]);
-      mma(fa[j & 1], fb[j & 1]);
+      if (j + 1 < kSteps) mma(fa[j & 1], fb[j & 1]);
       // the A tile of stage k + 2 goes, half after each of the first two
       // steps, into the slot that held stage k - 1's B tile: spreading the
       // DMA keeps the address queues from filling at the barrier
       constexpr int kHalf = kLoads / 2;
       if (j < 2 && k >= 1 && k + 2 < nst) issue(buf[(2 * I + 4) % kNS], k + 2, O_A{}, j * kHalf, (j + 1) * kHalf);
     }
-    // this wave's pieces of stage k + 1 have landed; only the A tile of stage
-    // k + 2 may remain in flight
+    // this wave's pieces of stage k + 1 have landed (only the A tile of stage
+    // k + 2 may remain in flight) and its reads of stage k have completed
+    // (the last step's fragments are in registers), so stage k's slots may
+    // be refilled once every wave has passed the barrier
     if (k + 2 < nst) wait_vm<kLoads>();
     else wait_vm<0>();
+    wait_lgkm0();
     LLP_BARRIER();
     if (k + 1 < nst) read_step(buf[(2 * I + 2) % kNS], buf[(2 * I + 3) % kNS], 0, fa[0], fb[0]);
     if (k + 2 < nst) issue(sa, k + 2, O_B{});  // unit 2k + 5 goes to slot (2k) % 5
+    // the last step of stage k multiplies while the next stage's first
+    // fragments come from LDS (after the barrier every wave reads at once)
+    mma(fa[(kSteps - 1) & 1], fb[(kSteps - 1) & 1]);
   };
 
   // units 0 .. 4: stages 0 and 1 and the A tile of stage 2
