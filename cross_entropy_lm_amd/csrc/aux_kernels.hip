@@ -15,14 +15,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Per token: merge the per-block (m, s) partials (m in log2 units, s = sum of
 // 2^(y - m)), then lse = (M + log2 S) ln 2 and logp = z[t] - lse for a target
 // in [0, V), else +0 (RL-Kernel PR #495, "Behavior changes"). A block of 1024
-// threads takes 64 tokens; the 16 threads of a token merge the partials
-// i = j, j + 16, ... in increasing i, then the 16 results are merged in
-// increasing j: a fixed order that depends on neither the batch size nor the
-// chunking. Loads are coalesced over the 64 consecutive tokens.
+// threads takes 16 tokens; the 64 threads of a token merge the partials
+// i = j, j + 64, ... in increasing i (loaded kCombBatch at a time), then the 64
+// results are merged by a fixed pairwise tree (j with j + 32, then j + 16,
+// ...): an order that depends on neither the batch size nor the chunking.
+// Loads are coalesced over the 16 consecutive tokens (one 128-byte line).
 // With g and tcoef (fused forward + backward) it also writes the one-hot
 // part tcoef[n] = g (1 - p_t), p_t = 2^(z_t log2 e - lse log2 e), for a valid
 // token (0 <= t < V, g != 0), else +0.
-constexpr int kCombTok = 64, kCombSl = 16;
+constexpr int kCombTok = 16, kCombSl = 64, kCombBatch = 4;
 __device__ __forceinline__ void lse_merge(float& M, float& S, float m, float s) {
   if (m == -INFINITY) return;
   if (m > M) {
@@ -41,14 +42,27 @@ __global__ __launch_bounds__(kCombTok * kCombSl) void lse_combine_kernel(
   const int64_t n = (int64_t)blockIdx.x * kCombTok + tk;
   float M = -INFINITY, S = 0.0f;
   if (n < N)
-    for (int64_t i = sl; i < P; i += kCombSl) {
-      const float2 q = partials[i * ldp + n];
-      lse_merge(M, S, q.x, q.y);
+    for (int64_t i0 = sl; i0 < P; i0 += kCombSl * kCombBatch) {
+      float2 q[kCombBatch];
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) {
+        const int64_t i = i0 + u * kCombSl;
+        q[u] = i < P ? partials[i * ldp + n] : make_float2(-INFINITY, 0.0f);
+      }
+#pragma unroll
+      for (int u = 0; u < kCombBatch; ++u) lse_merge(M, S, q[u].x, q[u].y);
     }
   part[sl][tk] = make_float2(M, S);
-  __syncthreads();
+#pragma unroll
+  for (int w = kCombSl / 2; w >= 1; w >>= 1) {
+    __syncthreads();
+    if (sl < w) {
+      const float2 o = part[sl + w][tk];
+      lse_merge(M, S, o.x, o.y);
+      part[sl][tk] = make_float2(M, S);
+    }
+  }
   if (sl != 0 || n >= N) return;
-  for (int j = 1; j < kCombSl; ++j) lse_merge(M, S, part[j][tk].x, part[j][tk].y);
   const float l = (M + __builtin_amdgcn_logf(S)) * kLn2;
   if (lse != nullptr) lse[n] = l;
   const int64_t t = targets[n];
