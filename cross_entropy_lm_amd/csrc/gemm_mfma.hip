@@ -709,10 +709,21 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (
 // K chunks at or past K read as 0 (offset past the buffer's end); a chunk that
 // straddles K relies on the operand's padding columns being +0, which the
 // host guarantees when it enables this path.
-template <typename T>
+//
+// kMn: both operands are stored K-row-major instead ([K][ld], the tile's 256
+// rows contiguous within each K row: A = dlogits^T [V][C], B = W [V][D] for
+// dH). A stage is then 64 K rows of 512 bytes per operand (the same 32 KiB
+// slot); one DMA instruction moves two K rows, chunk p of K row k lands at
+// chunk p ^ 4 (k % 4). A fragment is two ds_read_b64_tr_b16: in each group
+// of 16 lanes, lane s points at 4 consecutive rows of K row s / 4, and the
+// transposed read hands lane r the row r of 4 consecutive K rows, so a lane
+// gets the same 8 K values in the same order as a 16-byte read of the
+// K-contiguous layout. K rows at or past K read as 0 (past the buffer end).
+template <typename T, bool kMn = false>
 __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, int64_t n0, const Frag& f,
                                              char* const (&buf)[kNS], Acc& acc) {
   static_assert(kTileM == kTileN, "A and B slots have one shape");
+  static_assert(!kMn || sizeof(T) == 2, "K-row-major operands are 16-bit");
   constexpr int per16 = ET<T>::per16;
   constexpr int BKE = kSB / (int)sizeof(T);                    // K elements per stage
   constexpr int kRowsPerLoad = 64 * 16 / kSB;                  // rows one wave instruction covers
@@ -726,17 +737,41 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
     const int nrec = bytes < 0x7FFFFFF0LL ? (int)bytes : 0x7FFFFFF0;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t rsA = rsrc_of(static_cast<const T*>(p.A) + m0 * p.lda, p.M - m0, p.lda);
-  const __amdgpu_buffer_rsrc_t rsB = rsrc_of(static_cast<const T*>(p.B) + n0 * p.ldb, p.N - n0, p.ldb);
-  uint32_t voA[kLoads], voB[kLoads];
-  int kel[kLoads];
-#pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
-    const int row = (wave * kLoads + j) * kRowsPerLoad + (lane >> 3);
-    const int c = (lane & 7) ^ (row & 7);  // LDS chunk lane & 7 holds global chunk c
-    voA[j] = (uint32_t)(row * p.lda * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
-    voB[j] = (uint32_t)(row * p.ldb * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
-    kel[j] = c * per16;
+  auto rsrc_mn = [](const void* base, int64_t off, int64_t K, int64_t ld) {
+    // from column `off` of K row 0 to the end of the [K][ld] buffer
+    const int64_t bytes = (K * ld - off) * (int64_t)sizeof(T);
+    const int nrec = bytes < 0x7FFFFFF0LL ? (int)bytes : 0x7FFFFFF0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(base) + off), (short)0, nrec,
+                                             0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t rsA = kMn ? rsrc_mn(p.A, m0, p.K, p.lda)
+                                         : rsrc_of(static_cast<const T*>(p.A) + m0 * p.lda, p.M - m0, p.lda);
+  const __amdgpu_buffer_rsrc_t rsB = kMn ? rsrc_mn(p.B, n0, p.K, p.ldb)
+                                         : rsrc_of(static_cast<const T*>(p.B) + n0 * p.ldb, p.N - n0, p.ldb);
+  // Per-lane offsets of the wave's first DMA instruction of a unit; the
+  // others follow at a wave-uniform stride (the swizzle term depends on the
+  // lane only), so one register per operand covers all of them.
+  uint32_t voA, voB, strA, strB;
+  int kel;  // K-contiguous: first K element of this lane's chunk
+  if constexpr (kMn) {
+    static_assert(kThreads / 64 == 8 && kLoads == 4, "K-row-major placement: 8 waves x 4 instructions per unit");
+    // instruction j of wave w moves K rows 2w + 16j + {0, 1} (lanes 0-31, 32-63),
+    // so a lane's K row modulo 4, and with it the swizzle, is the same for every j
+    const int krow = 2 * wave + (lane >> 5);        // K row of the stage this lane moves first
+    const int c = (lane & 31) ^ (4 * (krow & 3));   // LDS chunk lane & 31 holds global chunk c
+    voA = (uint32_t)(krow * p.lda * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
+    voB = (uint32_t)(krow * p.ldb * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
+    strA = (uint32_t)(16 * p.lda * (int64_t)sizeof(T));
+    strB = (uint32_t)(16 * p.ldb * (int64_t)sizeof(T));
+    kel = 0;
+  } else {
+    const int row = (wave * kLoads) * kRowsPerLoad + (lane >> 3);
+    const int c = (lane & 7) ^ (row & 7);  // LDS chunk lane & 7 holds global chunk c (row & 7 = (lane >> 3) & 7)
+    voA = (uint32_t)(row * p.lda * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
+    voB = (uint32_t)(row * p.ldb * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
+    strA = (uint32_t)(kRowsPerLoad * p.lda * (int64_t)sizeof(T));
+    strB = (uint32_t)(kRowsPerLoad * p.ldb * (int64_t)sizeof(T));
+    kel = c * per16;
   }
   const int lds_off = wave * kLoads * kRowsPerLoad * kSB;
   const int64_t nst = (p.K + BKE - 1) / BKE;
@@ -747,15 +782,56 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       if (j < j0 || j >= j1) continue;
-      const uint32_t vo = O ? voB[j] : voA[j];
-      const uint32_t off = (s * BKE + kel[j] < p.K) ? vo + (uint32_t)(s * kSB) : 0xFFFFFFF0u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(O ? rsB : rsA,
-                                               (lds_void_t*)(slot + lds_off + j * kRowsPerLoad * kSB), 16, off,
-                                               0, 0, 0);
+      const uint32_t vo = (O ? voB : voA) + (uint32_t)j * (O ? strB : strA);
+      uint32_t off;
+      if constexpr (kMn)  // K rows past K lie past the buffer's end and read as 0
+        off = vo + (uint32_t)(s * BKE * (O ? p.ldb : p.lda) * (int64_t)sizeof(T));
+      else
+        off = (s * BKE + kel < p.K) ? vo + (uint32_t)(s * kSB) : 0xFFFFFFF0u;
+      // K-row-major: the 1 KiB block of instruction j holds K rows 2w + 16j, +1
+      char* const dst = kMn ? slot + wave * 1024 + j * 8192 : slot + lds_off + j * kRowsPerLoad * kSB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(O ? rsB : rsA, (lds_void_t*)dst, 16, off, 0, 0, 0);
     }
   };
   // fragments of step j of the stage held in slots (sa, sb)
+  // K-row-major fragments: per-lane byte offset inside a slot of the fragment
+  // rows [r0, r0 + 32) for step 0 and the first half of K (steps and the second
+  // half add 16 and 4 K rows: immediate offsets)
+  auto mn_off = [&](int r0) {
+    const int s4 = (lane & 15) >> 2;                                // K row inside the group of 4
+    const int m = r0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);     // first of this lane's 4 rows
+    const int krow = 8 * (lane >> 5) + s4;
+    return krow * 512 + (((m >> 3) ^ (4 * s4)) << 4) + ((m & 7) << 1);
+  };
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  auto read_mn = [&](const char* slot, int off, int j) {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(slot + off + j * 16 * 512));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(slot + off + j * 16 * 512 + 4 * 512));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+    u32x4 r;
+    r[0] = a[0];
+    r[1] = a[1];
+    r[2] = b[0];
+    r[3] = b[1];
+    return r;
+  };
+  int mnA[MI], mnB[NI];
+  if constexpr (kMn) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) mnA[mi] = mn_off(f.wm * kWaveRowsM + mi * 32);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) mnB[ni] = mn_off(f.wn * kWaveColsN + ni * 32);
+  }
   auto read_step = [&](const char* sa, const char* sb, int j, u32x4 (&fa)[MI], u32x4 (&fb)[NI]) {
+    if constexpr (kMn) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) fa[mi] = read_mn(sa, mnA[mi], j);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) fb[ni] = read_mn(sb, mnB[ni], j);
+      return;
+    }
     const int c = 2 * j + (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
@@ -831,7 +907,7 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
   }
 }
 
-template <typename T, int E, bool kDma>
+template <typename T, int E, bool kDma, bool kMn = false>
 __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* const (&buf)[kNS]) {
   int tm, tn;
   tile_coords(id, p.tiles_m, p.tiles_n, tm, tn);
@@ -855,7 +931,7 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* con
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
   if constexpr (kDma) {
-    mainloop_dma<T>(p, m0, n0, f, buf, acc);
+    mainloop_dma<T, kMn>(p, m0, n0, f, buf, acc);
   } else {
     if (p.a_vec && p.b_vec)
       mainloop<T, true>(p, m0, n0, f, buf[0], acc);
@@ -871,19 +947,20 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* con
   if constexpr (E == EPI_ACCUM) epi_accum<T>(p, acc, m0, n0, f, L);
 }
 
-template <typename T, int E0, int E1, bool kDma>
+template <typename T, int E0, int E1, bool kDma, bool kMn0>
 __device__ __forceinline__ void gemm_dispatch(const GemmProblem& p0, const GemmProblem& p1, int ntiles0,
                                               char* const (&buf)[kNS]) {
   const int bid = blockIdx.x;
   if (bid < ntiles0) {
-    tile_run<T, E0, kDma>(p0, xcd_remap(bid, ntiles0), buf);
+    tile_run<T, E0, kDma, kMn0>(p0, xcd_remap(bid, ntiles0), buf);
   } else {
     const int b1 = bid - ntiles0;
     if constexpr (E1 != EPI_NONE) tile_run<T, E1, kDma>(p1, xcd_remap(b1, (int)gridDim.x - ntiles0), buf);
   }
 }
 
-template <typename T, int E0, int E1, bool kDma>
+// kMn0: the first problem's operands are K-row-major (DMA pipeline only)
+template <typename T, int E0, int E1, bool kDma, bool kMn0 = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmProblem p1, int ntiles0) {
   if constexpr (kDma) {
     // distinct LDS objects per slot (see kNS)
@@ -893,13 +970,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmP
     __shared__ __attribute__((aligned(16))) char st3[kStageArr];
     __shared__ __attribute__((aligned(16))) char st4[kStageArr];
     char* const buf[kNS] = {st0, st1, st2, st3, st4};
-    gemm_dispatch<T, E0, E1, true>(p0, p1, ntiles0, buf);
+    gemm_dispatch<T, E0, E1, true, kMn0>(p0, p1, ntiles0, buf);
   } else {
     static_assert(kLdsBytes >= 4 * kOpB, "epilogue regions fit in the staged buffer");
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     // the epilogues use the first four regions; the fifth is never touched
     char* const buf[kNS] = {smem, smem + kOpB, smem + 2 * kOpB, smem + 3 * kOpB, smem};
-    gemm_dispatch<T, E0, E1, false>(p0, p1, ntiles0, buf);
+    static_assert(!kMn0, "K-row-major operands need the DMA pipeline");
+    gemm_dispatch<T, E0, E1, false, false>(p0, p1, ntiles0, buf);
   }
 }
 
@@ -925,6 +1003,14 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
     if (dma) gemm_kernel<T, EPI_DLOGITS, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
     else gemm_kernel<T, EPI_DLOGITS, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
   } else if ((e0 == EPI_STORE || e0 == EPI_NONE) && (e1 == EPI_ACCUM || e1 == EPI_NONE)) {
+    const bool mn = p0 != nullptr && p0->mn;
+    if constexpr (sizeof(T) == 2) {
+      if (mn && dma) {
+        gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, true><<<grid, block, 0, s>>>(a, b, nt0);
+        return hipGetLastError();
+      }
+    }
+    if (mn) return hipErrorInvalidValue;  // K-row-major operands: 16-bit types, DMA pipeline
     if (dma) gemm_kernel<T, EPI_STORE, EPI_ACCUM, true><<<grid, block, 0, s>>>(a, b, nt0);
     else gemm_kernel<T, EPI_STORE, EPI_ACCUM, false><<<grid, block, 0, s>>>(a, b, nt0);
   } else {

@@ -84,6 +84,9 @@ struct GemmProblem {
   int dma;           // 1: direct-to-LDS pipeline allowed (both operands 16-byte aligned, a 256-row
                      //    tile spans < 2 GiB, and K % (16 / esize) == 0 or the padding columns
                      //    up to the next multiple of 8 are +0)
+  int mn;            // 1 (first problem of a STORE launch, 16-bit, DMA): A is stored [K][lda] and B
+                     //    [K][ldb] (rows of the tile contiguous within a K row) instead of K-contiguous;
+                     //    K * ld * esize < 2 GiB for both, ld % 8 == 0, 16-byte aligned
   int tiles_m, tiles_n;
   int epi;
   EpiParams ep;

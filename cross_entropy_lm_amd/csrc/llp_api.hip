@@ -242,7 +242,19 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   float* tcoef = reinterpret_cast<float*>(at(workspace, bp.off_tcoef));
   int32_t* head = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_head)) : nullptr;
   int32_t* next = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_next)) : nullptr;
-  if (want_dH) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
+  // dH = dlogits W can take both operands as stored, K (vocabulary) rows with
+  // the tile's rows contiguous: dlogits^T [V][ldSt] and W [V][D] itself. Then
+  // neither W^T nor the token-major dlogits copy is formed. 16-bit operands on
+  // the DMA pipeline only; the vocab-major copy must be in the workspace.
+  const int64_t lim = 0x7FFFFFF0LL;
+  const bool dw_dma = !want_dW || (aligned16(dSt) && aligned16(ht));
+  const bool mn = want_dH && e == 2 && dSt != nullptr && aligned16(W) && aligned16(dSt) && D % 8 == 0 &&
+                  V * D * e < lim && V * bp.ldSt * e < lim && dw_dma;
+  if (mn) {
+    Wt = nullptr;
+    dS = nullptr;
+  }
+  if (want_dH && !mn) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
   // per-chunk target lists: walked by db and by an operand-dtype dW table's
   // epilogue (an FP32 table takes its one-hot rows in the chunk preparation)
   const bool lists = want_db || (want_dW && dW_dtype != LLP_F32);
@@ -275,7 +287,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       p.ep.tcoef = tcoef;
       p.ep.dS = dS;
       p.ep.ldS = bp.ldS;
-      p.ep.dSt = (want_dW || want_db) ? dSt : nullptr;
+      p.ep.dSt = (want_dW || want_db || mn) ? dSt : nullptr;
       p.ep.ldSt = bp.ldSt;
       p.ep.scales = scales;
       p.ep.chunk = (int)k;
@@ -326,7 +338,18 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, bp.ldSt, V, Ck, scales, (int)k, head, next, targets, g, tcoef,
                               c0, v0, Vt, db, dW_dtype, s));
     GemmProblem ph = {}, pw = {};
-    if (want_dH) {
+    if (want_dH && mn) {
+      ph.A = dSt;
+      ph.B = W;
+      ph.lda = bp.ldSt;
+      ph.ldb = D;
+      ph.M = Ck;
+      ph.N = D;
+      ph.K = V;
+      ph.a_vec = ph.b_vec = 1;
+      ph.mn = 1;
+      ph.dma = 1;
+    } else if (want_dH) {
       ph.A = dS;
       ph.B = Wt;
       ph.lda = bp.ldS;
@@ -336,6 +359,8 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       ph.K = V;
       ph.a_vec = ph.b_vec = 1;
       ph.dma = dma_ok(ph, e, true);  // dS and W^T padding columns are written +0
+    }
+    if (want_dH) {
       ph.tiles_m = (int)ceil_div(Ck, kTile);
       ph.tiles_n = (int)ceil_div(D, kTile);
       ph.epi = EPI_STORE;
