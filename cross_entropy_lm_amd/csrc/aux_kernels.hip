@@ -171,8 +171,10 @@ __device__ __forceinline__ void softmax_grad_tile(int64_t bx, int64_t by, const 
         }
       }
     }
+    if (dS != nullptr) {  // uniform: the token-major copy goes through LDS
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) tile[i][c * kVec + j] = val[j];
+      for (int j = 0; j < kVec; ++j) tile[i][c * kVec + j] = val[j];
+    }
   }
   if (dS == nullptr) return;  // uniform
   __syncthreads();
@@ -696,11 +698,12 @@ hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
   const ListArgs la{c.targets, c.g, c.tok0, c.C, c.V, c.v0, c.Vt, c.head, c.next};
   const int64_t nl = c.head != nullptr ? (c.C + 3) / 4 : 0;
   constexpr int64_t kVec = 16 / (int64_t)sizeof(T);
-  const int ovec = (reinterpret_cast<uintptr_t>(c.h) % 16 == 0) && (reinterpret_cast<uintptr_t>(c.table) % 16 == 0) &&
-                   (c.D % kVec == 0) && (c.ldt % 4 == 0) && (c.D % 4 == 0);  // pieces start at multiples of 16
-  const OnehotArgs<T> oa{c.targets, c.g, c.tcoef, c.tok0, c.C, c.V, c.v0, c.Vt,
-                         static_cast<const T*>(c.h), c.D, c.D, c.table, c.ldt, ovec};
-  const int64_t no = c.table != nullptr ? c.C : 0;
+  const int ovec = (reinterpret_cast<uintptr_t>(c.oh_h) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(c.table) % 16 == 0) && (c.D % kVec == 0) && (c.ldt % 4 == 0) &&
+                   (c.D % 4 == 0);  // pieces start at multiples of 16
+  const OnehotArgs<T> oa{c.targets, c.g, c.tcoef, c.oh_tok0, c.oh_C, c.V, c.v0, c.Vt,
+                         static_cast<const T*>(c.oh_h), c.D, c.D, c.table, c.ldt, ovec};
+  const int64_t no = c.table != nullptr ? c.oh_C : 0;
   const int vec = (reinterpret_cast<uintptr_t>(c.h) % 16 == 0) && (reinterpret_cast<uintptr_t>(c.ht) % 16 == 0) &&
                   (c.D % kVec == 0) && (c.ldht % kVec == 0);
   const TransposeArgs<T> ta{static_cast<const T*>(c.h), c.C, c.D, c.D, static_cast<T*>(c.ht), c.ldht, vec};
@@ -724,7 +727,7 @@ hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
 }
 
 hipError_t launch_chunk_prep(int dt, const ChunkPrep& c, hipStream_t s) {
-  if (c.C == 0) return hipSuccess;
+  if (c.C == 0 && (c.table == nullptr || c.oh_C == 0)) return hipSuccess;
   switch (dt) {
     case DT_F32: return chunk_prep_t<float>(c, s);
     case DT_BF16: return chunk_prep_t<__bf16>(c, s);

@@ -429,7 +429,7 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
-        old[r][ni] = __builtin_nontemporal_load(&tb[mc * e.ldo + (n < p.N ? n : p.N - 1)]);
+        old[r][ni] = e.tab_store ? (TT)0.0f : __builtin_nontemporal_load(&tb[mc * e.ldo + (n < p.N ? n : p.N - 1)]);
         val[r][ni] = acc[mi][ni][r] * sc;
       }
     }
@@ -473,6 +473,9 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
 // so the two 32-lane row groups of an accumulator write fall on distinct banks.
 __device__ __forceinline__ int tab_swz(int rr) { return ((rr >> 2) & 1) << 5; }
 
+// kFresh: the table holds no values yet (first chunk without accumulate): +0
+// stands in for the old values, which are not read.
+template <bool kFresh>
 __device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
                                                const Frag& f, const EpiLds& L) {
   static_assert(MI == 4 && kWaveM == 2 && kTileN == 256, "two halves of four 32-row regions");
@@ -500,9 +503,13 @@ __device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, i
   // quarter k of half h: regions 2k and 2k + 1, pieces [2k kPpr, (2k + 2) kPpr)
   auto load_q = [&](int h, int k, f32x4 (&o)[2 * kPpr]) {
 #pragma unroll
-    for (int j = 0; j < 2 * kPpr; ++j)
-      o[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rs, vbase, row_of(h, 2 * kPpr * k + j) * (int)e.ldo * 4, 2 /* nt */));
+    for (int j = 0; j < 2 * kPpr; ++j) {
+      if constexpr (kFresh)
+        o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      else
+        o[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rs, vbase, row_of(h, 2 * kPpr * k + j) * (int)e.ldo * 4, 2 /* nt */));
+    }
   };
   auto to_lds = [&](int h) {
 #pragma unroll
@@ -557,16 +564,25 @@ __device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, i
   store_q(1, 1, qb);
 }
 
-template <typename T>
+// Which dW epilogue a kernel carries (one per kernel keeps the code small: the
+// dH and dW tiles' loops run side by side and share the instruction cache):
+// ACC_FAST and ACC_FRESH are epi_accum_fast (an FP32 table whose one-hot rows
+// are added beforehand; FRESH for a first chunk without accumulate), ACC_ANY
+// decides at run time among the list-walking epilogues.
+enum AccMode : int { ACC_ANY = 0, ACC_FAST = 1, ACC_FRESH = 2 };
+
+template <typename T, int kAcc>
 __device__ __forceinline__ void epi_accum(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
-                          const Frag& f, const EpiLds& L) {
-  if (p.ep.out_dt == DT_F32) {
-    if (p.ep.tab_fast)
-      epi_accum_fast(p, acc, m0, n0, f, L);
-    else
-      epi_accum_t<T, float>(p, acc, m0, n0, f, L);
+                                          const Frag& f, const EpiLds& L) {
+  if constexpr (kAcc == ACC_FAST) {
+    epi_accum_fast<false>(p, acc, m0, n0, f, L);
+  } else if constexpr (kAcc == ACC_FRESH) {
+    epi_accum_fast<true>(p, acc, m0, n0, f, L);
   } else {
-    epi_accum_t<T, T>(p, acc, m0, n0, f, L);
+    if (p.ep.out_dt == DT_F32)
+      epi_accum_t<T, float>(p, acc, m0, n0, f, L);
+    else
+      epi_accum_t<T, T>(p, acc, m0, n0, f, L);
   }
 }
 
@@ -907,7 +923,7 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
   }
 }
 
-template <typename T, int E, bool kDma, bool kMn = false>
+template <typename T, int E, bool kDma, bool kMn = false, int kAcc = ACC_ANY>
 __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* const (&buf)[kNS]) {
   int tm, tn;
   tile_coords(id, p.tiles_m, p.tiles_n, tm, tn);
@@ -944,10 +960,10 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* con
   if constexpr (E == EPI_LSE_Q) epi_lse_partial<T, true>(p, acc, tm, m0, n0, f);
   if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f, L);
   if constexpr (E == EPI_STORE) epi_store<T>(p, acc, m0, n0, f, L);
-  if constexpr (E == EPI_ACCUM) epi_accum<T>(p, acc, m0, n0, f, L);
+  if constexpr (E == EPI_ACCUM) epi_accum<T, kAcc>(p, acc, m0, n0, f, L);
 }
 
-template <typename T, int E0, int E1, bool kDma, bool kMn0>
+template <typename T, int E0, int E1, bool kDma, bool kMn0, int kAcc>
 __device__ __forceinline__ void gemm_dispatch(const GemmProblem& p0, const GemmProblem& p1, int ntiles0,
                                               char* const (&buf)[kNS]) {
   const int bid = blockIdx.x;
@@ -955,12 +971,12 @@ __device__ __forceinline__ void gemm_dispatch(const GemmProblem& p0, const GemmP
     tile_run<T, E0, kDma, kMn0>(p0, xcd_remap(bid, ntiles0), buf);
   } else {
     const int b1 = bid - ntiles0;
-    if constexpr (E1 != EPI_NONE) tile_run<T, E1, kDma>(p1, xcd_remap(b1, (int)gridDim.x - ntiles0), buf);
+    if constexpr (E1 != EPI_NONE) tile_run<T, E1, kDma, false, kAcc>(p1, xcd_remap(b1, (int)gridDim.x - ntiles0), buf);
   }
 }
 
 // kMn0: the first problem's operands are K-row-major (DMA pipeline only)
-template <typename T, int E0, int E1, bool kDma, bool kMn0 = false>
+template <typename T, int E0, int E1, bool kDma, bool kMn0 = false, int kAcc = ACC_ANY>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmProblem p1, int ntiles0) {
   if constexpr (kDma) {
     // distinct LDS objects per slot (see kNS)
@@ -970,14 +986,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmP
     __shared__ __attribute__((aligned(16))) char st3[kStageArr];
     __shared__ __attribute__((aligned(16))) char st4[kStageArr];
     char* const buf[kNS] = {st0, st1, st2, st3, st4};
-    gemm_dispatch<T, E0, E1, true, kMn0>(p0, p1, ntiles0, buf);
+    gemm_dispatch<T, E0, E1, true, kMn0, kAcc>(p0, p1, ntiles0, buf);
   } else {
     static_assert(kLdsBytes >= 4 * kOpB, "epilogue regions fit in the staged buffer");
     __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
     // the epilogues use the first four regions; the fifth is never touched
     char* const buf[kNS] = {smem, smem + kOpB, smem + 2 * kOpB, smem + 3 * kOpB, smem};
     static_assert(!kMn0, "K-row-major operands need the DMA pipeline");
-    gemm_dispatch<T, E0, E1, false, false>(p0, p1, ntiles0, buf);
+    gemm_dispatch<T, E0, E1, false, false, ACC_ANY>(p0, p1, ntiles0, buf);
   }
 }
 
@@ -1004,15 +1020,27 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
     else gemm_kernel<T, EPI_DLOGITS, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
   } else if ((e0 == EPI_STORE || e0 == EPI_NONE) && (e1 == EPI_ACCUM || e1 == EPI_NONE)) {
     const bool mn = p0 != nullptr && p0->mn;
-    if constexpr (sizeof(T) == 2) {
-      if (mn && dma) {
-        gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, true><<<grid, block, 0, s>>>(a, b, nt0);
-        return hipGetLastError();
+    // the dW epilogue of this launch (any mode serves when there are no dW tiles)
+    const int acc = p1 == nullptr ? ACC_FAST
+                    : !p1->ep.tab_fast ? ACC_ANY
+                    : p1->ep.tab_store ? ACC_FRESH
+                                       : ACC_FAST;
+    if (mn && !(sizeof(T) == 2 && dma)) return hipErrorInvalidValue;  // K-row-major: 16-bit, DMA pipeline
+    if (!dma) {
+      gemm_kernel<T, EPI_STORE, EPI_ACCUM, false><<<grid, block, 0, s>>>(a, b, nt0);
+    } else if (mn) {
+      if constexpr (sizeof(T) == 2) {
+        if (acc == ACC_FAST) gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, true, ACC_FAST><<<grid, block, 0, s>>>(a, b, nt0);
+        else if (acc == ACC_FRESH)
+          gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, true, ACC_FRESH><<<grid, block, 0, s>>>(a, b, nt0);
+        else gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, true, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
       }
+    } else {
+      if (acc == ACC_FAST) gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, false, ACC_FAST><<<grid, block, 0, s>>>(a, b, nt0);
+      else if (acc == ACC_FRESH)
+        gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, false, ACC_FRESH><<<grid, block, 0, s>>>(a, b, nt0);
+      else gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, false, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
     }
-    if (mn) return hipErrorInvalidValue;  // K-row-major operands: 16-bit types, DMA pipeline
-    if (dma) gemm_kernel<T, EPI_STORE, EPI_ACCUM, true><<<grid, block, 0, s>>>(a, b, nt0);
-    else gemm_kernel<T, EPI_STORE, EPI_ACCUM, false><<<grid, block, 0, s>>>(a, b, nt0);
   } else {
     return hipErrorInvalidValue;
   }

@@ -66,6 +66,8 @@ struct EpiParams {
   const int32_t* next;     // [C] next chunk token with the same target, -1 at the end
   int64_t ntok;            // tokens in the chunk
   int tab_fast;            // FP32 table without one-hot part, D % 4 == 0, 16-byte aligned, tile span < 2 GiB
+  int tab_store;           // the table holds no values yet (first chunk, no accumulate): +0 stands in for
+                           // the old values, which are not read (so no zero fill is needed)
   // EPI_STORE and EPI_ACCUM
   void* out;
   int64_t ldo;
@@ -155,6 +157,10 @@ struct ChunkPrep {
   const float* tcoef;
   float* table;  // [V][ldt] FP32 dW table, or null
   int64_t ldt;
+  // one-hot rows of tokens [oh_tok0, oh_tok0 + oh_C) (h rows from oh_h); may
+  // span the previous chunk too when that chunk's rows were deferred
+  int64_t oh_tok0, oh_C;
+  const void* oh_h;
   // transpose of the chunk's h rows (also read by the one-hot rows)
   const void* h;  // first row of the chunk
   int64_t D;

@@ -213,8 +213,14 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t e = esize(dtype);
   const int64_t te = (dW_dtype == LLP_F32) ? 4 : e;
+  // Without accumulate the first chunk's dW contraction stores into the
+  // table instead of adding (+0 standing in for the old values), so the table
+  // is zero-filled only when there is no chunk. An FP32 table's one-hot rows
+  // of that first chunk are added after it, by the next chunk's preparation
+  // (or by a launch of their own when there is one chunk).
+  const bool store_first = want_dW && !accumulate && N > 0;
   if (!accumulate) {
-    if (want_dW) LLP_LAUNCH(LLP_K_SMALL, launch_zero(dW, V * D, (int)te, s));
+    if (want_dW && !store_first) LLP_LAUNCH(LLP_K_SMALL, launch_zero(dW, V * D, (int)te, s));
     if (want_db) LLP_LAUNCH(LLP_K_SMALL, launch_zero(db, V, (int)te, s));
   }
   if (N == 0 || !(want_dH || want_dW || want_db)) return LLP_OK;
@@ -313,10 +319,14 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       cp.D = D;
       cp.ht = ht;
       cp.ldht = bp.ldSt;
-      if (dW_dtype == LLP_F32) {  // the one-hot rows go into the table here
+      if (dW_dtype == LLP_F32 && !(store_first && k == 0)) {  // the one-hot rows go into the table here
         cp.tcoef = tcoef;
         cp.table = static_cast<float*>(dW);
         cp.ldt = D;
+        // after a storing first chunk, chunk 1 adds the rows of both, in token order
+        cp.oh_tok0 = (store_first && k == 1) ? 0 : c0;
+        cp.oh_C = c0 + Ck - cp.oh_tok0;
+        cp.oh_h = static_cast<const char*>(h) + cp.oh_tok0 * D * e;
       }
     }
     if (fused) {
@@ -407,12 +417,30 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.head = dW_dtype == LLP_F32 ? nullptr : head;  // null: one-hot rows already added
       pw.ep.next = next;
       pw.ep.tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < 0x7FFFFFF0LL;
+      pw.ep.tab_store = (store_first && k == 0) ? 1 : 0;
       pw.ep.ntok = Ck;
       pw.ep.scales = scales;
       pw.ep.chunk = (int)k;
     }
     if (want_dH || want_dW)
       LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, want_dH ? &ph : nullptr, want_dW ? &pw : nullptr, s));
+  }
+  if (store_first && bp.K == 1 && dW_dtype == LLP_F32) {
+    // one chunk: its one-hot rows follow the contraction that stored the table
+    ChunkPrep cp = {};
+    cp.V = V;
+    cp.D = D;
+    cp.targets = targets;
+    cp.g = g;
+    cp.v0 = v0;
+    cp.Vt = Vt;
+    cp.tcoef = tcoef;
+    cp.table = static_cast<float*>(dW);
+    cp.ldt = D;
+    cp.oh_tok0 = 0;
+    cp.oh_C = N;
+    cp.oh_h = h;
+    LLP_LAUNCH(LLP_K_TRANSPOSE, launch_chunk_prep(dtype, cp, s));
   }
   return LLP_OK;
 }
