@@ -123,33 +123,45 @@ __device__ __forceinline__ void softmax_grad_tile(int64_t bx, int64_t by, const 
   float* coef_s = reinterpret_cast<float*>(smem + 64 * (64 + kVec) * sizeof(T));
   int32_t* t_s = reinterpret_cast<int32_t*>(coef_s + 64);
   const int64_t v0 = bx * 64, n0 = by * 64;
+  const int c = threadIdx.x % kCpr;
+  const bool full_n = n0 + (c + 1) * kVec <= C;
+  constexpr int kPass = 64 / kRpp;
+  // the tile's numerators are loaded first (they do not depend on the
+  // coefficients), and the coefficients' loads are unconditional (clamped
+  // index), so a tile waits for about one round trip
+  u32x4 x[kPass];
+#pragma unroll
+  for (int ps = 0; ps < kPass; ++ps) {
+    const int64_t v = v0 + threadIdx.x / kCpr + ps * kRpp;
+    if (v < V && full_n) x[ps] = *reinterpret_cast<const u32x4*>(qt + v * ldq + n0 + c * kVec);
+  }
   if (threadIdx.x < 64) {
     // column n: the token's factor -(g / s) 2^(m_b - lse log2 e); 64-row tiles lie in one 128-row block
     const int64_t n = n0 + threadIdx.x;
+    const int64_t nc = n < C ? n : C - 1;
+    const int64_t tt = targets[nc];
+    const float gv = g[nc];
+    const float m2 = partials[(v0 >> 7) * ldp + nc].x;
+    const float ln = lse[nc];
     float coef = 0.0f;
     int32_t t = -1;
-    if (n < C) {
-      const int64_t tt = targets[n];
-      const float gv = g[n];
-      if (tt >= 0 && tt < V && gv != 0.0f) {
-        const float m2 = partials[(v0 >> 7) * ldp + n].x;
-        const float f = (m2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m2 - lse[n] * kLog2e);
-        coef = -(gv * scales[chunk].y) * f;
-        t = (int32_t)tt;
-      }
+    if (n < C && tt >= 0 && tt < V && gv != 0.0f) {
+      const float f = (m2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m2 - ln * kLog2e);
+      coef = -(gv * scales[chunk].y) * f;
+      t = (int32_t)tt;
     }
     coef_s[threadIdx.x] = coef;
     t_s[threadIdx.x] = t;
   }
   __syncthreads();
-  const int c = threadIdx.x % kCpr;
-  const bool full_n = n0 + (c + 1) * kVec <= C;
-  for (int i = threadIdx.x / kCpr; i < 64; i += kRpp) {
+#pragma unroll
+  for (int ps = 0; ps < kPass; ++ps) {
+    const int i = threadIdx.x / kCpr + ps * kRpp;
     const int64_t v = v0 + i;
     T val[kVec];
     if (v < V && full_n) {
       T* q = qt + v * ldq + n0 + c * kVec;
-      *reinterpret_cast<u32x4*>(val) = *reinterpret_cast<const u32x4*>(q);
+      *reinterpret_cast<u32x4*>(val) = x[ps];
 #pragma unroll
       for (int j = 0; j < kVec; ++j) {
         const int nl = c * kVec + j;
