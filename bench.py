@@ -75,7 +75,8 @@ def traffic_from_profiles(kernel: str, workload: str):
 
 
 # rocprofv3 kernel names -> the launch-trace kinds of the library
-PMC_KERNELS = {"dh_dw": ("Li3ELi4E",), "dlogits": ("Li2ELi0E",), "fwd_lse": ("Li1ELi0E", "gemm_kernel<bool _Accum")}
+PMC_KERNELS = {"dh_dw": ("Li3ELi4E",), "dlogits": ("Li2ELi0E",), "fwd_lse": ("Li1ELi0E", "gemm_kernel<bool _Accum"),
+               "dh_dw_fwd": ("gemm3_kernel",)}
 COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
 
 
@@ -102,7 +103,7 @@ def summarize_pmc(args):
     counters' units to bytes."""
     fetch, write, cfetch, cwrite = args.summarize_pmc
     pats = PMC_KERNELS[args.pmc_kernel]
-    is_k = lambda n: "gemm_kernel" in n and any(x in n for x in pats)  # noqa: E731
+    is_k = lambda n: ("gemm_kernel" in n or "gemm3_kernel" in n) and any(x in n for x in pats)  # noqa: E731
     is_copy = lambda n: "copyBuffer" in n or "copy_kernel" in n  # noqa: E731
     f_val, f_n = pmc_per_dispatch(fetch, is_k)
     w_val, w_n = pmc_per_dispatch(write, is_k)
@@ -222,7 +223,8 @@ def run_linear(w, args, torch, llp):
     for name, step, plf in (
             ("split", split_step, {"fwd_lse": 2 * N * V * D, "dlogits": 2 * N * V * D / K,
                                    "dh_dw": 4 * N * V * D / K}),
-            ("fused", fused_step, {"fwd_lse": 2 * N * V * D / K, "dh_dw": 4 * N * V * D / K})):
+            ("fused", fused_step, {"fwd_lse": 2 * N * V * D / K, "dh_dw": 4 * N * V * D / K,
+                                   "dh_dw_fwd": 6 * N * V * D / K})):
         log(f"{name}: warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
         ms, tr = time_steps(step, args, torch, llp, stream)
         kernels = kernel_table(tr, args.steps, plf)

@@ -997,6 +997,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmP
   }
 }
 
+// One chunk's dH (K-row-major operands) and dW tiles together with the next
+// chunk's forward tiles (EPI_LSE_Q), which write their own numerator and
+// partial buffers: the launch tails overlap. The dW tiles, the shortest, come
+// last.
+template <typename T, int kAcc>
+__global__ __launch_bounds__(kThreads, 1) void gemm3_kernel(GemmProblem p0, GemmProblem p1, GemmProblem p2,
+                                                             int nt0, int nt2) {
+  __shared__ __attribute__((aligned(16))) char st0[kStageArr];
+  __shared__ __attribute__((aligned(16))) char st1[kStageArr];
+  __shared__ __attribute__((aligned(16))) char st2[kStageArr];
+  __shared__ __attribute__((aligned(16))) char st3[kStageArr];
+  __shared__ __attribute__((aligned(16))) char st4[kStageArr];
+  char* const buf[kNS] = {st0, st1, st2, st3, st4};
+  const int bid = blockIdx.x;
+  if (bid < nt0) {
+    tile_run<T, EPI_STORE, true, true, kAcc>(p0, xcd_remap(bid, nt0), buf);
+  } else if (bid < nt0 + nt2) {
+    tile_run<T, EPI_LSE_Q, true, false, kAcc>(p2, xcd_remap(bid - nt0, nt2), buf);
+  } else {
+    tile_run<T, EPI_ACCUM, true, false, kAcc>(p1, xcd_remap(bid - nt0 - nt2, (int)gridDim.x - nt0 - nt2), buf);
+  }
+}
+
+template <typename T>
+hipError_t launch3_t(const GemmProblem& p0, const GemmProblem* p1, const GemmProblem& p2, hipStream_t s) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorInvalidValue;
+  } else {
+    const int nt0 = p0.tiles_m * p0.tiles_n, nt2 = p2.tiles_m * p2.tiles_n;
+    const int nt1 = p1 ? p1->tiles_m * p1->tiles_n : 0;
+    GemmProblem empty = {};
+    const GemmProblem& b = p1 ? *p1 : empty;
+    const int acc = p1 == nullptr ? ACC_FAST : !p1->ep.tab_fast ? ACC_ANY : p1->ep.tab_store ? ACC_FRESH : ACC_FAST;
+    if (!p0.mn || !p0.dma || !p2.dma || (p1 && !p1->dma) || acc == ACC_ANY || p0.epi != EPI_STORE ||
+        p2.epi != EPI_LSE_Q)
+      return hipErrorInvalidValue;
+    dim3 grid(nt0 + nt1 + nt2), block(kThreads);
+    if (acc == ACC_FAST) gemm3_kernel<T, ACC_FAST><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+    else gemm3_kernel<T, ACC_FRESH><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+    return hipGetLastError();
+  }
+}
+
 template <typename T>
 hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s) {
   const int nt0 = p0 ? p0->tiles_m * p0->tiles_n : 0;
@@ -1048,6 +1091,14 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t launch_gemm3(int dt, const GemmProblem& p0, const GemmProblem* p1, const GemmProblem& p2, hipStream_t s) {
+  switch (dt) {
+    case DT_BF16: return launch3_t<__bf16>(p0, p1, p2, s);
+    case DT_F16: return launch3_t<_Float16>(p0, p1, p2, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemm(int dt, const GemmProblem* p0, const GemmProblem* p1, hipStream_t s) {
   switch (dt) {

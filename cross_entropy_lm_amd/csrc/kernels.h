@@ -97,6 +97,10 @@ struct GemmProblem {
 // Launch one or two independent problems of the same operand dtype in one
 // grid (the second problem's tiles follow the first's). Returns hipError_t.
 hipError_t launch_gemm(int dt, const GemmProblem* p0, const GemmProblem* p1, hipStream_t s);
+// A chunk's dH (p0: EPI_STORE, K-row-major operands) and dW (p1: EPI_ACCUM,
+// fast epilogue, or null) with the next chunk's forward (p2: EPI_LSE_Q) in one
+// grid; 16-bit operands, DMA pipeline. Returns hipErrorInvalidValue otherwise.
+hipError_t launch_gemm3(int dt, const GemmProblem& p0, const GemmProblem* p1, const GemmProblem& p2, hipStream_t s);
 
 // partials [P][N] + zt -> logp, lse (one thread per token, fixed order over P).
 hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,

@@ -261,6 +261,36 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     dS = nullptr;
   }
   if (want_dH && !mn) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
+  // Fused path with two numerator / partial buffers: chunk k + 1's forward
+  // tiles run in the launch of chunk k's dH / dW (its fast epilogue only).
+  const bool tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < lim;
+  const bool overlap = fused && mn && aligned16(h) && bp.off_dSt2 >= 0 && (!want_dW || tab_fast);
+  void* const dSt_buf[2] = {dSt, overlap ? at(workspace, bp.off_dSt2) : dSt};
+  float2* const part_buf[2] = {part, overlap ? reinterpret_cast<float2*>(at(workspace, bp.off_part2)) : part};
+  // the forward tile problem and the combine of chunk kk (fused path)
+  auto fwd_problem = [&](int64_t kk) {
+    const int64_t c0 = kk * bp.C;
+    const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
+    GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
+    p.ep.bias = b;
+    p.ep.targets = targets;
+    p.ep.tok0 = c0;
+    p.ep.v0 = v0;
+    p.ep.Vt = Vt;
+    p.epi = EPI_LSE_Q;
+    p.ep.partials = part_buf[kk & 1];
+    p.ep.ldp = bp.C;
+    p.ep.zt = zt;
+    p.ep.dSt = dSt_buf[kk & 1];
+    p.ep.ldSt = bp.ldSt;
+    return p;
+  };
+  auto combine = [&](int64_t kk) {
+    const int64_t c0 = kk * bp.C;
+    const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
+    return launch_lse_combine(part_buf[kk & 1], bp.P, bp.C, zt + c0, targets + c0, V, Ck, logp_out + c0,
+                              lse_fused + c0, g + c0, tcoef + c0, s);
+  };
   // per-chunk target lists: walked by db and by an operand-dtype dW table's
   // epilogue (an FP32 table takes its one-hot rows in the chunk preparation)
   const bool lists = want_db || (want_dW && dW_dtype != LLP_F32);
@@ -268,6 +298,8 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   for (int64_t k = 0; k < bp.K; ++k) {
     const int64_t c0 = k * bp.C;
     const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
+    void* const dSt = dSt_buf[k & 1];      // this chunk's numerator / dlogits^T buffer
+    float2* const part = part_buf[k & 1];  // and its forward partials
     GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
     p.ep.bias = b;
     p.ep.targets = targets;
@@ -276,15 +308,12 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     p.ep.Vt = Vt;
     if (fused) {
       // the chunk's logits tile: lse partials, target logits, softmax numerators
-      p.epi = EPI_LSE_Q;
-      p.ep.partials = part;
-      p.ep.ldp = bp.C;
-      p.ep.zt = zt;
-      p.ep.dSt = dSt;
-      p.ep.ldSt = bp.ldSt;
-      LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &p, nullptr, s));
-      LLP_LAUNCH(LLP_K_COMBINE, launch_lse_combine(part, bp.P, bp.C, zt + c0, targets + c0, V, Ck, logp_out + c0,
-                                                   lse_fused + c0, g + c0, tcoef + c0, s));
+      // (with overlap, chunks after the first were launched with the previous dH / dW)
+      if (!overlap || k == 0) {
+        const GemmProblem pf = fwd_problem(k);
+        LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &pf, nullptr, s));
+        LLP_LAUNCH(LLP_K_COMBINE, combine(k));
+      }
     } else {
       // dlogits of the chunk, recomputed from the logits tile and the saved lse
       p.epi = EPI_DLOGITS;
@@ -422,8 +451,14 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.scales = scales;
       pw.ep.chunk = (int)k;
     }
-    if (want_dH || want_dW)
+    if (overlap && k + 1 < bp.K) {
+      // with the next chunk's forward tiles, then that chunk's combine
+      const GemmProblem pf = fwd_problem(k + 1);
+      LLP_LAUNCH(LLP_K_DH_DW_FWD, launch_gemm3(dtype, ph, want_dW ? &pw : nullptr, pf, s));
+      LLP_LAUNCH(LLP_K_COMBINE, combine(k + 1));
+    } else if (want_dH || want_dW) {
       LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, want_dH ? &ph : nullptr, want_dW ? &pw : nullptr, s));
+    }
   }
   if (store_first && bp.K == 1 && dW_dtype == LLP_F32) {
     // one chunk: its one-hot rows follow the contraction that stored the table

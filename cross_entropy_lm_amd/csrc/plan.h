@@ -114,6 +114,10 @@ struct BwdPlan {
   int64_t P = 0;                         // partial rows per token: kWaveM per vocab tile
   int64_t off_part = -1;                 // float2 [P][C]: one chunk's forward partials
   int64_t off_zt = -1;                   // float [N]: target logits
+  // second numerator and partial buffers (16-bit operands, dH, K >= 2): the
+  // next chunk's forward then runs in the same launch as this chunk's dH / dW
+  int64_t off_dSt2 = -1;
+  int64_t off_part2 = -1;
   int64_t bytes = 0;
 };
 
@@ -159,6 +163,11 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   if (want_dW || want_db || fused) {
     if (!mul_ok(V, p->ldSt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_dSt = L.add(n);
+    if (fused && e == 2 && want_dH && p->K >= 2) {
+      p->off_dSt2 = L.add(n);
+      if (!mul_ok(p->P, p->C, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
+      p->off_part2 = L.add(n);
+    }
   }
   if (want_dW) {
     if (!mul_ok(D, p->ldSt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
