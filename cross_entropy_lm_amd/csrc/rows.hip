@@ -22,6 +22,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kRowThreads = 256;
+#ifndef LLP_BWD_UNROLL
+#define LLP_BWD_UNROLL 4
+#endif
+constexpr int kBwdUnroll = LLP_BWD_UNROLL;  // 16-byte pieces per thread in flight (backward)
 
 template <typename T> struct RT;
 template <> struct RT<__bf16> { static constexpr int per16 = 8; };
@@ -183,19 +187,21 @@ __global__ __launch_bounds__(kRowThreads) void rows_bwd_kernel(const T* X, int64
   u32x4* dv = reinterpret_cast<u32x4*>(dx + head);
   const int64_t nv = (V - head) / per16;
   int64_t j = tid;
-  for (; j + kRowThreads < nv; j += 2 * kRowThreads) {
-    const u32x4 a0 = xv[j], a1 = xv[j + kRowThreads];
-    float f0[per16], f1[per16];
-    unpack<T>(a0, f0);
-    unpack<T>(a1, f1);
-    const int64_t v0 = head + j * per16, v1 = v0 + (int64_t)kRowThreads * per16;
+  // kBwdUnroll 16-byte pieces per thread in flight; the row is streamed once,
+  // so loads and stores are non-temporal
+  for (; j + (kBwdUnroll - 1) * kRowThreads < nv; j += kBwdUnroll * kRowThreads) {
+    u32x4 a[kBwdUnroll];
 #pragma unroll
-    for (int i = 0; i < per16; ++i) {
-      f0[i] = grad1<T>(f0[i], v0 + i, t, gv, l2, valid);
-      f1[i] = grad1<T>(f1[i], v1 + i, t, gv, l2, valid);
+    for (int u = 0; u < kBwdUnroll; ++u) a[u] = __builtin_nontemporal_load(&xv[j + u * kRowThreads]);
+#pragma unroll
+    for (int u = 0; u < kBwdUnroll; ++u) {
+      float f[per16];
+      unpack<T>(a[u], f);
+      const int64_t v0 = head + (j + u * kRowThreads) * per16;
+#pragma unroll
+      for (int i = 0; i < per16; ++i) f[i] = grad1<T>(f[i], v0 + i, t, gv, l2, valid);
+      __builtin_nontemporal_store(pack<T>(f), &dv[j + u * kRowThreads]);
     }
-    dv[j] = pack<T>(f0);
-    dv[j + kRowThreads] = pack<T>(f1);
   }
   for (; j < nv; j += kRowThreads) {
     float f0[per16];
