@@ -165,15 +165,47 @@ def time_steps(step, args, torch, llp, stream):
     return e0.elapsed_time(e1) / args.steps, llp.llp_trace_read()
 
 
-def kernel_table(tr, steps, per_launch_flops):
+def kernel_table(tr, steps, step_flops):
+    """Per launch kind: time per step, launches, average launch time and (for
+    the contractions) TFLOP/s = the kind's algorithmic flop per step / its time
+    per step, i.e. the average launch's flop over the average launch time."""
     kernels = {}
     for k, (tms, cnt) in tr.items():
         if cnt == 0:
             continue
         kernels[k] = {"ms_per_step": tms / steps, "launches_per_step": cnt / steps, "avg_launch_ms": tms / cnt}
-        if per_launch_flops.get(k):
-            kernels[k]["tflops"] = per_launch_flops[k] / (tms / cnt * 1e-3) / 1e12
+        if step_flops.get(k):
+            kernels[k]["tflops"] = step_flops[k] / (tms / steps * 1e-3) / 1e12
+            kernels[k]["flop_per_launch"] = step_flops[k] / (cnt / steps)
     return kernels
+
+
+def fused_step_flops(N, D, V, C, K, overlap, pairing):
+    """Algorithmic flop per step of each contraction launch kind of the single
+    call: chunk k's logits tile, dH and (its share of) dW each cost 2 C_k V D.
+    With overlap, chunk k + 1's forward tiles ride in chunk k's dH / dW launch
+    (dh_dw_fwd) and only chunk 0's forward has a launch of its own; with
+    pairing, the dW of chunks (2j, 2j + 1) runs in the launch of chunk 2j + 1
+    (or of a last chunk without a partner)."""
+    ck = [min(C, N - k * C) for k in range(K)]
+    f = 2 * V * D
+    out = {"fwd_lse": 0, "dh_dw": 0, "dh_dw_fwd": 0}
+    for k in range(K):
+        if pairing:
+            dw = f * (ck[k - 1] + ck[k]) if k % 2 == 1 else (f * ck[k] if k == K - 1 else 0)
+        else:
+            dw = f * ck[k]
+        if overlap:
+            if k == 0:
+                out["fwd_lse"] += f * ck[0]
+            if k + 1 < K:
+                out["dh_dw_fwd"] += f * ck[k] + dw + f * ck[k + 1]
+            else:
+                out["dh_dw"] += f * ck[k] + dw
+        else:
+            out["fwd_lse"] += f * ck[k]
+            out["dh_dw"] += f * ck[k] + dw
+    return out
 
 
 def run_linear(w, args, torch, llp):
@@ -220,14 +252,17 @@ def run_linear(w, args, torch, llp):
     model_flops = A.linear_model_flops(N, D, V)
     peak = PEAK_TFLOPS[w.dtype]
     results = {}
-    for name, step, plf in (
-            ("split", split_step, {"fwd_lse": 2 * N * V * D, "dlogits": 2 * N * V * D / K,
-                                   "dh_dw": 4 * N * V * D / K}),
-            ("fused", fused_step, {"fwd_lse": 2 * N * V * D / K, "dh_dw": 4 * N * V * D / K,
-                                   "dh_dw_fwd": 6 * N * V * D / K})):
+    # the single call overlaps the next chunk's forward with 16-bit operands and
+    # runs dW once per pair of chunks with an FP32 table (K >= 2)
+    pairing = args.table == "f32" and K >= 2
+    overlap = w.dtype in ("bf16", "f16") and pairing
+    for name, step, sf in (
+            ("split", split_step, {"fwd_lse": 2 * N * V * D, "dlogits": 2 * N * V * D,
+                                   "dh_dw": 4 * N * V * D}),
+            ("fused", fused_step, fused_step_flops(N, D, V, C, K, overlap, pairing))):
         log(f"{name}: warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
         ms, tr = time_steps(step, args, torch, llp, stream)
-        kernels = kernel_table(tr, args.steps, plf)
+        kernels = kernel_table(tr, args.steps, sf)
         mfma = {k: v for k, v in kernels.items() if "tflops" in v}
         results[name] = {
             "ms_per_step": ms, "tokens_per_s": A.tokens_per_s(N, ms),

@@ -753,16 +753,17 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
     const int nrec = bytes < 0x7FFFFFF0LL ? (int)bytes : 0x7FFFFFF0;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
   };
-  auto rsrc_mn = [](const void* base, int64_t off, int64_t K, int64_t ld) {
-    // from column `off` of K row 0 to the end of the [K][ld] buffer
-    const int64_t bytes = (K * ld - off) * (int64_t)sizeof(T);
+  auto rsrc_mn = [](const void* base, int64_t off, int64_t K, int64_t ld, int64_t cols) {
+    // from column `off` of K row 0 to column round8(cols) of K row K - 1 (the
+    // operand may be the column range of a wider buffer that ends there)
+    const int64_t bytes = ((K - 1) * ld + ((cols + 7) & ~int64_t(7)) - off) * (int64_t)sizeof(T);
     const int nrec = bytes < 0x7FFFFFF0LL ? (int)bytes : 0x7FFFFFF0;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(base) + off), (short)0, nrec,
                                              0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t rsA = kMn ? rsrc_mn(p.A, m0, p.K, p.lda)
+  const __amdgpu_buffer_rsrc_t rsA = kMn ? rsrc_mn(p.A, m0, p.K, p.lda, p.M)
                                          : rsrc_of(static_cast<const T*>(p.A) + m0 * p.lda, p.M - m0, p.lda);
-  const __amdgpu_buffer_rsrc_t rsB = kMn ? rsrc_mn(p.B, n0, p.K, p.ldb)
+  const __amdgpu_buffer_rsrc_t rsB = kMn ? rsrc_mn(p.B, n0, p.K, p.ldb, p.N)
                                          : rsrc_of(static_cast<const T*>(p.B) + n0 * p.ldb, p.N - n0, p.ldb);
   // Per-lane offsets of the wave's first DMA instruction of a unit; the
   // others follow at a wave-uniform stride (the swizzle term depends on the
@@ -770,15 +771,17 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
   uint32_t voA, voB, strA, strB;
   int kel;  // K-contiguous: first K element of this lane's chunk
   if constexpr (kMn) {
-    static_assert(kThreads / 64 == 8 && kLoads == 4, "K-row-major placement: 8 waves x 4 instructions per unit");
-    // instruction j of wave w moves K rows 2w + 16j + {0, 1} (lanes 0-31, 32-63),
-    // so a lane's K row modulo 4, and with it the swizzle, is the same for every j
+    constexpr int nw = kThreads / 64;
+    static_assert(nw % 2 == 0 && kLoads * 2 * nw == 64, "K-row-major placement: two K rows per instruction");
+    // instruction j of wave w moves K rows 2w + 2 nw j + {0, 1} (lanes 0-31,
+    // 32-63); 2 nw is a multiple of 4, so a lane's K row modulo 4, and with it
+    // the swizzle, is the same for every j
     const int krow = 2 * wave + (lane >> 5);        // K row of the stage this lane moves first
     const int c = (lane & 31) ^ (4 * (krow & 3));   // LDS chunk lane & 31 holds global chunk c
     voA = (uint32_t)(krow * p.lda * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
     voB = (uint32_t)(krow * p.ldb * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
-    strA = (uint32_t)(16 * p.lda * (int64_t)sizeof(T));
-    strB = (uint32_t)(16 * p.ldb * (int64_t)sizeof(T));
+    strA = (uint32_t)(2 * nw * p.lda * (int64_t)sizeof(T));
+    strB = (uint32_t)(2 * nw * p.ldb * (int64_t)sizeof(T));
     kel = 0;
   } else {
     const int row = (wave * kLoads) * kRowsPerLoad + (lane >> 3);
@@ -804,8 +807,8 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
         off = vo + (uint32_t)(s * BKE * (O ? p.ldb : p.lda) * (int64_t)sizeof(T));
       else
         off = (s * BKE + kel < p.K) ? vo + (uint32_t)(s * kSB) : 0xFFFFFFF0u;
-      // K-row-major: the 1 KiB block of instruction j holds K rows 2w + 16j, +1
-      char* const dst = kMn ? slot + wave * 1024 + j * 8192 : slot + lds_off + j * kRowsPerLoad * kSB;
+      // K-row-major: the 1 KiB block of instruction j holds K rows 2w + 2 nw j, +1
+      char* const dst = kMn ? slot + wave * 1024 + j * (kThreads / 64) * 1024 : slot + lds_off + j * kRowsPerLoad * kSB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(O ? rsB : rsA, (lds_void_t*)dst, 16, off, 0, 0, 0);
     }
   };

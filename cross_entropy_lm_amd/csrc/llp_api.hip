@@ -225,8 +225,22 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   }
   if (N == 0 || !(want_dH || want_dW || want_db)) return LLP_OK;
 
+  const int64_t lim = 0x7FFFFFF0LL;
+  const bool tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < lim;
+  // Fused path with an FP32 table: one dW contraction per pair of chunks
+  // (2j, 2j + 1) over the columns of both, which sit side by side in the
+  // vocab-major buffer [V][2 ldSt] and the h^T buffer [D][2 ldSt]: the table
+  // is read and written once per pair. The pair shares one power-of-two scale
+  // (scale index = pair index), so both halves of the contraction agree.
+  const bool pairing = fused && want_dW && tab_fast && bp.K >= 2 && bp.ldP == 2 * bp.ldSt;
+  const int64_t ldq = pairing ? bp.ldP : bp.ldSt;  // leading dimension of those buffers
+  auto sidx = [&](int64_t k) { return (int)(pairing ? k >> 1 : k); };
+  // the chunk whose launch carries the first dW contraction
+  const int64_t fdw = pairing ? 1 : 0;
+
   float2* scales = reinterpret_cast<float2*>(at(workspace, bp.off_scales));
-  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, bp.C, bp.K, dtype == LLP_F16 ? 15 : 0, scales, s));
+  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, pairing ? 2 * bp.C : bp.C, pairing ? ceil_div(bp.K, 2) : bp.K,
+                                              dtype == LLP_F16 ? 15 : 0, scales, s));
   const float* lse_use = lse;
   float* lse_fused = nullptr;  // where the fused path writes lse
   if (fused) {
@@ -252,10 +266,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   // the tile's rows contiguous: dlogits^T [V][ldSt] and W [V][D] itself. Then
   // neither W^T nor the token-major dlogits copy is formed. 16-bit operands on
   // the DMA pipeline only; the vocab-major copy must be in the workspace.
-  const int64_t lim = 0x7FFFFFF0LL;
   const bool dw_dma = !want_dW || (aligned16(dSt) && aligned16(ht));
   const bool mn = want_dH && e == 2 && dSt != nullptr && aligned16(W) && aligned16(dSt) && D % 8 == 0 &&
-                  V * D * e < lim && V * bp.ldSt * e < lim && dw_dma;
+                  V * D * e < lim && V * ldq * e < lim && dw_dma;
   if (mn) {
     Wt = nullptr;
     dS = nullptr;
@@ -263,10 +276,19 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   if (want_dH && !mn) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
   // Fused path with two numerator / partial buffers: chunk k + 1's forward
   // tiles run in the launch of chunk k's dH / dW (its fast epilogue only).
-  const bool tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < lim;
   const bool overlap = fused && mn && aligned16(h) && bp.off_dSt2 >= 0 && (!want_dW || tab_fast);
   void* const dSt_buf[2] = {dSt, overlap ? at(workspace, bp.off_dSt2) : dSt};
   float2* const part_buf[2] = {part, overlap ? reinterpret_cast<float2*>(at(workspace, bp.off_part2)) : part};
+  // chunk k's numerator / dlogits^T columns: with pairing, half k % 2 of the
+  // buffer of pair k / 2 (the pairs alternate between the two buffers with
+  // overlap); the h^T columns likewise, in the one h^T buffer
+  auto qbuf = [&](int64_t k) -> void* {
+    if (!pairing) return dSt_buf[k & 1];
+    return static_cast<char*>(dSt_buf[(k >> 1) & 1]) + (k & 1) * bp.ldSt * e;
+  };
+  auto hbuf = [&](int64_t k) -> void* {
+    return pairing ? static_cast<char*>(ht) + (k & 1) * bp.ldSt * e : ht;
+  };
   // the forward tile problem and the combine of chunk kk (fused path)
   auto fwd_problem = [&](int64_t kk) {
     const int64_t c0 = kk * bp.C;
@@ -281,8 +303,8 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     p.ep.partials = part_buf[kk & 1];
     p.ep.ldp = bp.C;
     p.ep.zt = zt;
-    p.ep.dSt = dSt_buf[kk & 1];
-    p.ep.ldSt = bp.ldSt;
+    p.ep.dSt = qbuf(kk);
+    p.ep.ldSt = ldq;
     return p;
   };
   auto combine = [&](int64_t kk) {
@@ -298,7 +320,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   for (int64_t k = 0; k < bp.K; ++k) {
     const int64_t c0 = k * bp.C;
     const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
-    void* const dSt = dSt_buf[k & 1];      // this chunk's numerator / dlogits^T buffer
+    void* const dSt = qbuf(k);             // this chunk's numerator / dlogits^T columns
     float2* const part = part_buf[k & 1];  // and its forward partials
     GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
     p.ep.bias = b;
@@ -323,9 +345,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       p.ep.dS = dS;
       p.ep.ldS = bp.ldS;
       p.ep.dSt = (want_dW || want_db || mn) ? dSt : nullptr;
-      p.ep.ldSt = bp.ldSt;
+      p.ep.ldSt = ldq;
       p.ep.scales = scales;
-      p.ep.chunk = (int)k;
+      p.ep.chunk = sidx(k);
       LLP_LAUNCH(LLP_K_DLOGITS, launch_gemm(dtype, &p, nullptr, s));
     }
     // one launch: target lists, the chunk's h transposed, and (fused) the softmax gradient
@@ -346,41 +368,42 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     if (want_dW) {
       cp.h = static_cast<const char*>(h) + c0 * D * e;
       cp.D = D;
-      cp.ht = ht;
-      cp.ldht = bp.ldSt;
-      if (dW_dtype == LLP_F32 && !(store_first && k == 0)) {  // the one-hot rows go into the table here
+      cp.ht = hbuf(k);
+      cp.ldht = ldq;
+      if (dW_dtype == LLP_F32 && !(store_first && k <= fdw)) {  // the one-hot rows go into the table here
         cp.tcoef = tcoef;
         cp.table = static_cast<float*>(dW);
         cp.ldt = D;
-        // after a storing first chunk, chunk 1 adds the rows of both, in token order
-        cp.oh_tok0 = (store_first && k == 1) ? 0 : c0;
+        // after the contraction that stored the table, the next chunk adds the
+        // rows of every chunk so far, in token order
+        cp.oh_tok0 = (store_first && k == fdw + 1) ? 0 : c0;
         cp.oh_C = c0 + Ck - cp.oh_tok0;
         cp.oh_h = static_cast<const char*>(h) + cp.oh_tok0 * D * e;
       }
     }
     if (fused) {
       cp.qt = dSt;
-      cp.ldq = bp.ldSt;
+      cp.ldq = ldq;
       cp.partials = part;
       cp.ldp = bp.C;
       cp.lse = lse_fused + c0;
       cp.gc = g + c0;
       cp.tc = targets + c0;
       cp.scales = scales;
-      cp.chunk = (int)k;
+      cp.chunk = sidx(k);
       cp.dS = dS;
       cp.ldS = bp.ldS;
     }
     if (cp.head != nullptr || cp.ht != nullptr || cp.qt != nullptr || cp.table != nullptr)
       LLP_LAUNCH(fused ? LLP_K_DLOGITS : LLP_K_TRANSPOSE, launch_chunk_prep(dtype, cp, s));
     if (want_db)
-      LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, bp.ldSt, V, Ck, scales, (int)k, head, next, targets, g, tcoef,
+      LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, ldq, V, Ck, scales, sidx(k), head, next, targets, g, tcoef,
                               c0, v0, Vt, db, dW_dtype, s));
     GemmProblem ph = {}, pw = {};
     if (want_dH && mn) {
       ph.A = dSt;
       ph.B = W;
-      ph.lda = bp.ldSt;
+      ph.lda = ldq;
       ph.ldb = D;
       ph.M = Ck;
       ph.N = D;
@@ -416,16 +439,21 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       ph.ep.W = W;
       ph.ep.ldW = D;
       ph.ep.scales = scales;
-      ph.ep.chunk = (int)k;
+      ph.ep.chunk = sidx(k);
     }
-    if (want_dW) {
-      pw.A = dSt;
-      pw.B = ht;
-      pw.lda = bp.ldSt;
-      pw.ldb = bp.ldSt;
+    // with pairing, the dW contraction of pair j runs in the launch of its
+    // second chunk (or of a last chunk without a partner), over K = ldSt + Ck
+    // columns (the first chunk's padding columns are +0 in both operands)
+    const bool do_dw = want_dW && (!pairing || (k & 1) || k == bp.K - 1);
+    if (do_dw) {
+      const bool second = pairing && (k & 1);
+      pw.A = second ? qbuf(k - 1) : dSt;
+      pw.B = second ? hbuf(k - 1) : hbuf(k);
+      pw.lda = ldq;
+      pw.ldb = ldq;
       pw.M = V;
       pw.N = D;
-      pw.K = Ck;
+      pw.K = second ? bp.ldSt + Ck : Ck;
       pw.a_vec = pw.b_vec = 1;
       pw.dma = dma_ok(pw, e, true);  // dlogits^T and h^T padding columns are written +0
       pw.tiles_m = (int)ceil_div(V, kTile);
@@ -436,7 +464,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.out_dt = dW_dtype;
       pw.ep.targets = targets;
       pw.ep.g = g;
-      pw.ep.tok0 = c0;
+      pw.ep.tok0 = second ? c0 - bp.C : c0;
       pw.ep.V = V;
       pw.ep.v0 = v0;
       pw.ep.Vt = Vt;
@@ -446,22 +474,23 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.head = dW_dtype == LLP_F32 ? nullptr : head;  // null: one-hot rows already added
       pw.ep.next = next;
       pw.ep.tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < 0x7FFFFFF0LL;
-      pw.ep.tab_store = (store_first && k == 0) ? 1 : 0;
+      pw.ep.tab_store = (store_first && k == fdw) ? 1 : 0;
       pw.ep.ntok = Ck;
       pw.ep.scales = scales;
-      pw.ep.chunk = (int)k;
+      pw.ep.chunk = sidx(k);
     }
     if (overlap && k + 1 < bp.K) {
       // with the next chunk's forward tiles, then that chunk's combine
       const GemmProblem pf = fwd_problem(k + 1);
-      LLP_LAUNCH(LLP_K_DH_DW_FWD, launch_gemm3(dtype, ph, want_dW ? &pw : nullptr, pf, s));
+      LLP_LAUNCH(LLP_K_DH_DW_FWD, launch_gemm3(dtype, ph, do_dw ? &pw : nullptr, pf, s));
       LLP_LAUNCH(LLP_K_COMBINE, combine(k + 1));
-    } else if (want_dH || want_dW) {
-      LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, want_dH ? &ph : nullptr, want_dW ? &pw : nullptr, s));
+    } else if (want_dH || do_dw) {
+      LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, want_dH ? &ph : nullptr, do_dw ? &pw : nullptr, s));
     }
   }
-  if (store_first && bp.K == 1 && dW_dtype == LLP_F32) {
-    // one chunk: its one-hot rows follow the contraction that stored the table
+  if (store_first && bp.K == fdw + 1 && dW_dtype == LLP_F32) {
+    // the contraction that stored the table was the last one: the one-hot
+    // rows of every chunk follow it
     ChunkPrep cp = {};
     cp.V = V;
     cp.D = D;

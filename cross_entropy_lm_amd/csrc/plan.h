@@ -99,14 +99,18 @@ inline int plan_fwd(int64_t N, int64_t D, int64_t V, int dtype, FwdPlan* p) {
 struct BwdPlan {
   int64_t C = 0, K = 0;                  // tokens per chunk, number of chunks
   int64_t ldWt = 0, ldS = 0, ldSt = 0;   // leading dimensions (elements), multiples of 8
+  // leading dimension of the vocab-major and h^T buffers: 2 ldSt in the fused
+  // layout with dW and K >= 2, whose buffers hold a pair of chunks (chunk 2j in
+  // the columns [0, C), chunk 2j + 1 from column ldSt), else ldSt
+  int64_t ldP = 0;
   int64_t off_scales = -1;               // float2 [K]
   int64_t off_lse = -1;                  // float [N] when the caller gives no lse
   FwdPlan fwd;                           // and the forward's workspace, placed after it
   int64_t off_fwd = -1;
   int64_t off_Wt = -1;                   // W^T [D][ldWt]            (dH)
   int64_t off_dS = -1;                   // dlogits [C][ldS]         (dH)
-  int64_t off_dSt = -1;                  // dlogits^T [V][ldSt]      (dW or db)
-  int64_t off_ht = -1;                   // h^T of one chunk [D][ldSt] (dW)
+  int64_t off_dSt = -1;                  // dlogits^T [V][ldP]       (dW or db)
+  int64_t off_ht = -1;                   // h^T of one chunk (or pair) [D][ldP] (dW)
   int64_t off_tcoef = -1;                // float [N]: one-hot part g (1 - p_t) per token
   int64_t off_head = -1;                 // int32 [V]: first chunk token per target   (dW or db)
   int64_t off_next = -1;                 // int32 [C]: next chunk token, same target (dW or db)
@@ -137,6 +141,7 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   p->ldWt = round_up(V, 8);
   p->ldS = round_up(V, 8);
   p->ldSt = round_up(p->C, 8);
+  p->ldP = (fused && want_dW && p->K >= 2) ? 2 * p->ldSt : p->ldSt;
   Layout L;
   int64_t n;
   p->off_scales = L.add(p->K * 8);
@@ -161,7 +166,7 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     p->off_dS = L.add(n);
   }
   if (want_dW || want_db || fused) {
-    if (!mul_ok(V, p->ldSt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
+    if (!mul_ok(V, p->ldP, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_dSt = L.add(n);
     if (fused && e == 2 && want_dH && p->K >= 2) {
       p->off_dSt2 = L.add(n);
@@ -170,7 +175,7 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     }
   }
   if (want_dW) {
-    if (!mul_ok(D, p->ldSt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
+    if (!mul_ok(D, p->ldP, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_ht = L.add(n);
   }
   p->off_tcoef = L.add(N * 4);

@@ -275,3 +275,33 @@ def test_fused_bias_big_vocab_default_chunk():
     rw, rb = O.linear_logp_vocab_rows(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], vr)
     assert_close(dW[vr], rw, *tg, "dW")
     assert_close(db[vr], rb, *tg, "db")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_fused_dw_chunk_pairs(dt):
+    """The FP32 table takes one dW contraction per pair of chunks: K = 2 (the
+    pair's store is the last contraction and the one-hot rows of both chunks
+    follow it), K = 3 (a last chunk without a partner), K = 4 with a ragged
+    last chunk, and K = 5 with accumulate; dW and db against the oracle, dH
+    bitwise equal to the unchunked run's."""
+    w = synth.LinearWorkload(f"pairs_{dt}", 300, 136, 1031, dt, True, 128, "normal")
+    d = synth.make_linear_t(w, DEV)
+    host = synth.make_linear_np(w)
+    _, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], False, True,
+                                    True)
+    tg = TOL[dt]["grad"]
+    ref = fused(w, d, chunk=300)
+    for chunk in (150, 100, 80):  # K = 2, 3, 4 (last chunk 60 tokens)
+        _, _, dH, dW, db = fused(w, d, chunk=chunk)
+        assert bits_equal(dH, ref[2]), chunk
+        assert_close(dW, rdW, *tg, f"dW chunk {chunk}")
+        assert_close(db, rdb, *tg, f"db chunk {chunk}")
+    gen = torch.Generator().manual_seed(11)
+    a0 = torch.randn((w.V, w.D), generator=gen).to(DEV)
+    b0 = torch.randn((w.V,), generator=gen).to(DEV)
+    _, _, _, dW, db = fused(w, d, want=(True, True, True), chunk=64, accumulate=True, dW=a0.clone(),
+                            db=b0.clone())  # K = 5
+    _, adW, adb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], False, True,
+                                    True, dW0=a0.cpu().double().numpy(), db0=b0.cpu().double().numpy())
+    assert_close(dW, adW, *tg, "dW accumulate, chunk 64")
+    assert_close(db, adb, *tg, "db accumulate, chunk 64")
