@@ -76,7 +76,7 @@ def traffic_from_profiles(kernel: str, workload: str):
 
 # rocprofv3 kernel names -> the launch-trace kinds of the library
 PMC_KERNELS = {"dh_dw": ("Li3ELi4E",), "dlogits": ("Li2ELi0E",), "fwd_lse": ("Li1ELi0E", "gemm_kernel<bool _Accum"),
-               "dh_dw_fwd": ("gemm3_kernel",)}
+               "dh_dw_fwd": ("gemm3_kernel",), "rows_fwd": ("rows_fwd_kernel",), "rows_bwd": ("rows_bwd_kernel",)}
 COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
 
 
@@ -103,7 +103,8 @@ def summarize_pmc(args):
     counters' units to bytes."""
     fetch, write, cfetch, cwrite = args.summarize_pmc
     pats = PMC_KERNELS[args.pmc_kernel]
-    is_k = lambda n: ("gemm_kernel" in n or "gemm3_kernel" in n) and any(x in n for x in pats)  # noqa: E731
+    rows = args.pmc_kernel.startswith("rows")
+    is_k = lambda n: (rows or "gemm_kernel" in n or "gemm3_kernel" in n) and any(x in n for x in pats)  # noqa: E731
     is_copy = lambda n: "copyBuffer" in n or "copy_kernel" in n  # noqa: E731
     f_val, f_n = pmc_per_dispatch(fetch, is_k)
     w_val, w_n = pmc_per_dispatch(write, is_k)
@@ -269,6 +270,23 @@ def run_linear(w, args, torch, llp):
             "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / (peak * 1e12),
             "pct_mfma_peak_model_flops": 100.0 * model_flops / (ms * 1e-3) / (peak * 1e12),
             "dominant": max(mfma, key=lambda k: mfma[k]["ms_per_step"]), "kernels": kernels}
+    # same-box reference: the vendor GEMM (hipBLASLt through torch.matmul) on
+    # the forward logits shape, logits written to HBM, no epilogue
+    Wt_ = d["W"].t()
+    hmat = d["h"]
+    for _ in range(2):
+        z = torch.matmul(hmat, Wt_)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        z = torch.matmul(hmat, Wt_)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_gemm = e0.elapsed_time(e1) / 3
+    del z
+    gemm_ref = {"ms": ms_gemm, "tflops": 2 * N * V * D / (ms_gemm * 1e-3) / 1e12,
+                "what": f"torch.matmul h [{N},{D}] x W^T -> [{N},{V}] logits ({w.dtype}), vendor GEMM, no epilogue"}
     main = results[args.path]
     other = "split" if args.path == "fused" else "fused"
     dom = main["dominant"]
@@ -296,6 +314,7 @@ def run_linear(w, args, torch, llp):
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_from_profiles(dom, w.name)},
         "kernels": main["kernels"],
+        "gemm_reference": gemm_ref,
         other: {"path": PATHS[other], **results[other]},
         **({"cpu_baseline": {k: v for k, v in cpu.items() if not k.startswith("_")}}
            if cpu is not None and not args.no_cpu_baseline else {}),
@@ -392,6 +411,37 @@ def run_logits(w, args, torch, llp):
                           "GBps": nbytes[k] / (tms / cnt * 1e-3) / 1e9}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     total = A.logits_only_bytes(N, V, 2)
+    out = {
+        "metric": "fwd+bwd logits-only logp N32768 V151936 bf16; GB/s",
+        "value": total / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded counter-based generator)",
+        "config": {"workload": w.name, "N": N, "V": V, "peak_extra_bytes": peak_extra},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBps"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": kernels[dom]["GBps"] / PEAK_HBM_GBS,
+                     "traffic": traffic_from_profiles(dom, w.name)},
+        "kernels": kernels,
+        "cpu_baseline": {"value": S * V * 3 * 2 / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                         "sample": f"first {S} rows: FP64 numpy oracle logp + dlogits, {dt:.2f} s"},
+    }
+    def copy_reference(dst):
+        # same-box reference: a plain device copy of the same bytes (one read
+        # and one write of the logits, what rows_bwd moves), into a buffer
+        # whose contents are no longer needed
+        for _ in range(2):
+            dst.copy_(d["logits"])
+        e0.record(stream)
+        for _ in range(args.steps):
+            dst.copy_(d["logits"])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_copy = e0.elapsed_time(e1) / args.steps
+        out["copy_reference"] = {"ms": ms_copy, "GBps": 2 * N * V * 2 / (ms_copy * 1e-3) / 1e9,
+                                 "what": "torch copy_ of the logits into a same-size buffer (1 read + 1 write)"}
+
+    if args.no_lse_free:
+        copy_reference(dl)
+        return out
     # the backward for a caller that kept no lse: the row is reduced, then
     # written (two reads, one write); its dlogits equal the saved-lse ones bit for bit
     dl2 = torch.empty_like(dl)
@@ -406,21 +456,10 @@ def run_logits(w, args, torch, llp):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_nolse = e0.elapsed_time(e1) / args.steps
-    return {
-        "metric": "fwd+bwd logits-only logp N32768 V151936 bf16; GB/s",
-        "value": total / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded counter-based generator)",
-        "config": {"workload": w.name, "N": N, "V": V, "peak_extra_bytes": peak_extra},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBps"], "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": kernels[dom]["GBps"] / PEAK_HBM_GBS,
-                     "traffic": traffic_from_profiles(dom, w.name)},
-        "kernels": kernels,
-        "bwd_without_lse": {"ms": ms_nolse, "GBps": 3 * N * V * 2 / (ms_nolse * 1e-3) / 1e9,
-                            "bytes": "2 reads + 1 write of the logits", "bitwise_equal_to_saved_lse": same},
-        "cpu_baseline": {"value": S * V * 3 * 2 / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                         "sample": f"first {S} rows: FP64 numpy oracle logp + dlogits, {dt:.2f} s"},
-    }
+    out["bwd_without_lse"] = {"ms": ms_nolse, "GBps": 3 * N * V * 2 / (ms_nolse * 1e-3) / 1e9,
+                              "bytes": "2 reads + 1 write of the logits", "bitwise_equal_to_saved_lse": same}
+    copy_reference(dl2)
+    return out
 
 
 def main():
@@ -441,6 +480,9 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="print the HBM traffic summary of --pmc-kernel from rocprofv3 counter CSVs")
     ap.add_argument("--pmc-kernel", default="dh_dw", choices=sorted(PMC_KERNELS))
+    ap.add_argument("--no-lse-free", action="store_true",
+                    help="logits-only workload: leave out the extra timing of the backward without a saved lse "
+                         "(so that every rows_bwd dispatch of a profiled run is the saved-lse one)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args)
