@@ -36,7 +36,8 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float m, float s) 
 __global__ __launch_bounds__(kCombTok * kCombSl) void lse_combine_kernel(
     const float2* __restrict__ partials, int64_t P, int64_t ldp, const float* __restrict__ zt,
     const int64_t* __restrict__ targets, int64_t V, int64_t N, float* __restrict__ logp,
-    float* __restrict__ lse, const float* __restrict__ g, float* __restrict__ tcoef) {
+    float* __restrict__ lse, const float* __restrict__ g, float* __restrict__ tcoef,
+    const int32_t* __restrict__ qflag, const float2* __restrict__ sc, float* __restrict__ cq) {
   __shared__ float2 part[kCombSl][kCombTok];
   const int tk = threadIdx.x % kCombTok, sl = threadIdx.x / kCombTok;
   const int64_t n = (int64_t)blockIdx.x * kCombTok + tk;
@@ -72,6 +73,13 @@ __global__ __launch_bounds__(kCombTok * kCombSl) void lse_combine_kernel(
     const float pt = (t >= 0 && t < V) ? __builtin_amdgcn_exp2f(fmaf(zt[n], kLog2e, -(l * kLog2e))) : 0.0f;
     tcoef[n] = (t >= 0 && t < V && gv != 0.0f) ? fmaf(-gv, pt, gv) : 0.0f;
   }
+  if (cq != nullptr) {
+    // per-token mode: the factor that turns the stored 2^(z log2 e) into -(g / s) p
+    // (a flagged token's column is rescaled to p itself before use)
+    const float gv = g[n];
+    const float e = qflag[n] ? 1.0f : __builtin_amdgcn_exp2f(-(l * kLog2e));
+    cq[n] = (t >= 0 && t < V && gv != 0.0f) ? -(gv * sc[0].y) * e : 0.0f;
+  }
 }
 
 // Fused forward + backward, one chunk of C tokens: from the stored numerators
@@ -97,6 +105,8 @@ struct SoftmaxGradArgs {
   int64_t V, C;
   T* dS;
   int64_t ldS;
+  // per-token mode: only the columns of flagged tokens are rescaled (qfix_tile)
+  const int32_t* qflag;
 };
 
 template <typename T>
@@ -209,6 +219,36 @@ __device__ __forceinline__ void softmax_grad_tile(int64_t bx, int64_t by, const 
   }
 }
 
+// Per-token mode: the column of a token whose numerators were stored partly
+// block-relative (qflag set) becomes 2^(z log2 e - lse log2 e) = p, in place:
+// a block b (128 rows) in range holds 2^(z log2 e) (factor 2^(-lse log2 e)),
+// any other block 2^(z log2 e - m_b) (factor 2^(m_b - lse log2 e)), a block of
+// -inf holds +0. The same range test as the forward's. A workgroup takes 64
+// tokens x 1024 vocab rows and returns at once when none of its tokens is flagged.
+template <typename T>
+__device__ __forceinline__ void qfix_tile(int64_t bx, int64_t by, const SoftmaxGradArgs<T>& a) {
+  const int tn = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int64_t n = by * 64 + tn;
+  const bool fl = n < a.C && a.qflag[n] != 0;
+  if (!__syncthreads_or(fl ? 1 : 0)) return;
+  if (!fl) return;  // no barrier follows
+  const float l2 = a.lse[n] * kLog2e;
+  const int64_t v0 = bx * 1024, v1 = (a.V < v0 + 1024) ? a.V : v0 + 1024;
+  int64_t bcur = -1;
+  float fac = 0.0f;
+  for (int64_t v = v0 + rg; v < v1; v += 4) {
+    const int64_t b = v >> 7;
+    if (b != bcur) {
+      bcur = b;
+      const float m2 = a.partials[b * a.ldp + n].x;
+      const bool inr = m2 >= kQtokLo && m2 <= kQtokHi;
+      fac = (m2 == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((inr ? 0.0f : m2) - l2);
+    }
+    T* q = a.qt + v * a.ldq + n;
+    *q = (T)((float)*q * fac);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void softmax_grad_kernel(SoftmaxGradArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[softmax_grad_lds<T>()];
@@ -254,6 +294,7 @@ struct TransposeArgs {
   T* dst;
   int64_t ldd;
   int vec;
+  const float* rowscale;  // [rows] or null: dst[c][r] = src[r][c] rowscale[r], rounded once
 };
 
 template <typename T>
@@ -282,6 +323,11 @@ __device__ __forceinline__ void transpose_tile(int64_t bx, int64_t by, const Tra
     } else {
 #pragma unroll
       for (int j = 0; j < kVec; ++j) v[j] = (r < rows && c + j < cols) ? src[r * lds + c + j] : (T)0;
+    }
+    if (a.rowscale != nullptr && r < rows) {
+      const float rs = a.rowscale[r];
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) v[j] = (T)((float)v[j] * rs);
     }
 #pragma unroll
     for (int j = 0; j < kVec; ++j) tile[i][ch * kVec + j] = v[j];
@@ -353,12 +399,16 @@ __global__ void db_accum_kernel(const T* __restrict__ dSt, int64_t ldSt, int64_t
                                 const int32_t* __restrict__ head, const int32_t* __restrict__ next,
                                 const int64_t* __restrict__ targets, const float* __restrict__ g,
                                 const float* __restrict__ tcoef, int64_t tok0, int64_t v0, int64_t Vt,
-                                TT* __restrict__ db) {
+                                TT* __restrict__ db, const float* __restrict__ cq) {
   const int lane = threadIdx.x & 63;
   const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (v >= V) return;  // uniform per wave
   float s = 0.0f;
-  for (int64_t c = lane; c < C; c += 64) s += (float)dSt[v * ldSt + c];
+  if (cq == nullptr) {
+    for (int64_t c = lane; c < C; c += 64) s += (float)dSt[v * ldSt + c];
+  } else {  // per-token mode: the stored value times the token's factor (chunk-local cq)
+    for (int64_t c = lane; c < C; c += 64) s += (float)dSt[v * ldSt + c] * cq[c];
+  }
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) {
     float val = s * scales[chunk].x;
@@ -603,7 +653,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(OnehotArgs<T> oa, int64
     return;
   }
   b -= nt;
-  softmax_grad_tile<T>(b % sgx, b / sgx, sa, smem);
+  if (sa.qflag != nullptr)
+    qfix_tile<T>(b % sgx, b / sgx, sa);
+  else
+    softmax_grad_tile<T>(b % sgx, b / sgx, sa, smem);
 }
 
 __global__ void fill_kernel(uint32_t* __restrict__ p, int64_t nwords, uint32_t word) {
@@ -633,15 +686,16 @@ hipError_t transpose_t(const void* src, int64_t rows, int64_t cols, int64_t lds,
 template <typename T>
 hipError_t db_t(const void* dSt, int64_t ldSt, int64_t V, int64_t C, const float2* scales, int chunk,
                 const int32_t* head, const int32_t* next, const int64_t* targets, const float* g,
-                const float* tcoef, int64_t tok0, int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s) {
+                const float* tcoef, int64_t tok0, int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s,
+                const float* cq) {
   dim3 grid((unsigned)((V + 3) / 4));
   if (tdt == DT_F32)
     db_accum_kernel<T, float><<<grid, 256, 0, s>>>(static_cast<const T*>(dSt), ldSt, V, C, scales, chunk,
                                                    head, next, targets, g, tcoef, tok0, v0, Vt,
-                                                   static_cast<float*>(db));
+                                                   static_cast<float*>(db), cq);
   else
     db_accum_kernel<T, T><<<grid, 256, 0, s>>>(static_cast<const T*>(dSt), ldSt, V, C, scales, chunk,
-                                               head, next, targets, g, tcoef, tok0, v0, Vt, static_cast<T*>(db));
+                                               head, next, targets, g, tcoef, tok0, v0, Vt, static_cast<T*>(db), cq);
   return hipGetLastError();
 }
 
@@ -649,10 +703,12 @@ hipError_t db_t(const void* dSt, int64_t ldSt, int64_t V, int64_t C, const float
 
 hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,
                               const int64_t* targets, int64_t V, int64_t N, float* logp,
-                              float* lse, const float* g, float* tcoef, hipStream_t s) {
+                              float* lse, const float* g, float* tcoef, hipStream_t s,
+                              const int32_t* qflag, const float2* sc, float* cq) {
   if (N == 0) return hipSuccess;
+  if (cq != nullptr && (qflag == nullptr || sc == nullptr || g == nullptr)) return hipErrorInvalidValue;
   lse_combine_kernel<<<(unsigned)((N + kCombTok - 1) / kCombTok), kCombTok * kCombSl, 0, s>>>(
-      partials, P, ldp, zt, targets, V, N, logp, lse, g, tcoef);
+      partials, P, ldp, zt, targets, V, N, logp, lse, g, tcoef, qflag, sc, cq);
   return hipGetLastError();
 }
 
@@ -718,12 +774,13 @@ hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
   const int64_t no = c.table != nullptr ? c.oh_C : 0;
   const int vec = (reinterpret_cast<uintptr_t>(c.h) % 16 == 0) && (reinterpret_cast<uintptr_t>(c.ht) % 16 == 0) &&
                   (c.D % kVec == 0) && (c.ldht % kVec == 0);
-  const TransposeArgs<T> ta{static_cast<const T*>(c.h), c.C, c.D, c.D, static_cast<T*>(c.ht), c.ldht, vec};
+  const TransposeArgs<T> ta{static_cast<const T*>(c.h), c.C, c.D, c.D, static_cast<T*>(c.ht), c.ldht, vec, c.cq};
   const int64_t tgx = (c.C + 63) / 64;
   const int64_t nt = c.ht != nullptr ? tgx * ((c.D + 63) / 64) : 0;
-  const SoftmaxGradArgs<T> sa = sg_args<T>(c.qt, c.ldq, c.partials, c.ldp, c.lse, c.gc, c.tc, c.scales, c.chunk, c.V,
-                                           c.C, c.dS, c.ldS);
-  const int64_t sgx = (c.V + 63) / 64;
+  SoftmaxGradArgs<T> sa = sg_args<T>(c.qt, c.ldq, c.partials, c.ldp, c.lse, c.gc, c.tc, c.scales, c.chunk, c.V,
+                                     c.C, c.dS, c.ldS);
+  sa.qflag = c.qflag;  // per-token mode: the fixup of flagged columns instead of the gradient pass
+  const int64_t sgx = c.qflag != nullptr ? (c.V + 1023) / 1024 : (c.V + 63) / 64;
   const int64_t ns = c.qt != nullptr ? sgx * ((c.C + 63) / 64) : 0;
   const int64_t total = no + nl + nt + ns;
   if (total == 0) return hipSuccess;
@@ -731,6 +788,7 @@ hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
     if (no) onehot_rows_kernel<T><<<(unsigned)no, 256, 0, s>>>(oa);
     if (nl) target_lists_kernel<<<(unsigned)nl, 256, 0, s>>>(la);
     if (nt) transpose_kernel<T><<<dim3((unsigned)tgx, (unsigned)(nt / tgx)), 256, 0, s>>>(ta);
+    if (ns && c.qflag != nullptr) return hipErrorInvalidValue;  // the fixup runs in the joint launch only
     if (ns) softmax_grad_kernel<T><<<dim3((unsigned)sgx, (unsigned)(ns / sgx)), 256, 0, s>>>(sa);
     return hipGetLastError();
   }
@@ -758,15 +816,16 @@ hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, 
 hipError_t launch_db_accum(int dt, const void* dSt, int64_t ldSt, int64_t V, int64_t C,
                            const float2* scales, int chunk, const int32_t* head, const int32_t* next,
                            const int64_t* targets, const float* g, const float* tcoef, int64_t tok0,
-                           int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s) {
+                           int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s, const float* cq) {
   switch (dt) {
     case DT_F32:
-      return db_t<float>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, v0, Vt, db, tdt, s);
+      return db_t<float>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, v0, Vt, db, tdt, s, cq);
     case DT_BF16:
-      return db_t<__bf16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, v0, Vt, db, tdt, s);
+      return db_t<__bf16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, v0, Vt, db, tdt, s,
+                          cq);
     case DT_F16:
       return db_t<_Float16>(dSt, ldSt, V, C, scales, chunk, head, next, targets, g, tcoef, tok0, v0, Vt, db, tdt,
-                            s);
+                            s, cq);
     default: return hipErrorInvalidValue;
   }
 }

@@ -215,12 +215,23 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, 
     T* col[NI];     // this lane's column of the tile in the vocab-major buffer
     bool keep[NI];  // the column lies in [0, round8(N)); past N it stores +0
     bool live[NI];
+    float mul[NI];  // stored value = q mul (per-token mode: 2^m for a block in range)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int64_t n = n0 + f.col(ni);
       col[ni] = static_cast<T*>(e.dSt) + n;
       keep[ni] = n < npad;
       live[ni] = n < p.N;
+      mul[ni] = 1.0f;
+      // every row of the block is -inf (masked, or past V): its q are 0, not
+      // 2^(-inf - (-inf))
+      if (m2[ni] == -INFINITY) live[ni] = false;
+      if (e.qtok) {
+        const bool inr = m2[ni] >= kQtokLo && m2[ni] <= kQtokHi;
+        if (inr) mul[ni] = __builtin_amdgcn_exp2f(m2[ni]);
+        // lanes l and l + 32 hold the same column and block: one of them flags it
+        if (!inr && m2[ni] != -INFINITY && f.lane < 32 && n < p.N) e.qflag[e.tok0 + n] = 1;
+      }
     }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -233,7 +244,9 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, 
           // a block whose rows all lie past V has m = -inf; its rows are not stored
           const float q = __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2[ni]));
           s[ni] += q;
-          if (v < p.M && keep[ni]) col[ni][off] = (T)(live[ni] ? q : 0.0f);
+          // per-token mode: the target's entry is +0 (its one-hot part is exact elsewhere)
+          const bool st = live[ni] && !(e.qtok && v == tgt[ni]);
+          if (v < p.M && keep[ni]) col[ni][off] = (T)(st ? q * mul[ni] : 0.0f);
         }
       }
   }
@@ -362,12 +375,15 @@ __device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_
   const float sc = e.scales[e.chunk].x;
   int32_t* ts = reinterpret_cast<int32_t*>(smem);
   float* cs = reinterpret_cast<float*>(smem + kTileM * sizeof(int32_t));
+  float* fs = reinterpret_cast<float*>(smem + kTileM * (sizeof(int32_t) + sizeof(float)));
   for (int i = threadIdx.x; i < kTileM; i += kThreads) {
     const int64_t m = m0 + i;
     int64_t t = -1;
     const bool valid = m < p.M && token_valid(e, e.tok0 + m, t);
     ts[i] = valid ? (int32_t)t : -1;
     cs[i] = valid ? e.tcoef[e.tok0 + m] : 0.0f;
+    // per-token mode: the row's factor s rowf (s a power of two, so the product is exact)
+    fs[i] = e.rowf == nullptr ? sc : (m < p.M ? sc * e.rowf[e.tok0 + m] : 0.0f);
   }
   __syncthreads();
 #pragma unroll
@@ -379,10 +395,12 @@ __device__ __forceinline__ void epi_store(const GemmProblem& p, Acc& acc, int64_
       const int32_t tr = ts[rl];
       const T* wrow = W + (int64_t)(tr >= 0 ? tr : 0) * e.ldW;  // row 0 stands in; its value is not used
       const float c = cs[rl];
+      const float fr = fs[rl];
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const int64_t n = n0 + f.col(ni);
-        const float base = acc[mi][ni][r] * sc;
+        // a zero factor (a token that takes no part) gives +0, whatever the sign of C
+        const float base = fr == 0.0f ? 0.0f : acc[mi][ni][r] * fr;
         const float withw = fmaf(c, ld_f32(wrow, n < p.N ? n : 0), base);
         if (m < p.M && n < p.N) {
           const float o = tr >= 0 ? withw : base;

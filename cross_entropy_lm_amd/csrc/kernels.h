@@ -9,6 +9,13 @@
 
 namespace llp {
 
+// Per-token numerator mode (fused path, bf16): a 128-row block whose max m
+// (log2 units) lies in [kQtokLo, kQtokHi] stores 2^(z log2 e) itself. The range
+// keeps q and the fp32 sums of q W finite (m <= 64 nats) and keeps the
+// probabilities that matter out of bf16's subnormals (m >= -40 nats).
+constexpr float kQtokLo = -57.70780f;  // -40 log2 e
+constexpr float kQtokHi = 92.33248f;   // 64 log2 e
+
 // Element type codes (same values as llp_dtype).
 enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
@@ -46,7 +53,15 @@ struct EpiParams {
   int64_t ldp;
   float* zt;               // [tokens] target logit
   // EPI_LSE_Q also stores q = exp2(z log2 e - m) (m: the wave-row block's max, the
-  // partial's first member) into dSt [V][ldSt], +0 in columns [N, round8(N))
+  // partial's first member) into dSt [V][ldSt], +0 in columns [N, round8(N)).
+  // With qtok (bf16 operands) it stores instead, for a block whose max lies in
+  // [kQtokLo, kQtokHi] (log2 units), q = exp2(z log2 e), per-token units; a
+  // block of -inf stores +0; any other block stores the block-relative q and
+  // sets qflag[token] = 1. The target's entry is +0 in both cases.
+  int qtok;
+  int32_t* qflag;          // [tokens]
+  // EPI_STORE with qtok: out = s rowf[token] C + tcoef W[t] (+0 where rowf is 0)
+  const float* rowf;       // [tokens] per-token factor -(g / s) 2^(-lse log2 e), or null
   // EPI_DLOGITS (M = vocab, N = chunk tokens)
   const float* lse;        // [tokens]
   void* dS;                // [N][ldS] token-major softmax part / s, or null
@@ -103,9 +118,12 @@ hipError_t launch_gemm(int dt, const GemmProblem* p0, const GemmProblem* p1, hip
 hipError_t launch_gemm3(int dt, const GemmProblem& p0, const GemmProblem* p1, const GemmProblem& p2, hipStream_t s);
 
 // partials [P][N] + zt -> logp, lse (one thread per token, fixed order over P).
+// With cq (per-token mode), also cq[n] = -(g / s) 2^(-lse log2 e) for a valid token
+// without qflag, -(g / s) with it, +0 otherwise (s from sc = (s, 1 / s)).
 hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,
                               const int64_t* targets, int64_t V, int64_t N, float* logp,
-                              float* lse, const float* g, float* tcoef, hipStream_t s);
+                              float* lse, const float* g, float* tcoef, hipStream_t s,
+                              const int32_t* qflag = nullptr, const float2* sc = nullptr, float* cq = nullptr);
 
 // Fused forward + backward: softmax part of one chunk's dlogits from the stored
 // numerators, in place (vocab-major) and transposed into dS (token-major; dS may
@@ -130,7 +148,8 @@ hipError_t launch_chunk_scales(const float* g, int64_t N, int64_t C, int64_t K, 
 hipError_t launch_db_accum(int dt, const void* dSt, int64_t ldSt, int64_t V, int64_t C,
                            const float2* scales, int chunk, const int32_t* head, const int32_t* next,
                            const int64_t* targets, const float* g, const float* tcoef, int64_t tok0,
-                           int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s);
+                           int64_t v0, int64_t Vt, void* db, int tdt, hipStream_t s,
+                           const float* cq = nullptr);
 
 // Per chunk [tok0, tok0 + C): head[t] = first valid token with target t and
 // next[n] = the following one (-1 at the end), local indices, in token order.
@@ -152,6 +171,11 @@ hipError_t launch_shard_combine(const float* lse_sh, const float* zt_sh, int64_t
 // the chunk).
 struct ChunkPrep {
   int64_t C, V;
+  // per-token mode of the fused path (bf16): no softmax-gradient pass; the h
+  // transpose multiplies token n's row by cq[n] (chunk-local pointer) and the
+  // columns of flagged tokens (qflag) are rescaled to 2^(z log2 e - lse log2 e)
+  const float* cq;
+  const int32_t* qflag;
   // target lists and one-hot rows (targets, g, tcoef indexed tok0 + local token)
   const int64_t* targets;
   const float* g;

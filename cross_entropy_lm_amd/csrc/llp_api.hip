@@ -289,6 +289,19 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   auto hbuf = [&](int64_t k) -> void* {
     return pairing ? static_cast<char*>(ht) + (k & 1) * bp.ldSt * e : ht;
   };
+  // Per-token mode of the single call (bf16 operands, the layout of the
+  // K-row-major dH whether or not dH is asked for, so that every subset of
+  // outputs computes alike): the forward stores 2^(z log2 e) for blocks in
+  // range, the combine forms each token's factor -(g / s) 2^(-lse log2 e), and
+  // the consumers apply it: the dH epilogue per row, the dW contraction through
+  // the h transpose scaled per token, db per token. No softmax-gradient pass;
+  // the preparation only rescales the columns of flagged tokens.
+  const bool qtok = fused && dtype == LLP_BF16 && dSt != nullptr && aligned16(W) && aligned16(dSt) && D % 8 == 0 &&
+                    V * D * e < lim && V * 2 * bp.ldSt * e < lim && dw_dma;
+  if (qtok && want_dH && !mn) return LLP_EINVAL;  // not reached: the conditions above imply the K-row-major dH
+  int32_t* const qflag = qtok ? reinterpret_cast<int32_t*>(at(workspace, bp.off_qflag)) : nullptr;
+  float* const cq = qtok ? reinterpret_cast<float*>(at(workspace, bp.off_cq)) : nullptr;
+  if (qtok) LLP_LAUNCH(LLP_K_SMALL, launch_zero(qflag, N, 4, s));
   // the forward tile problem and the combine of chunk kk (fused path)
   auto fwd_problem = [&](int64_t kk) {
     const int64_t c0 = kk * bp.C;
@@ -305,13 +318,16 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     p.ep.zt = zt;
     p.ep.dSt = qbuf(kk);
     p.ep.ldSt = ldq;
+    p.ep.qtok = qtok ? 1 : 0;
+    p.ep.qflag = qflag;
     return p;
   };
   auto combine = [&](int64_t kk) {
     const int64_t c0 = kk * bp.C;
     const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
     return launch_lse_combine(part_buf[kk & 1], bp.P, bp.C, zt + c0, targets + c0, V, Ck, logp_out + c0,
-                              lse_fused + c0, g + c0, tcoef + c0, s);
+                              lse_fused + c0, g + c0, tcoef + c0, s, qtok ? qflag + c0 : nullptr,
+                              scales + sidx(kk), qtok ? cq + c0 : nullptr);
   };
   // per-chunk target lists: walked by db and by an operand-dtype dW table's
   // epilogue (an FP32 table takes its one-hot rows in the chunk preparation)
@@ -393,12 +409,16 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       cp.chunk = sidx(k);
       cp.dS = dS;
       cp.ldS = bp.ldS;
+      if (qtok) {
+        cp.cq = cq + c0;  // scales the chunk's h rows in the transpose
+        cp.qflag = qflag + c0;
+      }
     }
     if (cp.head != nullptr || cp.ht != nullptr || cp.qt != nullptr || cp.table != nullptr)
       LLP_LAUNCH(fused ? LLP_K_DLOGITS : LLP_K_TRANSPOSE, launch_chunk_prep(dtype, cp, s));
     if (want_db)
       LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, ldq, V, Ck, scales, sidx(k), head, next, targets, g, tcoef,
-                              c0, v0, Vt, db, dW_dtype, s));
+                              c0, v0, Vt, db, dW_dtype, s, qtok ? cq + c0 : nullptr));
     GemmProblem ph = {}, pw = {};
     if (want_dH && mn) {
       ph.A = dSt;
@@ -440,6 +460,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       ph.ep.ldW = D;
       ph.ep.scales = scales;
       ph.ep.chunk = sidx(k);
+      ph.ep.rowf = cq;  // per-token mode: indexed tok0 + row
     }
     // with pairing, the dW contraction of pair j runs in the launch of its
     // second chunk (or of a last chunk without a partner), over K = ldSt + Ck

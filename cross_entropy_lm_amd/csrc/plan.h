@@ -118,6 +118,8 @@ struct BwdPlan {
   int64_t P = 0;                         // partial rows per token: kWaveM per vocab tile
   int64_t off_part = -1;                 // float2 [P][C]: one chunk's forward partials
   int64_t off_zt = -1;                   // float [N]: target logits
+  int64_t off_qflag = -1;                // int32 [N]: per-token mode, tokens with block-relative numerators
+  int64_t off_cq = -1;                   // float [N]: per-token mode, the tokens' gradient factors
   // second numerator and partial buffers (16-bit operands, dH, K >= 2): the
   // next chunk's forward then runs in the same launch as this chunk's dH / dW
   int64_t off_dSt2 = -1;
@@ -158,6 +160,8 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     if (!mul_ok(p->P, p->C, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
     p->off_part = L.add(n);
     p->off_zt = L.add(N * 4);
+    p->off_qflag = L.add(N * 4);
+    p->off_cq = L.add(N * 4);
   }
   if (want_dH) {
     if (!mul_ok(D, p->ldWt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;

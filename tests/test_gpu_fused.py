@@ -305,3 +305,80 @@ def test_fused_dw_chunk_pairs(dt):
                                     True, dW0=a0.cpu().double().numpy(), db0=b0.cpu().double().numpy())
     assert_close(dW, adW, *tg, "dW accumulate, chunk 64")
     assert_close(db, adb, *tg, "db accumulate, chunk 64")
+
+
+def _oracle_all(h, W, b, t, g):
+    h64, W64 = h.double().cpu().numpy(), W.double().cpu().numpy()
+    b64 = b.double().cpu().numpy() if b is not None else None
+    t64, g64 = t.cpu().numpy(), g.double().cpu().numpy()
+    rlogp, rlse = O.linear_logp_fwd(h64, W64, b64, t64)
+    rdH, rdW, rdb = O.linear_logp_bwd(h64, W64, b64, t64, g64, True, True, b is not None)
+    return rlogp, rlse, rdH, rdW, rdb, h64 @ W64.T + (b64 if b64 is not None else 0.0)
+
+
+def _block_max_range(z):
+    """(smallest, largest) over tokens and 128-row vocab blocks of the block's max logit."""
+    V = z.shape[1]
+    m = np.stack([z[:, i:i + 128].max(axis=1) for i in range(0, V, 128)], axis=1)
+    return float(m.min()), float(m.max())
+
+
+def test_fused_bf16_logits_out_of_the_stored_range():
+    """bf16 numerators are stored per token (2^(z log2 e)) for 128-row blocks whose
+    max lies in [-40, 64] nats; other blocks are stored relative to their max and
+    their token's column is rescaled before use. Mixed batch: 64 tokens with h
+    scaled by 256 (block maxima far above 64 nats) beside
+    ordinary tokens; then every logit near -100 (every block below -40)."""
+    w = synth.LinearWorkload("range_bf16", 300, 136, 1031, "bf16", True, 128, "normal")
+    d = synth.make_linear_t(w, DEV)
+    h = d["h"].clone()
+    h[:64] = h[:64] * 256.0  # a power of two: exact in bf16
+    rlogp, rlse, rdH, rdW, rdb, z = _oracle_all(h, d["W"], d["b"], d["t"], d["g"])
+    assert _block_max_range(z[:64])[1] > 64.0  # the scaled tokens' blocks leave the range
+    lo2, hi2 = _block_max_range(z[64:])
+    assert -40.0 < lo2 and hi2 < 64.0, (lo2, hi2)  # the others stay inside it
+    for chunk in (128, 300):
+        L = llp()
+        logp, lse, dH, dW, db = L.linear_logp_fwd_bwd(h, d["W"], d["b"], d["t"], d["g"], True, True, True,
+                                                      chunk=chunk)
+        torch.cuda.synchronize()
+        assert_close(logp, rlogp, *TOL["bf16"]["logp"], f"logp chunk {chunk}")
+        assert_close(lse, rlse, *TOL["bf16"]["logp"], f"lse chunk {chunk}")
+        # large dynamic range (softmax rows of the scaled tokens are nearly one-hot,
+        # and their dW terms cancel between tokens): normalised error, as for the
+        # fused-vs-split comparison
+        for x, r, n in ((dH, rdH, "dH"), (dW, rdW, "dW"), (db, rdb, "db")):
+            e = norm_err(x, r)
+            assert e <= SPLIT_CLOSE["bf16"], f"{n} chunk {chunk}: normalised error {e:.2e}"
+        # the ordinary tokens' dH rows at the elementwise tolerance
+        assert_close(dH[64:], rdH[64:], *TOL["bf16"]["grad"], f"dH (unscaled tokens) chunk {chunk}")
+    # every logit near -100: every block lies below the range
+    b2 = (d["b"].float() - 100.0).to(torch.bfloat16)
+    rlogp, rlse, rdH, rdW, rdb, z = _oracle_all(d["h"], d["W"], b2, d["t"], d["g"])
+    assert _block_max_range(z)[1] < -40.0
+    logp, lse, dH, dW, db = fused(w, dict(d, b=b2))
+    assert_close(logp, rlogp, *TOL["bf16"]["logp"], "logp (logits near -100)")
+    for x, r, n in ((dH, rdH, "dH"), (dW, rdW, "dW"), (db, rdb, "db")):
+        assert_close(x, r, *TOL["bf16"]["grad"], f"{n} (logits near -100)")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_fused_masked_vocab_blocks(dt):
+    """A bias of -inf on vocabulary rows [512, V) masks whole 128-row blocks:
+    their probabilities are 0 (stored numerators +0) and every output stays
+    finite and matches the oracle; targets lie in the unmasked rows."""
+    w = synth.LinearWorkload(f"masked_{dt}", 300, 136, 1031, dt, True, 128, "normal")
+    d = synth.make_linear_t(w, DEV)
+    b = d["b"].clone()
+    b[512:] = float("-inf")
+    t = d["t"] % 512
+    rlogp, rlse, rdH, rdW, rdb, _ = _oracle_all(d["h"], d["W"], b, t, d["g"])
+    logp, lse, dH, dW, db = fused(w, dict(d, b=b, t=t))
+    for x in (logp, lse, dH, dW, db):
+        assert bool(torch.isfinite(x.float()).all())
+    tl, tg = TOL[dt]["logp"], TOL[dt]["grad"]
+    assert_close(logp, rlogp, *tl, "logp (masked)")
+    assert_close(dH, rdH, *tg, "dH (masked)")
+    assert_close(dW, rdW, *tg, "dW (masked)")
+    assert_close(db, rdb, *tg, "db (masked)")
+    assert bool((dW[512:] == 0).all()) and bool((db[512:] == 0).all())
