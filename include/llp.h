@@ -151,10 +151,16 @@ LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t 
  * contractions instead of four. This follows from g being fixed once the loss
  * reduction is fixed; the fused linear cross-entropy is measured as one
  * complete forward + backward training operation (Liger-Kernel PR #1324,
- * "Benchmark results", "Methodology").
+ * "Benchmark results", "Methodology"). With bf16 operands the numerators are
+ * exp(z) itself wherever a block's maximum lies in [-40, 64] (else as above),
+ * and each token's gradient factor is applied by the dH, dW and db steps.
+ * With an FP32 dW table and two or more chunks, dW is accumulated once per
+ * pair of consecutive chunks (the table is read and written once per pair);
+ * the workspace then holds two chunks' columns side by side.
  * logp and lse are bit-identical to linear_logp_fwd's. The gradients round
- * the softmax part twice (the stored numerator, then the gradient), so they
- * match linear_logp_bwd's to within that rounding, not bitwise.
+ * the softmax part twice (the stored numerator, then the gradient or, for
+ * bf16, the h row scaled by the token's factor), so they match
+ * linear_logp_bwd's to within that rounding, not bitwise.
  * With dH, dW and db all NULL this is linear_logp_fwd (and the workspace
  * query returns the forward's size). Deterministic.
  */
