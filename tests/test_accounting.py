@@ -51,3 +51,30 @@ def test_flop_counts():
     assert A.linear_fwd_bwd_flops(16384, 4096, 32000) == 4 * A.contraction_flops(16384, 32000, 4096)
     assert A.linear_model_flops(1, 1, 1) == 6
     assert A.logits_only_bytes(32768, 151936, 2) == 3 * 32768 * 151936 * 2
+
+
+def test_bench_per_launch_kind_flops():
+    """The bench's per-kind flop of the single call adds up to three N x V x D
+    contractions for every chunking and schedule, and splits as the schedule
+    says: with overlap only chunk 0's forward has a launch of its own; with
+    pairing the last launch holds the dW of the last pair (two chunks when K is
+    even, one when K is odd)."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+
+    D, V = 64, 1000
+    for N, C in ((16384, 2048), (300, 128), (300, 7), (4096, 512), (5, 5), (1000, 300)):
+        K = -(-N // C)
+        for overlap in (False, True):
+            for pairing in (False, True):
+                f = bench.fused_step_flops(N, D, V, C, K, overlap, pairing)
+                assert sum(f.values()) == 6 * N * V * D, (N, C, overlap, pairing)
+                last = min(C, N - (K - 1) * C)
+                if overlap:
+                    assert f["fwd_lse"] == 2 * min(C, N) * V * D
+                    if pairing and K >= 2:
+                        pair = last + (C if K % 2 == 0 else 0)
+                        assert f["dh_dw"] == 2 * last * V * D + 2 * pair * V * D
+                else:
+                    assert f["fwd_lse"] == 2 * N * V * D and f.get("dh_dw_fwd", 0) == 0
