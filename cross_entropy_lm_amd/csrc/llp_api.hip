@@ -239,8 +239,6 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   const int64_t fdw = pairing ? 1 : 0;
 
   float2* scales = reinterpret_cast<float2*>(at(workspace, bp.off_scales));
-  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, pairing ? 2 * bp.C : bp.C, pairing ? ceil_div(bp.K, 2) : bp.K,
-                                              dtype == LLP_F16 ? 15 : 0, scales, s));
   const float* lse_use = lse;
   float* lse_fused = nullptr;  // where the fused path writes lse
   if (fused) {
@@ -273,6 +271,20 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     Wt = nullptr;
     dS = nullptr;
   }
+  // Per-token mode of the single call (bf16 operands, the layout of the
+  // K-row-major dH whether or not dH is asked for, so that every subset of
+  // outputs computes alike): the forward stores 2^(z log2 e) for blocks in
+  // range, the combine forms each token's factor -(g / s) 2^(-lse log2 e), and
+  // the consumers apply it: the dH epilogue per row, the dW contraction through
+  // the h transpose scaled per token, db per token. No softmax-gradient pass;
+  // the preparation only rescales the columns of flagged tokens.
+  const bool qtok = fused && dtype == LLP_BF16 && dSt != nullptr && aligned16(W) && aligned16(dSt) && D % 8 == 0 &&
+                    V * D * e < lim && V * 2 * bp.ldSt * e < lim && dw_dma;
+  if (qtok && want_dH && !mn) return LLP_EINVAL;  // not reached: the conditions above imply the K-row-major dH
+  int32_t* const qflag = qtok ? reinterpret_cast<int32_t*>(at(workspace, bp.off_qflag)) : nullptr;
+  float* const cq = qtok ? reinterpret_cast<float*>(at(workspace, bp.off_cq)) : nullptr;
+  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, pairing ? 2 * bp.C : bp.C, pairing ? ceil_div(bp.K, 2) : bp.K,
+                                              dtype == LLP_F16 ? 15 : 0, scales, s));
   if (want_dH && !mn) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
   // Fused path with two numerator / partial buffers: chunk k + 1's forward
   // tiles run in the launch of chunk k's dH / dW (its fast epilogue only).
@@ -289,18 +301,6 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   auto hbuf = [&](int64_t k) -> void* {
     return pairing ? static_cast<char*>(ht) + (k & 1) * bp.ldSt * e : ht;
   };
-  // Per-token mode of the single call (bf16 operands, the layout of the
-  // K-row-major dH whether or not dH is asked for, so that every subset of
-  // outputs computes alike): the forward stores 2^(z log2 e) for blocks in
-  // range, the combine forms each token's factor -(g / s) 2^(-lse log2 e), and
-  // the consumers apply it: the dH epilogue per row, the dW contraction through
-  // the h transpose scaled per token, db per token. No softmax-gradient pass;
-  // the preparation only rescales the columns of flagged tokens.
-  const bool qtok = fused && dtype == LLP_BF16 && dSt != nullptr && aligned16(W) && aligned16(dSt) && D % 8 == 0 &&
-                    V * D * e < lim && V * 2 * bp.ldSt * e < lim && dw_dma;
-  if (qtok && want_dH && !mn) return LLP_EINVAL;  // not reached: the conditions above imply the K-row-major dH
-  int32_t* const qflag = qtok ? reinterpret_cast<int32_t*>(at(workspace, bp.off_qflag)) : nullptr;
-  float* const cq = qtok ? reinterpret_cast<float*>(at(workspace, bp.off_cq)) : nullptr;
   if (qtok) LLP_LAUNCH(LLP_K_SMALL, launch_zero(qflag, N, 4, s));
   // the forward tile problem and the combine of chunk kk (fused path)
   auto fwd_problem = [&](int64_t kk) {
