@@ -181,31 +181,35 @@ def kernel_table(tr, steps, step_flops):
     return kernels
 
 
-def fused_step_flops(N, D, V, C, K, overlap, pairing):
+def fused_step_flops(N, D, V, C, K, overlap, pairing, pair_dh=False):
     """Algorithmic flop per step of each contraction launch kind of the single
     call: chunk k's logits tile, dH and (its share of) dW each cost 2 C_k V D.
     With overlap, chunk k + 1's forward tiles ride in chunk k's dH / dW launch
     (dh_dw_fwd) and only chunk 0's forward has a launch of its own; with
     pairing, the dW of chunks (2j, 2j + 1) runs in the launch of chunk 2j + 1
-    (or of a last chunk without a partner)."""
+    (or of a last chunk without a partner); with pair_dh (small chunks) the dH
+    of a pair runs there too, and a launch left with neither dH nor dW is a
+    forward-only launch (fwd_lse)."""
     ck = [min(C, N - k * C) for k in range(K)]
     f = 2 * V * D
     out = {"fwd_lse": 0, "dh_dw": 0, "dh_dw_fwd": 0}
     for k in range(K):
-        if pairing:
-            dw = f * (ck[k - 1] + ck[k]) if k % 2 == 1 else (f * ck[k] if k == K - 1 else 0)
-        else:
-            dw = f * ck[k]
+        pair = ck[k - 1] + ck[k] if k % 2 == 1 else (ck[k] if k == K - 1 else 0)
+        dw = f * pair if pairing else f * ck[k]
+        dh = f * pair if pair_dh else f * ck[k]
         if overlap:
             if k == 0:
                 out["fwd_lse"] += f * ck[0]
             if k + 1 < K:
-                out["dh_dw_fwd"] += f * ck[k] + dw + f * ck[k + 1]
+                if dh == 0 and dw == 0:
+                    out["fwd_lse"] += f * ck[k + 1]
+                else:
+                    out["dh_dw_fwd"] += dh + dw + f * ck[k + 1]
             else:
-                out["dh_dw"] += f * ck[k] + dw
+                out["dh_dw"] += dh + dw
         else:
             out["fwd_lse"] += f * ck[k]
-            out["dh_dw"] += f * ck[k] + dw
+            out["dh_dw"] += dh + dw
     return out
 
 
@@ -257,10 +261,11 @@ def run_linear(w, args, torch, llp):
     # runs dW once per pair of chunks with an FP32 table (K >= 2)
     pairing = args.table == "f32" and K >= 2
     overlap = w.dtype in ("bf16", "f16") and pairing
+    pair_dh = overlap and C % 8 == 0 and -(-C // 256) * -(-D // 256) < 128
     for name, step, sf in (
             ("split", split_step, {"fwd_lse": 2 * N * V * D, "dlogits": 2 * N * V * D,
                                    "dh_dw": 4 * N * V * D}),
-            ("fused", fused_step, fused_step_flops(N, D, V, C, K, overlap, pairing))):
+            ("fused", fused_step, fused_step_flops(N, D, V, C, K, overlap, pairing, pair_dh))):
         log(f"{name}: warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
         ms, tr = time_steps(step, args, torch, llp, stream)
         kernels = kernel_table(tr, args.steps, sf)

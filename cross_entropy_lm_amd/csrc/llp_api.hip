@@ -302,6 +302,12 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     return pairing ? static_cast<char*>(ht) + (k & 1) * bp.ldSt * e : ht;
   };
   if (qtok) LLP_LAUNCH(LLP_K_SMALL, launch_zero(qflag, N, 4, s));
+  // With pairing and the K-row-major dH, a chunk whose dH grid is small (fewer
+  // than 128 tiles: small chunks) takes dH once per pair as well, over both
+  // chunks' columns (contiguous when C % 8 == 0): twice the tiles for the same
+  // contraction over the vocabulary. Every dH element still accumulates over
+  // V in the same order, so dH is bitwise the same either way.
+  const bool pair_dh = pairing && mn && bp.C % 8 == 0 && ceil_div(bp.C, kTile) * ceil_div(D, kTile) < 128;
   // the forward tile problem and the combine of chunk kk (fused path)
   auto fwd_problem = [&](int64_t kk) {
     const int64_t c0 = kk * bp.C;
@@ -420,18 +426,24 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, ldq, V, Ck, scales, sidx(k), head, next, targets, g, tcoef,
                               c0, v0, Vt, db, dW_dtype, s, qtok ? cq + c0 : nullptr));
     GemmProblem ph = {}, pw = {};
-    if (want_dH && mn) {
-      ph.A = dSt;
+    // this launch's dH: chunk k, or with pair_dh the pair (k - 1, k) at odd k
+    // (none at an even k that has a partner)
+    const bool dh_pair = pair_dh && (k & 1);
+    const bool do_dh = want_dH && (!pair_dh || (k & 1) || k == bp.K - 1);
+    const int64_t h0 = dh_pair ? c0 - bp.C : c0;  // first token of this dH
+    const int64_t hM = dh_pair ? bp.C + Ck : Ck;  // its tokens
+    if (do_dh && mn) {
+      ph.A = dh_pair ? qbuf(k - 1) : dSt;
       ph.B = W;
       ph.lda = ldq;
       ph.ldb = D;
-      ph.M = Ck;
+      ph.M = hM;
       ph.N = D;
       ph.K = V;
       ph.a_vec = ph.b_vec = 1;
       ph.mn = 1;
       ph.dma = 1;
-    } else if (want_dH) {
+    } else if (do_dh) {
       ph.A = dS;
       ph.B = Wt;
       ph.lda = bp.ldS;
@@ -442,16 +454,16 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       ph.a_vec = ph.b_vec = 1;
       ph.dma = dma_ok(ph, e, true);  // dS and W^T padding columns are written +0
     }
-    if (want_dH) {
-      ph.tiles_m = (int)ceil_div(Ck, kTile);
+    if (do_dh) {
+      ph.tiles_m = (int)ceil_div(hM, kTile);
       ph.tiles_n = (int)ceil_div(D, kTile);
       ph.epi = EPI_STORE;
-      ph.ep.out = static_cast<char*>(dH) + c0 * D * (dH_dtype == LLP_F32 ? 4 : e);
+      ph.ep.out = static_cast<char*>(dH) + h0 * D * (dH_dtype == LLP_F32 ? 4 : e);
       ph.ep.ldo = D;
       ph.ep.out_dt = dH_dtype;
       ph.ep.targets = targets;
       ph.ep.g = g;
-      ph.ep.tok0 = c0;
+      ph.ep.tok0 = h0;
       ph.ep.V = V;
       ph.ep.v0 = v0;
       ph.ep.Vt = Vt;
@@ -503,10 +515,13 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     if (overlap && k + 1 < bp.K) {
       // with the next chunk's forward tiles, then that chunk's combine
       const GemmProblem pf = fwd_problem(k + 1);
-      LLP_LAUNCH(LLP_K_DH_DW_FWD, launch_gemm3(dtype, ph, do_dw ? &pw : nullptr, pf, s));
+      if (do_dh)
+        LLP_LAUNCH(LLP_K_DH_DW_FWD, launch_gemm3(dtype, ph, do_dw ? &pw : nullptr, pf, s));
+      else  // pair_dh at an even chunk with a partner: no dH and (pairing) no dW in this launch
+        LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &pf, nullptr, s));
       LLP_LAUNCH(LLP_K_COMBINE, combine(k + 1));
-    } else if (want_dH || do_dw) {
-      LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, want_dH ? &ph : nullptr, do_dw ? &pw : nullptr, s));
+    } else if (do_dh || do_dw) {
+      LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, do_dh ? &ph : nullptr, do_dw ? &pw : nullptr, s));
     }
   }
   if (store_first && bp.K == fdw + 1 && dW_dtype == LLP_F32) {

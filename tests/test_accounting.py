@@ -66,10 +66,11 @@ def test_bench_per_launch_kind_flops():
     D, V = 64, 1000
     for N, C in ((16384, 2048), (300, 128), (300, 7), (4096, 512), (5, 5), (1000, 300)):
         K = -(-N // C)
-        for overlap in (False, True):
-            for pairing in (False, True):
-                f = bench.fused_step_flops(N, D, V, C, K, overlap, pairing)
-                assert sum(f.values()) == 6 * N * V * D, (N, C, overlap, pairing)
+        for overlap, pairing, pair_dh in ((False, False, False), (False, True, False), (True, False, False),
+                                          (True, True, False), (True, True, True), (False, True, True)):
+            f = bench.fused_step_flops(N, D, V, C, K, overlap, pairing, pair_dh)
+            assert sum(f.values()) == 6 * N * V * D, (N, C, overlap, pairing, pair_dh)
+            if not pair_dh:
                 last = min(C, N - (K - 1) * C)
                 if overlap:
                     assert f["fwd_lse"] == 2 * min(C, N) * V * D
@@ -78,3 +79,8 @@ def test_bench_per_launch_kind_flops():
                         assert f["dh_dw"] == 2 * last * V * D + 2 * pair * V * D
                 else:
                     assert f["fwd_lse"] == 2 * N * V * D and f.get("dh_dw_fwd", 0) == 0
+            elif overlap and K >= 3:
+                # pair dH: chunk 0's forward, and the even chunks' launches carry only
+                # the next (odd) chunk's forward
+                ck = [min(C, N - k * C) for k in range(K)]
+                assert f["fwd_lse"] == 2 * V * D * (ck[0] + sum(ck[j] for j in range(1, K, 2)))
