@@ -227,12 +227,17 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
 
   const int64_t lim = 0x7FFFFFF0LL;
   const bool tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < lim;
-  // Fused path with an FP32 table: one dW contraction per pair of chunks
+  // With an FP32 table (both paths): one dW contraction per pair of chunks
   // (2j, 2j + 1) over the columns of both, which sit side by side in the
   // vocab-major buffer [V][2 ldSt] and the h^T buffer [D][2 ldSt]: the table
   // is read and written once per pair. The pair shares one power-of-two scale
   // (scale index = pair index), so both halves of the contraction agree.
-  const bool pairing = fused && want_dW && tab_fast && bp.K >= 2 && bp.ldP == 2 * bp.ldSt;
+  // The two-call path has no forward tiles to fill the launches that carry no
+  // dW, so it pairs only small chunks (16-bit operands, C % 8 == 0, a dH grid
+  // of fewer than 128 tiles), whose dH is then paired too (see pair_dh).
+  // Shapes alone decide, so every subset of outputs accumulates dW alike.
+  const bool small_dh = e == 2 && bp.C % 8 == 0 && ceil_div(bp.C, kTile) * ceil_div(D, kTile) < 128;
+  const bool pairing = want_dW && tab_fast && bp.K >= 2 && bp.ldP == 2 * bp.ldSt && (fused || small_dh);
   const int64_t ldq = pairing ? bp.ldP : bp.ldSt;  // leading dimension of those buffers
   auto sidx = [&](int64_t k) { return (int)(pairing ? k >> 1 : k); };
   // the chunk whose launch carries the first dW contraction
@@ -307,7 +312,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   // chunks' columns (contiguous when C % 8 == 0): twice the tiles for the same
   // contraction over the vocabulary. Every dH element still accumulates over
   // V in the same order, so dH is bitwise the same either way.
-  const bool pair_dh = pairing && mn && bp.C % 8 == 0 && ceil_div(bp.C, kTile) * ceil_div(D, kTile) < 128;
+  const bool pair_dh = pairing && mn && small_dh;
   // the forward tile problem and the combine of chunk kk (fused path)
   auto fwd_problem = [&](int64_t kk) {
     const int64_t c0 = kk * bp.C;

@@ -99,9 +99,10 @@ inline int plan_fwd(int64_t N, int64_t D, int64_t V, int dtype, FwdPlan* p) {
 struct BwdPlan {
   int64_t C = 0, K = 0;                  // tokens per chunk, number of chunks
   int64_t ldWt = 0, ldS = 0, ldSt = 0;   // leading dimensions (elements), multiples of 8
-  // leading dimension of the vocab-major and h^T buffers: 2 ldSt in the fused
-  // layout with dW and K >= 2, whose buffers hold a pair of chunks (chunk 2j in
-  // the columns [0, C), chunk 2j + 1 from column ldSt), else ldSt
+  // leading dimension of the vocab-major and h^T buffers: 2 ldSt where dW is
+  // accumulated once per pair of chunks (dW, K >= 2; the two-call layout only
+  // for small chunks), whose buffers hold a pair (chunk 2j in the columns
+  // [0, C), chunk 2j + 1 from column ldSt), else ldSt
   int64_t ldP = 0;
   int64_t off_scales = -1;               // float2 [K]
   int64_t off_lse = -1;                  // float [N] when the caller gives no lse
@@ -143,7 +144,10 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   p->ldWt = round_up(V, 8);
   p->ldS = round_up(V, 8);
   p->ldSt = round_up(p->C, 8);
-  p->ldP = (fused && want_dW && p->K >= 2) ? 2 * p->ldSt : p->ldSt;
+  // (the two-call layout pairs only small chunks: 16-bit operands, C % 8 == 0
+  // and fewer than 128 tiles of 256 x 256 in a chunk's dH)
+  const bool small = esize(dtype) == 2 && p->C % 8 == 0 && ceil_div(p->C, kTile) * ceil_div(D, kTile) < 128;
+  p->ldP = (want_dW && p->K >= 2 && (fused || small)) ? 2 * p->ldSt : p->ldSt;
   Layout L;
   int64_t n;
   p->off_scales = L.add(p->K * 8);

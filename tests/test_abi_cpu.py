@@ -66,6 +66,13 @@ def test_workspace_queries():
     # chunk workspace: W^T, dlogits and dlogits^T in bf16 plus h^T of one chunk
     expect = 32000 * 4096 * 2 + 2048 * 32000 * 2 * 2 + 4096 * 2048 * 2
     assert expect <= full < expect + (1 << 20)
+    # small chunks (fewer than 128 dH tiles) pair dW: dlogits^T and h^T of two chunks
+    small = b(4096, 2048, 32768, BF16, 512, True, True, False, True)
+    expect_small = 32768 * 2048 * 2 + 512 * 32768 * 2 + 2 * 512 * 32768 * 2 + 2 * 2048 * 512 * 2
+    assert expect_small <= small < expect_small + (1 << 20)
+    # dH alone: W^T and the token-major dlogits of one chunk, no vocab-major buffer
+    expect_dh = 32000 * 4096 * 2 + 2048 * 32000 * 2
+    assert expect_dh <= only_dh < expect_dh + (1 << 20)
 
 
 @pytest.mark.parametrize("args,status", [
