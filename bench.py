@@ -132,6 +132,17 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -247,14 +258,33 @@ def run_linear(w, args, torch, llp):
 
     # correctness gate before timing (and the CPU baseline on the same sample), for both paths
     cpu = None
+    accuracy = {}
     for name, step in (("split", split_step), ("fused", fused_step)):
         step()
         torch.cuda.synchronize()
         if not args.no_gate or not args.no_cpu_baseline:
-            cpu = oracle_sample(w, args, logp, dH, cpu, name)
+            cpu, accuracy[name] = oracle_sample(w, args, logp, dH, dW, cpu, name)
 
-    flops = A.linear_fwd_bwd_flops(N, D, V)
-    model_flops = A.linear_model_flops(N, D, V)
+    # peak device memory of one single call above its inputs: the wrapper
+    # allocates the outputs and the workspace (the library allocates nothing)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    outs = llp.linear_logp_fwd_bwd(d["h"], d["W"], d["b"], d["t"], d["g"], True, True, w.bias, chunk=chunk,
+                                   dW_dtype=tdt)
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base
+    out_bytes = sum(x.numel() * x.element_size() for x in outs if x is not None)
+    del outs
+    memory = {"peak_extra_bytes": peak_extra, "workspace_bytes": ws_x.numel(), "output_bytes": out_bytes,
+              "what": "torch.cuda.max_memory_allocated above the inputs during one linear_logp_fwd_bwd "
+                      "call that allocates its outputs (logp, lse, dH, dW" + (", db" if w.bias else "") +
+                      ") and workspace; the library itself allocates nothing"}
+    log(f"peak extra memory {peak_extra / 2**20:.1f} MiB = workspace {ws_x.numel() / 2**20:.1f} MiB + "
+        f"outputs {out_bytes / 2**20:.1f} MiB")
+
+    flops8 = A.linear_fwd_bwd_flops(N, D, V)
+    exec_flops = {"fused": A.linear_model_flops(N, D, V), "split": flops8}
     peak = PEAK_TFLOPS[w.dtype]
     results = {}
     # the single call overlaps the next chunk's forward with 16-bit operands and
@@ -272,9 +302,14 @@ def run_linear(w, args, torch, llp):
         mfma = {k: v for k, v in kernels.items() if "tflops" in v}
         results[name] = {
             "ms_per_step": ms, "tokens_per_s": A.tokens_per_s(N, ms),
-            "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / (peak * 1e12),
-            "pct_mfma_peak_model_flops": 100.0 * model_flops / (ms * 1e-3) / (peak * 1e12),
+            # the flop this path executes: 3 contractions (single call) or 4 (split)
+            "executed_flop_per_step": exec_flops[name],
+            "pct_mfma_peak": 100.0 * exec_flops[name] / (ms * 1e-3) / (peak * 1e12),
             "dominant": max(mfma, key=lambda k: mfma[k]["ms_per_step"]), "kernels": kernels}
+        if name == "fused":
+            # not executed work: the four contractions of a forward + backward
+            # that recomputes the logits, over this path's time
+            results[name]["pct_mfma_peak_8vd_equivalent"] = 100.0 * flops8 / (ms * 1e-3) / (peak * 1e12)
     # same-box reference: the vendor GEMM (hipBLASLt through torch.matmul) on
     # the forward logits shape, logits written to HBM, no epilogue
     Wt_ = d["W"].t()
@@ -315,21 +350,27 @@ def run_linear(w, args, torch, llp):
                    "bias": w.bias, "g": w.g, "dW_table": args.table, "outputs": "logp,lse,dH,dW" +
                    (",db" if w.bias else ""), "path": PATHS[args.path]},
         "pct_mfma_peak": main["pct_mfma_peak"],
-        "pct_mfma_peak_model_flops": main["pct_mfma_peak_model_flops"],
+        "pct_mfma_peak_basis": f"{main['executed_flop_per_step']:.4e} flop executed per step "
+                               f"({'6' if args.path == 'fused' else '8'} V D per token)",
+        **({"pct_mfma_peak_8vd_equivalent": main["pct_mfma_peak_8vd_equivalent"]} if args.path == "fused" else {}),
+        "memory": memory,
+        **({"accuracy": accuracy[args.path]} if args.path in accuracy else {}),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_from_profiles(dom, w.name)},
         "kernels": main["kernels"],
         "gemm_reference": gemm_ref,
-        other: {"path": PATHS[other], **results[other]},
+        other: {"path": PATHS[other], **results[other],
+                **({"accuracy": accuracy[other]} if other in accuracy else {})},
         **({"cpu_baseline": {k: v for k, v in cpu.items() if not k.startswith("_")}}
            if cpu is not None and not args.no_cpu_baseline else {}),
     }
 
 
-def oracle_sample(w, args, logp, dH, prev=None, label=""):
+def oracle_sample(w, args, logp, dH, dW, prev=None, label=""):
     """FP64 oracle forward + backward (logp, dH, dW) on the first S tokens,
     timed on the host cores once; each path's logp and dH rows are gated
-    against it."""
+    against it, and the accuracy diagnostics of dH (and of dW when the sample
+    is the whole batch) are returned with the CPU baseline."""
     from oracle import linear_logp as O
 
     S = min(args.cpu_sample_tokens, w.N)
@@ -346,8 +387,9 @@ def oracle_sample(w, args, logp, dH, prev=None, label=""):
         prev = {"value": S / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
                 "sample": f"first {S} tokens of {w.name}: FP64 numpy oracle forward + backward (logp, dH, dW)"
                           f"{' + db' if w.bias else ''}, {dt:.2f} s",
-                "_ref": (rlogp, rdH)}
-    rlogp, rdH = prev["_ref"]
+                "cpu": cpu_model(), "nproc": os.cpu_count(),
+                "_ref": (rlogp, rdH, rdW if S == w.N else None)}
+    rlogp, rdH, rdW = prev["_ref"]
     gl = logp[:S].double().cpu().numpy()
     gh = dH[:S].double().cpu().numpy()
     tl = {"f32": (1e-5, 5e-4)}.get(w.dtype, (5e-3, 5e-2))
@@ -357,7 +399,17 @@ def oracle_sample(w, args, logp, dH, prev=None, label=""):
     if not args.no_gate and not (ok_l and ok_h):
         raise SystemExit(f"correctness gate failed ({label}): logp ok={ok_l} dH ok={ok_h}")
     log(f"gate ok ({label}: logp, dH on {S} tokens)")
-    return prev
+    acc = {"dH": synth.accuracy(gh, rdH, w.dtype)}
+    if rdW is not None:
+        acc["dW"] = synth.accuracy(dW.double().cpu().numpy(), rdW, torch_dtype_name(dW.dtype))
+    acc["reference"] = f"FP64 oracle on tokens [0, {S}), the upstream g the path receives"
+    log(f"accuracy ({label}): dH max err / max {acc['dH']['max_err_over_max']:.2e}, "
+        f"{acc['dH']['pct_correctly_rounded']:.4f}% correctly rounded")
+    return prev, acc
+
+
+def torch_dtype_name(dt) -> str:
+    return {"torch.float32": "f32", "torch.bfloat16": "bf16", "torch.float16": "f16"}[str(dt)]
 
 
 # ----------------------------------------------------------------------------- logits only
@@ -390,6 +442,9 @@ def run_logits(w, args, torch, llp):
     dt = time.perf_counter() - t0
     gl = logp[:S].double().cpu().numpy()
     gd = dl[:S].double().cpu().numpy()
+    acc = {"dlogits": synth.accuracy(gd, rd, w.dtype), "reference": f"FP64 oracle on rows [0, {S})"}
+    log(f"accuracy: dlogits max err / max {acc['dlogits']['max_err_over_max']:.2e}, "
+        f"{acc['dlogits']['pct_correctly_rounded']:.4f}% correctly rounded")
     if not args.no_gate:
         if not (np.all(np.abs(gl - rlogp) <= 5e-3 + 5e-2 * np.abs(rlogp))
                 and np.all(np.abs(gd - rd) <= 5e-4 + 2e-2 * np.abs(rd))):
@@ -426,8 +481,10 @@ def run_logits(w, args, torch, llp):
                      "unit": "GB/s", "frac": kernels[dom]["GBps"] / PEAK_HBM_GBS,
                      "traffic": traffic_from_profiles(dom, w.name)},
         "kernels": kernels,
+        "accuracy": acc,
         "cpu_baseline": {"value": S * V * 3 * 2 / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                         "sample": f"first {S} rows: FP64 numpy oracle logp + dlogits, {dt:.2f} s"},
+                         "sample": f"first {S} rows: FP64 numpy oracle logp + dlogits, {dt:.2f} s",
+                         "cpu": cpu_model(), "nproc": os.cpu_count()},
     }
     def copy_reference(dst):
         # same-box reference: a plain device copy of the same bytes (one read

@@ -1,7 +1,9 @@
 // C ABI entry points (declared in include/llp.h): validate, lay out the
 // caller's workspace, and enqueue the kernels on the caller's stream.
+#include <stdlib.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <vector>
 
 #include "../../include/llp.h"
@@ -74,6 +76,31 @@ hipError_t traced(int kind, hipStream_t s, F&& launch) {
   return e;
 }
 #define LLP_LAUNCH(kind, expr) LLP_TRY(traced((kind), s, [&]() { return (expr); }))
+
+// Opt-in device check (LLP_CHECK_DEVICE=1 in the environment, read on every
+// call): each non-null pointer must be device or managed memory of the
+// current device. Runs after the other argument checks and before any launch.
+int check_device(std::initializer_list<const void*> ptrs) {
+  const char* v = getenv("LLP_CHECK_DEVICE");
+  if (v == nullptr || v[0] != '1') return LLP_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LLP_EHIP;
+  for (const void* p : ptrs) {
+    if (p == nullptr) continue;
+    hipPointerAttribute_t a = {};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+      (void)hipGetLastError();  // an unknown (host) pointer: clear the error it leaves
+      return LLP_EINVAL;
+    }
+    if (!(a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) || a.device != dev) return LLP_EINVAL;
+  }
+  return LLP_OK;
+}
+#define LLP_CHECK_DEVICE(...)                        \
+  do {                                               \
+    const int st_ = check_device({__VA_ARGS__});     \
+    if (st_ != LLP_OK) return st_;                   \
+  } while (0)
 
 // Logits tile problem over tokens [tok0, tok0 + n) of h: A = W [V][D], B = h rows.
 GemmProblem logits_problem(int64_t tok0, int64_t n, int64_t D, int64_t V, int dtype,
@@ -165,6 +192,7 @@ int linear_logp_fwd(int64_t N, int64_t D, int64_t V, int dtype, const void* h, c
   if (N == 0) return LLP_OK;
   if (h == nullptr || W == nullptr || targets == nullptr || logp == nullptr) return LLP_EINVAL;
   if ((size_t)fp.bytes > workspace_bytes || (fp.bytes > 0 && workspace == nullptr)) return LLP_EWORKSPACE;
+  LLP_CHECK_DEVICE(h, W, b, targets, logp, lse, workspace);
   return run_forward(N, D, V, dtype, h, W, b, targets, logp, lse, workspace, fp,
                      static_cast<hipStream_t>(stream));
 }
@@ -209,6 +237,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     return LLP_EINVAL;
   if (fused && N > 0 && logp_out == nullptr) return LLP_EINVAL;
   if ((size_t)bp.bytes > workspace_bytes || (bp.bytes > 0 && workspace == nullptr)) return LLP_EWORKSPACE;
+  // the layouts without W^T read W and the workspace with 16-byte accesses
+  if (N > 0 && (bp.kmajor || bp.qtok) && !(aligned16(W) && aligned16(workspace))) return LLP_EINVAL;
+  LLP_CHECK_DEVICE(h, W, b, targets, g, lse, logp_out, lse_out, dH, dW, db, workspace);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t e = esize(dtype);
@@ -256,36 +287,28 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     if (st != LLP_OK) return st;
     lse_use = lse_ws;
   }
-  void* Wt = want_dH ? at(workspace, bp.off_Wt) : nullptr;
-  void* dS = want_dH ? at(workspace, bp.off_dS) : nullptr;
-  void* dSt = (want_dW || want_db || fused) ? at(workspace, bp.off_dSt) : nullptr;
+  // dH = dlogits W takes both operands as stored when the plan says so
+  // (kmajor): K (vocabulary) rows with the tile's rows contiguous, dlogits^T
+  // [V][ldq] and W [V][D] itself; then neither W^T nor the token-major
+  // dlogits copy exists. 16-bit operands on the DMA pipeline only.
+  const bool mn = bp.kmajor;
+  void* Wt = (want_dH && !mn) ? at(workspace, bp.off_Wt) : nullptr;
+  void* dS = (want_dH && !mn) ? at(workspace, bp.off_dS) : nullptr;
+  void* dSt = bp.off_dSt >= 0 ? at(workspace, bp.off_dSt) : nullptr;
   float2* part = fused ? reinterpret_cast<float2*>(at(workspace, bp.off_part)) : nullptr;
   float* zt = fused ? reinterpret_cast<float*>(at(workspace, bp.off_zt)) : nullptr;
   void* ht = want_dW ? at(workspace, bp.off_ht) : nullptr;
   float* tcoef = reinterpret_cast<float*>(at(workspace, bp.off_tcoef));
   int32_t* head = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_head)) : nullptr;
   int32_t* next = (want_dW || want_db) ? reinterpret_cast<int32_t*>(at(workspace, bp.off_next)) : nullptr;
-  // dH = dlogits W can take both operands as stored, K (vocabulary) rows with
-  // the tile's rows contiguous: dlogits^T [V][ldSt] and W [V][D] itself. Then
-  // neither W^T nor the token-major dlogits copy is formed. 16-bit operands on
-  // the DMA pipeline only; the vocab-major copy must be in the workspace.
-  const bool dw_dma = !want_dW || (aligned16(dSt) && aligned16(ht));
-  const bool mn = want_dH && e == 2 && dSt != nullptr && aligned16(W) && aligned16(dSt) && D % 8 == 0 &&
-                  V * D * e < lim && V * ldq * e < lim && dw_dma;
-  if (mn) {
-    Wt = nullptr;
-    dS = nullptr;
-  }
-  // Per-token mode of the single call (bf16 operands, the layout of the
-  // K-row-major dH whether or not dH is asked for, so that every subset of
+  // Per-token mode of the single call (bf16 operands, decided by the plan from
+  // the shapes alone, whether or not dH is asked for, so that every subset of
   // outputs computes alike): the forward stores 2^(z log2 e) for blocks in
   // range, the combine forms each token's factor -(g / s) 2^(-lse log2 e), and
   // the consumers apply it: the dH epilogue per row, the dW contraction through
   // the h transpose scaled per token, db per token. No softmax-gradient pass;
   // the preparation only rescales the columns of flagged tokens.
-  const bool qtok = fused && dtype == LLP_BF16 && dSt != nullptr && aligned16(W) && aligned16(dSt) && D % 8 == 0 &&
-                    V * D * e < lim && V * 2 * bp.ldSt * e < lim && dw_dma;
-  if (qtok && want_dH && !mn) return LLP_EINVAL;  // not reached: the conditions above imply the K-row-major dH
+  const bool qtok = bp.qtok;
   int32_t* const qflag = qtok ? reinterpret_cast<int32_t*>(at(workspace, bp.off_qflag)) : nullptr;
   float* const cq = qtok ? reinterpret_cast<float*>(at(workspace, bp.off_cq)) : nullptr;
   LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, pairing ? 2 * bp.C : bp.C, pairing ? ceil_div(bp.K, 2) : bp.K,
@@ -601,6 +624,7 @@ int linear_logp_shard_fwd(int64_t N, int64_t D, int64_t Vs, int64_t v0, int64_t 
     return LLP_EINVAL;
   if ((reinterpret_cast<uintptr_t>(zt_shard) & 3) != 0) return LLP_EINVAL;
   if ((size_t)fp.bytes > workspace_bytes || (fp.bytes > 0 && workspace == nullptr)) return LLP_EWORKSPACE;
+  LLP_CHECK_DEVICE(h, W, b, targets, lse_shard, zt_shard, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   float2* partials = reinterpret_cast<float2*>(at(workspace, fp.off_partials));
   // -inf marks "target not in this share"; the tile holding the target overwrites it
@@ -628,6 +652,7 @@ int linear_logp_shard_combine(int64_t N, int64_t P, const float* lse_shards, con
   if (N == 0) return LLP_OK;
   if (lse_shards == nullptr || zt_shards == nullptr || targets == nullptr || (logp == nullptr && lse == nullptr))
     return LLP_EINVAL;
+  LLP_CHECK_DEVICE(lse_shards, zt_shards, targets, logp, lse);
   hipStream_t s = static_cast<hipStream_t>(stream);
   LLP_LAUNCH(LLP_K_COMBINE, launch_shard_combine(lse_shards, zt_shards, P, N, targets, Vt, logp, lse, s));
   return LLP_OK;
@@ -650,6 +675,7 @@ int logp_fwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t*
   if (st != LLP_OK) return st;
   if (N == 0) return LLP_OK;
   if (logits == nullptr || targets == nullptr || logp == nullptr) return LLP_EINVAL;
+  LLP_CHECK_DEVICE(logits, targets, logp, lse);
   hipStream_t s = static_cast<hipStream_t>(stream);
   LLP_LAUNCH(LLP_K_ROWS_FWD, launch_rows_fwd(dtype, logits, N, V, targets, logp, lse, s));
   return LLP_OK;
@@ -661,6 +687,7 @@ int logp_bwd(int64_t N, int64_t V, int dtype, const void* logits, const int64_t*
   if (st != LLP_OK) return st;
   if (N == 0) return LLP_OK;
   if (logits == nullptr || targets == nullptr || g == nullptr || dlogits == nullptr) return LLP_EINVAL;
+  LLP_CHECK_DEVICE(logits, targets, g, lse, dlogits);
   hipStream_t s = static_cast<hipStream_t>(stream);
   LLP_LAUNCH(LLP_K_ROWS_BWD, launch_rows_bwd(dtype, logits, N, V, targets, g, lse, dlogits, s));
   return LLP_OK;

@@ -108,8 +108,16 @@ struct BwdPlan {
   int64_t off_lse = -1;                  // float [N] when the caller gives no lse
   FwdPlan fwd;                           // and the forward's workspace, placed after it
   int64_t off_fwd = -1;
-  int64_t off_Wt = -1;                   // W^T [D][ldWt]            (dH)
-  int64_t off_dS = -1;                   // dlogits [C][ldS]         (dH)
+  // dH reads its operands as stored (vocabulary rows: dlogits^T [V][ldq] and
+  // W [V][D]) when the shapes allow it: 16-bit operands, D % 8 == 0, and both
+  // operands spanning < 2 GiB. The layout then holds no W^T and no token-major
+  // dlogits; W and the workspace must be 16-byte aligned (else LLP_EINVAL).
+  bool kmajor = false;
+  // bf16 single call: per-token numerators (same shape conditions, whether or
+  // not dH is asked for, so that every subset of outputs computes alike)
+  bool qtok = false;
+  int64_t off_Wt = -1;                   // W^T [D][ldWt]            (dH, not kmajor)
+  int64_t off_dS = -1;                   // dlogits [C][ldS]         (dH, not kmajor)
   int64_t off_dSt = -1;                  // dlogits^T [V][ldP]       (dW or db)
   int64_t off_ht = -1;                   // h^T of one chunk (or pair) [D][ldP] (dW)
   int64_t off_tcoef = -1;                // float [N]: one-hot part g (1 - p_t) per token
@@ -148,6 +156,14 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   // and fewer than 128 tiles of 256 x 256 in a chunk's dH)
   const bool small = esize(dtype) == 2 && p->C % 8 == 0 && ceil_div(p->C, kTile) * ceil_div(D, kTile) < 128;
   p->ldP = (want_dW && p->K >= 2 && (fused || small)) ? 2 * p->ldSt : p->ldSt;
+  {
+    const int64_t lim = 0x7FFFFFF0LL;
+    int64_t vd, vq;
+    const bool shape = e == 2 && D % 8 == 0 && mul_ok(V, D, &vd) && mul_ok(vd, e, &vd) && vd < lim &&
+                       mul_ok(V, 2 * p->ldSt, &vq) && mul_ok(vq, e, &vq) && vq < lim;
+    p->kmajor = want_dH && shape;
+    p->qtok = fused && dtype == LLP_BF16 && shape;
+  }
   Layout L;
   int64_t n;
   p->off_scales = L.add(p->K * 8);
@@ -167,16 +183,16 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     p->off_qflag = L.add(N * 4);
     p->off_cq = L.add(N * 4);
   }
-  if (want_dH) {
+  if (want_dH && !p->kmajor) {
     if (!mul_ok(D, p->ldWt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_Wt = L.add(n);
     if (!mul_ok(p->C, p->ldS, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_dS = L.add(n);
   }
-  if (want_dW || want_db || fused) {
+  if (want_dW || want_db || fused || p->kmajor) {
     if (!mul_ok(V, p->ldP, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_dSt = L.add(n);
-    if (fused && e == 2 && want_dH && p->K >= 2) {
+    if (fused && p->kmajor && p->K >= 2) {
       p->off_dSt2 = L.add(n);
       if (!mul_ok(p->P, p->C, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
       p->off_part2 = L.add(n);

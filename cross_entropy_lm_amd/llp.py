@@ -97,16 +97,99 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream):
-    if stream is not None:
-        return stream
-    return _torch().cuda.current_stream().cuda_stream
-
-
 def _contig(t, name):
     if t is not None and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+# ----------------------------------------------------------------------------- argument checks
+# Everything the C ABI cannot see (a tensor's dtype, its shape beyond the sizes
+# passed, its device) is checked here before the library is called, so that a
+# mismatch raises instead of letting a kernel read or write past a buffer.
+# dtype and shape checks come first; the device check last.
+
+def _expect(t, name, shape, dtypes):
+    """t is None, or a contiguous tensor of one of `dtypes` and exactly `shape`."""
+    if t is None:
+        return
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        want = " or ".join(str(d) for d in dtypes)
+        raise TypeError(f"{name} must have dtype {want}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _contig(t, name)
+
+
+def _operands(h, W):
+    """(N, D, V, torch dtype) of h [N, D] and W [V, D] of one operand dtype."""
+    torch = _torch()
+    if not isinstance(h, torch.Tensor) or h.dim() != 2:
+        raise ValueError("h must be a 2-D tensor [N, D]")
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor [V, D]")
+    dtype_code(h.dtype)
+    N, D = h.shape
+    V = W.shape[0]
+    _expect(h, "h", (N, D), (h.dtype,))
+    _expect(W, "W", (V, D), (h.dtype,))
+    return N, D, V, h.dtype
+
+
+def _table_dtypes(op_dtype):
+    torch = _torch()
+    return (torch.float32,) if op_dtype == torch.float32 else (torch.float32, op_dtype)
+
+
+def _same_device(named):
+    """Every given tensor lives on one GPU; returns that device."""
+    devs = [(n, t.device) for n, t in named if t is not None]
+    for n, d in devs:
+        if d.type != "cuda":
+            raise ValueError(f"{n} must be a GPU tensor, got device {d}")
+    if len({d for _, d in devs}) > 1:
+        raise ValueError("tensors on different devices: " + ", ".join(f"{n}={d}" for n, d in devs))
+    return devs[0][1] if devs else None
+
+
+def _workspace_arg(workspace):
+    if workspace is not None:
+        torch = _torch()
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("workspace must be a torch.Tensor")
+        _contig(workspace, "workspace")
+    return workspace
+
+
+class _OnStream:
+    """Allocations made inside run on the caller's stream (the caching
+    allocator then reuses a freed workspace only for later work on that
+    stream); with no stream given, torch's current stream is used."""
+
+    def __init__(self, stream, device):
+        torch = _torch()
+        self.ctx = None
+        if stream is None:
+            self.ptr = torch.cuda.current_stream(device).cuda_stream if device is not None else 0
+        elif isinstance(stream, torch.cuda.Stream):
+            self.ptr = stream.cuda_stream
+            self.ctx = torch.cuda.stream(stream)
+        else:
+            self.ptr = int(stream)
+            self.ctx = torch.cuda.stream(torch.cuda.ExternalStream(self.ptr, device=device))
+
+    def __enter__(self):
+        if self.ctx is not None:
+            self.ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            return self.ctx.__exit__(*exc)
+        return False
 
 
 def llp_version() -> int:
@@ -147,23 +230,62 @@ def _workspace(nbytes, workspace, device):
     return _torch().empty(max(nbytes, 1), dtype=_torch().uint8, device=device)
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _check_tables(V, D, op_dtype, dW_dtype, dW, db):
+    """dW [V, D] and db [V] (each optional) share one dtype, float32 or the
+    operand dtype; returns that dtype."""
+    torch = _torch()
+    ok = _table_dtypes(op_dtype)
+    tdt = torch.float32 if dW_dtype is None else dW_dtype
+    if tdt not in ok:
+        raise TypeError(f"dW_dtype must be float32 or the operand dtype {op_dtype}, got {tdt}")
+    _expect(dW, "dW", (V, D), ok)
+    _expect(db, "db", (V,), ok)
+    if dW is not None and db is not None and dW.dtype != db.dtype:
+        raise TypeError(f"dW and db must share one dtype, got {dW.dtype} and {db.dtype}")
+    if dW is not None:
+        tdt = dW.dtype
+    elif db is not None:
+        tdt = db.dtype
+    return tdt
+
+
+def _grad_tables(V, D, op_dtype, dW_dtype, dW, db, accumulate, want_dW, want_db, device):
+    """The dW / db tables to pass (allocated when requested and not given) and
+    their common dtype (checked by _check_tables first)."""
+    torch = _torch()
+    tdt = _check_tables(V, D, op_dtype, dW_dtype, dW, db)
+    if want_dW and dW is None:
+        dW = (torch.zeros if accumulate else torch.empty)((V, D), dtype=tdt, device=device)
+    if want_db and db is None:
+        db = (torch.zeros if accumulate else torch.empty)((V,), dtype=tdt, device=device)
+    return dW, db, tdt
+
+
 def linear_logp_fwd(h, W, b, targets, logp=None, lse=None, workspace=None, stream=None,
                     want_lse=True):
     """logp [N] (and lse [N]) for h [N, D], W [V, D], b [V] or None, targets [N] int64."""
     torch = _torch()
-    for t, n in ((h, "h"), (W, "W"), (b, "b"), (targets, "targets")):
-        _contig(t, n)
-    N, D = h.shape
-    V = W.shape[0]
-    dt = dtype_code(h.dtype)
-    if logp is None:
-        logp = torch.empty(N, dtype=torch.float32, device=h.device)
-    if lse is None and want_lse:
-        lse = torch.empty(N, dtype=torch.float32, device=h.device)
-    nbytes = linear_logp_fwd_workspace_size(N, D, V, dt)
-    ws = _workspace(nbytes, workspace, h.device)
-    st = lib().linear_logp_fwd(N, D, V, dt, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(logp),
-                               _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    N, D, V, odt = _operands(h, W)
+    _expect(b, "b", (V,), (odt,))
+    _expect(targets, "targets", (N,), (torch.int64,))
+    _expect(logp, "logp", (N,), (torch.float32,))
+    _expect(lse, "lse", (N,), (torch.float32,))
+    _workspace_arg(workspace)
+    dev = _same_device([("h", h), ("W", W), ("b", b), ("targets", targets), ("logp", logp), ("lse", lse),
+                        ("workspace", workspace)])
+    dt = dtype_code(odt)
+    with _OnStream(stream, dev) as st_:
+        if logp is None:
+            logp = torch.empty(N, dtype=torch.float32, device=dev)
+        if lse is None and want_lse:
+            lse = torch.empty(N, dtype=torch.float32, device=dev)
+        ws = _workspace(linear_logp_fwd_workspace_size(N, D, V, dt), workspace, dev)
+        st = lib().linear_logp_fwd(N, D, V, dt, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(logp),
+                                   _ptr(lse), _ptr(ws), _nbytes(ws), st_.ptr)
     _check(st, "linear_logp_fwd")
     return logp, lse
 
@@ -177,29 +299,29 @@ def linear_logp_bwd(h, W, b, targets, g, lse=None, want_dH=True, want_dW=True, w
     operand dtype). With ``accumulate`` the caller's dW/db are added into.
     """
     torch = _torch()
-    for t, n in ((h, "h"), (W, "W"), (b, "b"), (targets, "targets"), (g, "g"), (lse, "lse")):
-        _contig(t, n)
-    N, D = h.shape
-    V = W.shape[0]
-    dt = dtype_code(h.dtype)
-    tdt = torch.float32 if dW_dtype is None else dW_dtype
-    if want_dH and dH is None:
-        dH = torch.empty((N, D), dtype=h.dtype, device=h.device)
-    if want_dW and dW is None:
-        dW = (torch.zeros if accumulate else torch.empty)((V, D), dtype=tdt, device=h.device)
-    if want_db and db is None:
-        db = (torch.zeros if accumulate else torch.empty)((V,), dtype=tdt, device=h.device)
-    if dW is not None:
-        tdt = dW.dtype
-    elif db is not None:
-        tdt = db.dtype
-    nbytes = linear_logp_bwd_workspace_size(N, D, V, dt, chunk, dH is not None, dW is not None,
-                                            db is not None, lse is not None)
-    ws = _workspace(nbytes, workspace, h.device)
-    st = lib().linear_logp_bwd(N, D, V, dt, chunk, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(g),
-                               _ptr(lse), _ptr(dH), _ptr(dW), dtype_code(tdt), _ptr(db),
-                               int(bool(accumulate)), _ptr(ws), ws.numel() * ws.element_size(),
-                               _stream(stream))
+    N, D, V, odt = _operands(h, W)
+    _expect(b, "b", (V,), (odt,))
+    _expect(targets, "targets", (N,), (torch.int64,))
+    _expect(g, "g", (N,), (torch.float32,))
+    _expect(lse, "lse", (N,), (torch.float32,))
+    _expect(dH, "dH", (N, D), (odt,))
+    _workspace_arg(workspace)
+    if (want_db or db is not None) and b is None:
+        raise ValueError("db needs a bias b")
+    _check_tables(V, D, odt, dW_dtype, dW, db)
+    dev = _same_device([("h", h), ("W", W), ("b", b), ("targets", targets), ("g", g), ("lse", lse),
+                        ("dH", dH), ("dW", dW), ("db", db), ("workspace", workspace)])
+    dt = dtype_code(odt)
+    with _OnStream(stream, dev) as st_:
+        dW, db, tdt = _grad_tables(V, D, odt, dW_dtype, dW, db, accumulate, want_dW, want_db, dev)
+        if want_dH and dH is None:
+            dH = torch.empty((N, D), dtype=odt, device=dev)
+        nbytes = linear_logp_bwd_workspace_size(N, D, V, dt, chunk, dH is not None, dW is not None,
+                                                db is not None, lse is not None)
+        ws = _workspace(nbytes, workspace, dev)
+        st = lib().linear_logp_bwd(N, D, V, dt, chunk, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(g),
+                                   _ptr(lse), _ptr(dH), _ptr(dW), dtype_code(tdt), _ptr(db),
+                                   int(bool(accumulate)), _ptr(ws), _nbytes(ws), st_.ptr)
     _check(st, "linear_logp_bwd")
     return dH, dW, db
 
@@ -218,33 +340,34 @@ def linear_logp_fwd_bwd(h, W, b, targets, g, want_dH=True, want_dW=True, want_db
                         db=None, workspace=None, stream=None):
     """(logp, lse, dH, dW, db) in one call, for an upstream g known before the forward."""
     torch = _torch()
-    for t, n in ((h, "h"), (W, "W"), (b, "b"), (targets, "targets"), (g, "g")):
-        _contig(t, n)
-    N, D = h.shape
-    V = W.shape[0]
-    dt = dtype_code(h.dtype)
-    tdt = torch.float32 if dW_dtype is None else dW_dtype
-    if logp is None:
-        logp = torch.empty(N, dtype=torch.float32, device=h.device)
-    if lse is None and want_lse:
-        lse = torch.empty(N, dtype=torch.float32, device=h.device)
-    if want_dH and dH is None:
-        dH = torch.empty((N, D), dtype=h.dtype, device=h.device)
-    if want_dW and dW is None:
-        dW = (torch.zeros if accumulate else torch.empty)((V, D), dtype=tdt, device=h.device)
-    if want_db and db is None:
-        db = (torch.zeros if accumulate else torch.empty)((V,), dtype=tdt, device=h.device)
-    if dW is not None:
-        tdt = dW.dtype
-    elif db is not None:
-        tdt = db.dtype
-    nbytes = linear_logp_fwd_bwd_workspace_size(N, D, V, dt, chunk, dH is not None, dW is not None,
-                                                db is not None, lse is not None)
-    ws = _workspace(nbytes, workspace, h.device)
-    st = lib().linear_logp_fwd_bwd(N, D, V, dt, chunk, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(g),
-                                   _ptr(logp), _ptr(lse), _ptr(dH), _ptr(dW), dtype_code(tdt), _ptr(db),
-                                   int(bool(accumulate)), _ptr(ws), ws.numel() * ws.element_size(),
-                                   _stream(stream))
+    N, D, V, odt = _operands(h, W)
+    _expect(b, "b", (V,), (odt,))
+    _expect(targets, "targets", (N,), (torch.int64,))
+    _expect(g, "g", (N,), (torch.float32,))
+    _expect(logp, "logp", (N,), (torch.float32,))
+    _expect(lse, "lse", (N,), (torch.float32,))
+    _expect(dH, "dH", (N, D), (odt,))
+    _workspace_arg(workspace)
+    if (want_db or db is not None) and b is None:
+        raise ValueError("db needs a bias b")
+    _check_tables(V, D, odt, dW_dtype, dW, db)
+    dev = _same_device([("h", h), ("W", W), ("b", b), ("targets", targets), ("g", g), ("logp", logp),
+                        ("lse", lse), ("dH", dH), ("dW", dW), ("db", db), ("workspace", workspace)])
+    dt = dtype_code(odt)
+    with _OnStream(stream, dev) as st_:
+        dW, db, tdt = _grad_tables(V, D, odt, dW_dtype, dW, db, accumulate, want_dW, want_db, dev)
+        if logp is None:
+            logp = torch.empty(N, dtype=torch.float32, device=dev)
+        if lse is None and want_lse:
+            lse = torch.empty(N, dtype=torch.float32, device=dev)
+        if want_dH and dH is None:
+            dH = torch.empty((N, D), dtype=odt, device=dev)
+        nbytes = linear_logp_fwd_bwd_workspace_size(N, D, V, dt, chunk, dH is not None, dW is not None,
+                                                    db is not None, lse is not None)
+        ws = _workspace(nbytes, workspace, dev)
+        st = lib().linear_logp_fwd_bwd(N, D, V, dt, chunk, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(g),
+                                       _ptr(logp), _ptr(lse), _ptr(dH), _ptr(dW), dtype_code(tdt), _ptr(db),
+                                       int(bool(accumulate)), _ptr(ws), _nbytes(ws), st_.ptr)
     _check(st, "linear_logp_fwd_bwd")
     return logp, lse, dH, dW, db
 
@@ -254,20 +377,24 @@ def linear_logp_shard_fwd(h, W_shard, b_shard, targets, v0, Vt, lse_shard=None, 
     """(lse_shard [N], zt_shard [N]) of the vocabulary share W_shard = rows [v0, v0 + Vs) of a
     Vt-row vocabulary; zt_shard is -inf where the share does not hold the target."""
     torch = _torch()
-    for t, n in ((h, "h"), (W_shard, "W_shard"), (b_shard, "b_shard"), (targets, "targets")):
-        _contig(t, n)
-    N, D = h.shape
-    Vs = W_shard.shape[0]
-    dt = dtype_code(h.dtype)
-    if lse_shard is None:
-        lse_shard = torch.empty(N, dtype=torch.float32, device=h.device)
-    if zt_shard is None:
-        zt_shard = torch.empty(N, dtype=torch.float32, device=h.device)
-    nbytes = linear_logp_fwd_workspace_size(N, D, Vs, dt)
-    ws = _workspace(nbytes, workspace, h.device)
-    st = lib().linear_logp_shard_fwd(N, D, Vs, v0, Vt, dt, _ptr(h), _ptr(W_shard), _ptr(b_shard),
-                                     _ptr(targets), _ptr(lse_shard), _ptr(zt_shard), _ptr(ws),
-                                     ws.numel() * ws.element_size(), _stream(stream))
+    N, D, Vs, odt = _operands(h, W_shard)
+    _expect(b_shard, "b_shard", (Vs,), (odt,))
+    _expect(targets, "targets", (N,), (torch.int64,))
+    _expect(lse_shard, "lse_shard", (N,), (torch.float32,))
+    _expect(zt_shard, "zt_shard", (N,), (torch.float32,))
+    _workspace_arg(workspace)
+    dev = _same_device([("h", h), ("W_shard", W_shard), ("b_shard", b_shard), ("targets", targets),
+                        ("lse_shard", lse_shard), ("zt_shard", zt_shard), ("workspace", workspace)])
+    dt = dtype_code(odt)
+    with _OnStream(stream, dev) as st_:
+        if lse_shard is None:
+            lse_shard = torch.empty(N, dtype=torch.float32, device=dev)
+        if zt_shard is None:
+            zt_shard = torch.empty(N, dtype=torch.float32, device=dev)
+        ws = _workspace(linear_logp_fwd_workspace_size(N, D, Vs, dt), workspace, dev)
+        st = lib().linear_logp_shard_fwd(N, D, Vs, v0, Vt, dt, _ptr(h), _ptr(W_shard), _ptr(b_shard),
+                                         _ptr(targets), _ptr(lse_shard), _ptr(zt_shard), _ptr(ws), _nbytes(ws),
+                                         st_.ptr)
     _check(st, "linear_logp_shard_fwd")
     return lse_shard, zt_shard
 
@@ -276,18 +403,25 @@ def linear_logp_shard_combine(lse_shards, zt_shards, targets, Vt, logp=None, lse
                               stream=None):
     """(logp [N], lse [N]) from the shares' [P, N] lse and target-logit rows."""
     torch = _torch()
-    for t, n in ((lse_shards, "lse_shards"), (zt_shards, "zt_shards"), (targets, "targets")):
-        _contig(t, n)
+    if not isinstance(lse_shards, torch.Tensor) or lse_shards.dim() != 2:
+        raise ValueError("lse_shards must be a 2-D tensor [P, N]")
     P, N = lse_shards.shape
-    if tuple(zt_shards.shape) != (P, N):
-        raise ValueError("zt_shards must have the shape of lse_shards")
-    dev = lse_shards.device
-    if logp is None:
-        logp = torch.empty(N, dtype=torch.float32, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty(N, dtype=torch.float32, device=dev)
-    st = lib().linear_logp_shard_combine(N, P, _ptr(lse_shards), _ptr(zt_shards), _ptr(targets), Vt,
-                                         _ptr(logp), _ptr(lse), _stream(stream))
+    _expect(lse_shards, "lse_shards", (P, N), (torch.float32,))
+    _expect(zt_shards, "zt_shards", (P, N), (torch.float32,))
+    if zt_shards is None:
+        raise ValueError("zt_shards is required")
+    _expect(targets, "targets", (N,), (torch.int64,))
+    _expect(logp, "logp", (N,), (torch.float32,))
+    _expect(lse, "lse", (N,), (torch.float32,))
+    dev = _same_device([("lse_shards", lse_shards), ("zt_shards", zt_shards), ("targets", targets),
+                        ("logp", logp), ("lse", lse)])
+    with _OnStream(stream, dev) as st_:
+        if logp is None:
+            logp = torch.empty(N, dtype=torch.float32, device=dev)
+        if lse is None and want_lse:
+            lse = torch.empty(N, dtype=torch.float32, device=dev)
+        st = lib().linear_logp_shard_combine(N, P, _ptr(lse_shards), _ptr(zt_shards), _ptr(targets), Vt,
+                                             _ptr(logp), _ptr(lse), st_.ptr)
     _check(st, "linear_logp_shard_combine")
     return logp, lse
 
@@ -298,59 +432,83 @@ def linear_logp_shard_bwd(h, W_shard, b_shard, targets, g, lse, v0, Vt, want_dH=
     """(dH partial [N, D], dW_shard [Vs, D], db_shard [Vs]) of one vocabulary share, given the
     global lse. ``dH_dtype`` is float32 by default (the partials are summed by the caller)."""
     torch = _torch()
-    for t, n in ((h, "h"), (W_shard, "W_shard"), (b_shard, "b_shard"), (targets, "targets"), (g, "g"),
-                 (lse, "lse")):
-        _contig(t, n)
-    N, D = h.shape
-    Vs = W_shard.shape[0]
-    dt = dtype_code(h.dtype)
-    tdt = torch.float32 if dW_dtype is None else dW_dtype
+    N, D, Vs, odt = _operands(h, W_shard)
+    _expect(b_shard, "b_shard", (Vs,), (odt,))
+    _expect(targets, "targets", (N,), (torch.int64,))
+    _expect(g, "g", (N,), (torch.float32,))
+    _expect(lse, "lse", (N,), (torch.float32,))
+    if lse is None:
+        raise ValueError("lse (the merged lse of every share) is required")
     hdt = torch.float32 if dH_dtype is None else dH_dtype
-    if want_dH and dH is None:
-        dH = torch.empty((N, D), dtype=hdt, device=h.device)
+    if hdt not in _table_dtypes(odt):
+        raise TypeError(f"dH_dtype must be float32 or the operand dtype {odt}, got {hdt}")
+    _expect(dH, "dH", (N, D), _table_dtypes(odt))
     if dH is not None:
         hdt = dH.dtype
-    if want_dW and dW is None:
-        dW = (torch.zeros if accumulate else torch.empty)((Vs, D), dtype=tdt, device=h.device)
-    if want_db and db is None:
-        db = (torch.zeros if accumulate else torch.empty)((Vs,), dtype=tdt, device=h.device)
-    if dW is not None:
-        tdt = dW.dtype
-    elif db is not None:
-        tdt = db.dtype
-    nbytes = linear_logp_bwd_workspace_size(N, D, Vs, dt, chunk, dH is not None, dW is not None,
-                                            db is not None, True)
-    ws = _workspace(nbytes, workspace, h.device)
-    st = lib().linear_logp_shard_bwd(N, D, Vs, v0, Vt, dt, chunk, _ptr(h), _ptr(W_shard), _ptr(b_shard),
-                                     _ptr(targets), _ptr(g), _ptr(lse), _ptr(dH), dtype_code(hdt), _ptr(dW),
-                                     dtype_code(tdt), _ptr(db), int(bool(accumulate)), _ptr(ws),
-                                     ws.numel() * ws.element_size(), _stream(stream))
+    _workspace_arg(workspace)
+    if (want_db or db is not None) and b_shard is None:
+        raise ValueError("db needs a bias b_shard")
+    _check_tables(Vs, D, odt, dW_dtype, dW, db)
+    dev = _same_device([("h", h), ("W_shard", W_shard), ("b_shard", b_shard), ("targets", targets), ("g", g),
+                        ("lse", lse), ("dH", dH), ("dW", dW), ("db", db), ("workspace", workspace)])
+    dt = dtype_code(odt)
+    with _OnStream(stream, dev) as st_:
+        dW, db, tdt = _grad_tables(Vs, D, odt, dW_dtype, dW, db, accumulate, want_dW, want_db, dev)
+        if want_dH and dH is None:
+            dH = torch.empty((N, D), dtype=hdt, device=dev)
+        nbytes = linear_logp_bwd_workspace_size(N, D, Vs, dt, chunk, dH is not None, dW is not None,
+                                                db is not None, True)
+        ws = _workspace(nbytes, workspace, dev)
+        st = lib().linear_logp_shard_bwd(N, D, Vs, v0, Vt, dt, chunk, _ptr(h), _ptr(W_shard), _ptr(b_shard),
+                                         _ptr(targets), _ptr(g), _ptr(lse), _ptr(dH), dtype_code(hdt), _ptr(dW),
+                                         dtype_code(tdt), _ptr(db), int(bool(accumulate)), _ptr(ws), _nbytes(ws),
+                                         st_.ptr)
     _check(st, "linear_logp_shard_bwd")
     return dH, dW, db
 
 
-def logp_fwd(logits, targets, logp=None, lse=None, want_lse=True, stream=None):
+def _logits_arg(logits):
     torch = _torch()
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError("logits must be a 2-D tensor [N, V]")
+    dtype_code(logits.dtype)
     _contig(logits, "logits")
-    N, V = logits.shape
-    if logp is None:
-        logp = torch.empty(N, dtype=torch.float32, device=logits.device)
-    if lse is None and want_lse:
-        lse = torch.empty(N, dtype=torch.float32, device=logits.device)
-    st = lib().logp_fwd(N, V, dtype_code(logits.dtype), _ptr(logits), _ptr(targets), _ptr(logp),
-                        _ptr(lse), _stream(stream))
+    return logits.shape
+
+
+def logp_fwd(logits, targets, logp=None, lse=None, want_lse=True, stream=None):
+    """Logits-only forward: logp [N] (and lse [N]) from logits [N, V]."""
+    torch = _torch()
+    N, V = _logits_arg(logits)
+    _expect(targets, "targets", (N,), (torch.int64,))
+    _expect(logp, "logp", (N,), (torch.float32,))
+    _expect(lse, "lse", (N,), (torch.float32,))
+    dev = _same_device([("logits", logits), ("targets", targets), ("logp", logp), ("lse", lse)])
+    with _OnStream(stream, dev) as st_:
+        if logp is None:
+            logp = torch.empty(N, dtype=torch.float32, device=dev)
+        if lse is None and want_lse:
+            lse = torch.empty(N, dtype=torch.float32, device=dev)
+        st = lib().logp_fwd(N, V, dtype_code(logits.dtype), _ptr(logits), _ptr(targets), _ptr(logp),
+                            _ptr(lse), st_.ptr)
     _check(st, "logp_fwd")
     return logp, lse
 
 
 def logp_bwd(logits, targets, g, lse=None, dlogits=None, stream=None):
+    """Logits-only backward: dlogits [N, V] (the logits' dtype; may be the logits tensor itself)."""
     torch = _torch()
-    _contig(logits, "logits")
-    N, V = logits.shape
-    if dlogits is None:
-        dlogits = torch.empty_like(logits)
-    st = lib().logp_bwd(N, V, dtype_code(logits.dtype), _ptr(logits), _ptr(targets), _ptr(g),
-                        _ptr(lse), _ptr(dlogits), _stream(stream))
+    N, V = _logits_arg(logits)
+    _expect(targets, "targets", (N,), (torch.int64,))
+    _expect(g, "g", (N,), (torch.float32,))
+    _expect(lse, "lse", (N,), (torch.float32,))
+    _expect(dlogits, "dlogits", (N, V), (logits.dtype,))
+    dev = _same_device([("logits", logits), ("targets", targets), ("g", g), ("lse", lse), ("dlogits", dlogits)])
+    with _OnStream(stream, dev) as st_:
+        if dlogits is None:
+            dlogits = torch.empty_like(logits)
+        st = lib().logp_bwd(N, V, dtype_code(logits.dtype), _ptr(logits), _ptr(targets), _ptr(g),
+                            _ptr(lse), _ptr(dlogits), st_.ptr)
     _check(st, "logp_bwd")
     return dlogits
 

@@ -46,6 +46,11 @@
  * - Sizes are int64 everywhere; element offsets are computed in 64 bits
  *   (N * V may exceed 2^31; RL-Kernel PR #495 review of the INT_MAX loop
  *   counters).
+ * - Device check (opt-in): with the environment variable LLP_CHECK_DEVICE=1,
+ *   every call first asks HIP where each non-NULL pointer argument lives and
+ *   returns LLP_EINVAL (enqueuing nothing) unless it is device or managed
+ *   memory of the current device (the device-guard lesson of RL-Kernel PR
+ *   #495's review). Off by default: it costs a few microseconds per call.
  */
 #ifndef LLP_H
 #define LLP_H
@@ -88,15 +93,26 @@ LLP_API int64_t linear_logp_chunk_rows(int64_t N, int64_t V, int64_t chunk);
 LLP_API int64_t linear_logp_num_chunks(int64_t N, int64_t V, int64_t chunk);
 
 /*
- * Workspace bytes linear_logp_fwd needs for these shapes (0 for N = 0).
- * Returns a status; *bytes is written on LLP_OK.
+ * Workspace bytes linear_logp_fwd needs for these shapes (0 for N = 0): the
+ * per-token partial maxima and exp-sums of each 128-row vocabulary block and
+ * the target logits, which replace the [N, V] logits the pages' fused paths
+ * never keep (RL-Kernel PR #495, "Summary"; Liger-Kernel PR #1324,
+ * "Summary"). Returns a status; *bytes is written on LLP_OK. Errors as
+ * linear_logp_fwd's shape errors.
  */
 LLP_API int linear_logp_fwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, size_t* bytes);
 
 /*
- * Forward. h [N, D], W [V, D], b [V] or NULL, targets [N]  ->  logp [N]
- * (required) and lse [N] (NULL to skip). lse is the residual the backward
- * consumes. N = 0 enqueues nothing. D >= 1, V >= 1.
+ * Forward (RL-Kernel issue #261, "Current production path": linear_logp over
+ * hidden states, weight, optional bias and targets; RL-Kernel PR #495,
+ * "Summary": the row's max and sum of exponentials give lse, the target
+ * logit minus lse gives logp). h [N, D], W [V, D] (a linear layer's weight),
+ * b [V] or NULL, targets [N] int64  ->  logp [N] (required) and lse [N] (NULL
+ * to skip), float32. lse is the residual the backward consumes. N = 0
+ * enqueues nothing. Errors: LLP_EINVAL for N < 0, D < 1, V < 1, a bad dtype or
+ * a NULL h / W / targets / logp (N > 0); LLP_EOVERFLOW when N, V, N D or V D
+ * exceed the supported ranges; LLP_EWORKSPACE for a workspace below the
+ * query's size. h, W and b are read only; logp and lse are written once.
  */
 LLP_API int linear_logp_fwd(int64_t N, int64_t D, int64_t V, int dtype,
                     const void* h, const void* W, const void* b, const int64_t* targets,
@@ -106,7 +122,14 @@ LLP_API int linear_logp_fwd(int64_t N, int64_t D, int64_t V, int dtype,
 /*
  * Workspace bytes linear_logp_bwd needs. It depends on which outputs are
  * requested (want_* nonzero) and on whether the caller passes lse
- * (have_lse nonzero); unrequested outputs add nothing.
+ * (have_lse nonzero); unrequested outputs add nothing (RL-Kernel issue #261,
+ * "Correctness boundary": no allocation that the requested outputs do not
+ * need). It holds one chunk's (or, where dW is accumulated per pair of
+ * chunks, two chunks') softmax part in the operand dtype (the chunk
+ * workspace of RL-Kernel issue #261, "Static traffic model"), the chunk's h
+ * transposed, and per-token scalars. With 16-bit operands and D % 8 == 0 (V D
+ * and 2 V round8(C) elements each below 2^30) dH reads W as stored and no
+ * transposed copy of W is held.
  */
 LLP_API int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
                                    int want_dH, int want_dW, int want_db, int have_lse,
@@ -129,6 +152,9 @@ LLP_API int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int 
  *   values (gradient accumulation across calls).
  * NULL outputs are never read or written. N = 0 writes only the zero fill of
  * dW/db (when accumulate = 0).
+ * Alignment: with 16-bit operands and D % 8 == 0 (the layout without a W
+ * transpose, see the workspace query) W and the workspace must be 16-byte
+ * aligned, else LLP_EINVAL (nothing is enqueued).
  * Deterministic: the same inputs give bit-identical outputs on every call.
  */
 LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
@@ -161,6 +187,8 @@ LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t 
  * the softmax part twice (the stored numerator, then the gradient or, for
  * bf16, the h row scaled by the token's factor), so they match
  * linear_logp_bwd's to within that rounding, not bitwise.
+ * Alignment: as linear_logp_bwd; with bf16 operands and D % 8 == 0 W and the
+ * workspace must be 16-byte aligned even when dH is not requested.
  * With dH, dW and db all NULL this is linear_logp_fwd (and the workspace
  * query returns the forward's size). Deterministic.
  */

@@ -156,11 +156,25 @@ def linear_logp_token_rows(h_rows, W, b, t_rows, g_rows):
     return logp, lse, dS @ _as64(W) + 0.0
 
 
-def linear_logp_vocab_rows(h, W, b, t, g, vrows, token_block=1024):
+def linear_lse(h, W, b, token_block=1024):
+    """lse [N] of every token (``row_logsumexp`` of its logits), evaluated
+    token block by token block so that the [N, V] logits are never held."""
+    h = _as64(h)
+    W = _as64(W)
+    bb = None if b is None else _as64(b)
+    out = np.zeros(h.shape[0], F64)
+    for n0 in range(0, h.shape[0], token_block):
+        n1 = min(h.shape[0], n0 + token_block)
+        out[n0:n1] = row_logsumexp(logits(h[n0:n1], W, bb))
+    return out
+
+
+def linear_logp_vocab_rows(h, W, b, t, g, vrows, token_block=1024, lse=None):
     """dW[v, :] and db[v] for a subset of vocabulary rows ``vrows``.
 
     These need every token's lse, which is evaluated token block by token
-    block (each token's lse is independent of the others); the sum over
+    block (each token's lse is independent of the others), or taken from
+    ``lse`` (the ``linear_lse`` of the same h, W, b) when given; the sum over
     tokens then runs over all N in increasing token order per block and
     block order, as a plain sum.
     """
@@ -174,14 +188,35 @@ def linear_logp_vocab_rows(h, W, b, t, g, vrows, token_block=1024):
     dW = np.zeros((vrows.size, D), F64)
     db = np.zeros(vrows.size, F64)
     bb = None if b is None else _as64(b)
+    # the sampled rows' logits and, when lse is given, only those: the
+    # softmax gradient of a column needs its token's lse and its own logit
+    Wv = W[vrows]
+    bv = None if bb is None else bb[vrows]
     for n0 in range(0, N, token_block):
         n1 = min(N, n0 + token_block)
-        z = logits(h[n0:n1], W, bb)
-        lse = row_logsumexp(z)
-        dS = softmax_grad(z, lse, t[n0:n1], g[n0:n1])[:, vrows]
+        if lse is None:
+            z = logits(h[n0:n1], W, bb)
+            lse_b = row_logsumexp(z)
+            dS = softmax_grad(z, lse_b, t[n0:n1], g[n0:n1])[:, vrows]
+        else:
+            dS = _softmax_grad_columns(logits(h[n0:n1], Wv, bv), _as64(lse)[n0:n1], t[n0:n1], g[n0:n1], vrows, V)
         dW += dS.T @ h[n0:n1]
         db += dS.sum(axis=0)
     return dW + 0.0, db + 0.0
+
+
+def _softmax_grad_columns(zc, lse, t, g, vrows, V):
+    """Columns ``vrows`` of ``softmax_grad``: the same two products
+    g [v == t] - g exp(z - lse), with +0 rows for an out-of-range target or
+    g == 0, evaluated on the sampled columns' logits ``zc`` only."""
+    g = _as64(g)
+    t = np.asarray(t, dtype=np.int64)
+    ok = valid_targets(t, V) & (g != 0)
+    p = np.exp(_as64(zc) - lse[:, None])
+    onehot = (t[:, None] == vrows[None, :]).astype(F64) * ok[:, None]
+    d = g[:, None] * onehot - g[:, None] * p
+    d[~ok] = 0.0
+    return d + 0.0
 
 
 # ----------------------------------------------------------------------------- logits-only op

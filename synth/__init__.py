@@ -177,6 +177,37 @@ def quantize_np(x32: np.ndarray, dtype: str):
     raise ValueError(dtype)
 
 
+# significant bits and smallest quantum (subnormal spacing) of each dtype
+_PREC = {"bf16": (8, -133), "f16": (11, -24), "f32": (24, -149)}
+
+
+def round_f64_np(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to the nearest value of ``dtype`` (ties to even),
+    returned as float64: the "correctly rounded" reference of a result stored
+    in that dtype. One rounding, straight from float64 (no double rounding via
+    fp32). Values beyond the dtype's finite range are not handled (the
+    gradients compared here are far inside it)."""
+    x = np.asarray(x, dtype=np.float64)
+    bits, qmin = _PREC[dtype]
+    _, e = np.frexp(x)  # |x| = m 2^e with m in [0.5, 1)
+    q = np.ldexp(1.0, np.maximum(e - bits, qmin))
+    return np.round(x / q) * q  # x / q is exact (a power-of-two scaling); np.round ties to even
+
+
+def accuracy(got: np.ndarray, ref: np.ndarray, dtype: str) -> dict:
+    """Diagnostics of a low-precision result against a float64 reference:
+    max |err| / max |ref| and the fraction of elements equal to the correctly
+    rounded reference (the two figures RL-Kernel PR #495 prints per
+    implementation, "Prior art & reuse decision")."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    m = float(np.abs(ref).max()) if ref.size else 0.0
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    cr = float(np.mean(got == round_f64_np(ref, dtype))) if ref.size else 1.0
+    return {"max_err": err, "max_ref": m, "max_err_over_max": err / m if m > 0 else err,
+            "pct_correctly_rounded": 100.0 * cr, "elements": int(ref.size), "dtype": dtype}
+
+
 # ----------------------------------------------------------------------------- torch path
 def _torch():
     import torch

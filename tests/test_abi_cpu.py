@@ -62,17 +62,34 @@ def test_workspace_queries():
     only_dh = b(16384, 4096, 32000, BF16, 2048, True, False, False, True)
     only_dw = b(16384, 4096, 32000, BF16, 2048, False, True, False, True)
     no_lse = b(16384, 4096, 32000, BF16, 2048, True, True, False, False)
-    assert only_dh < full and only_dw < full and no_lse > full
-    # chunk workspace: W^T, dlogits and dlogits^T in bf16 plus h^T of one chunk
-    expect = 32000 * 4096 * 2 + 2048 * 32000 * 2 * 2 + 4096 * 2048 * 2
+    assert only_dh < full and only_dw <= full and no_lse > full
+    # 16-bit operands with D % 8 == 0: dH reads dlogits^T and W as stored, so
+    # the chunk workspace is dlogits^T plus h^T of one chunk (no W^T, no
+    # token-major dlogits: nothing the requested outputs do not need)
+    expect = 2048 * 32000 * 2 + 4096 * 2048 * 2
     assert expect <= full < expect + (1 << 20)
     # small chunks (fewer than 128 dH tiles) pair dW: dlogits^T and h^T of two chunks
     small = b(4096, 2048, 32768, BF16, 512, True, True, False, True)
-    expect_small = 32768 * 2048 * 2 + 512 * 32768 * 2 + 2 * 512 * 32768 * 2 + 2 * 2048 * 512 * 2
+    expect_small = 2 * 512 * 32768 * 2 + 2 * 2048 * 512 * 2
     assert expect_small <= small < expect_small + (1 << 20)
-    # dH alone: W^T and the token-major dlogits of one chunk, no vocab-major buffer
-    expect_dh = 32000 * 4096 * 2 + 2048 * 32000 * 2
+    # dH alone: the vocab-major dlogits of one chunk
+    expect_dh = 2048 * 32000 * 2
     assert expect_dh <= only_dh < expect_dh + (1 << 20)
+    # fp32 operands (and D % 8 != 0) keep the transposed path: W^T, both
+    # dlogits layouts and h^T
+    f32 = b(4096, 1024, 8192, F32, 512, True, True, False, True)
+    expect_f32 = 1024 * 8192 * 4 + 512 * 8192 * 4 * 2 + 1024 * 512 * 4
+    assert expect_f32 <= f32 < expect_f32 + (1 << 20)
+    odd = b(4096, 1020, 8192, BF16, 512, True, False, False, True)
+    expect_odd = 1020 * 8192 * 2 + 512 * 8192 * 2
+    assert expect_odd <= odd < expect_odd + (1 << 20)
+    # the single call at 16384 x 4096 x 32000, bf16, chunk 2048, FP32 table:
+    # two pair buffers of numerators [V][2 x 2048], h^T of a pair, two chunks'
+    # forward partials and per-token arrays (about 540 MiB)
+    fq = llp.linear_logp_fwd_bwd_workspace_size
+    single = fq(16384, 4096, 32000, BF16, 2048, True, True, False, True)
+    expect_single = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 250 * 2048 * 8
+    assert expect_single <= single < expect_single + (1 << 20)
 
 
 @pytest.mark.parametrize("args,status", [
@@ -133,6 +150,11 @@ def test_bwd_argument_errors():
     assert _bwd(nbytes=need - 1) == llp.LLP_EWORKSPACE
     assert _bwd(ws=None, nbytes=need) == llp.LLP_EWORKSPACE
     assert _bwd(N=1 << 31) == llp.LLP_EOVERFLOW
+    # 16-bit operands with D % 8 == 0 read W and the workspace with 16-byte
+    # accesses: a misaligned pointer is rejected before any launch
+    assert _bwd(dt=BF16, W=FAKE + 2) == E
+    assert _bwd(dt=F16, ws=FAKE + 8) == E
+    assert _bwd(dt=BF16, W=FAKE + 2, dH=None, dW=None, db=None) == llp.LLP_OK  # nothing requested
 
 
 def _fused(N=256, D=128, V=1024, dt=F32, chunk=64, h=FAKE, W=FAKE, b=FAKE, t=FAKE, g=FAKE, logp=FAKE,
@@ -157,6 +179,9 @@ def test_fused_argument_errors_and_workspace():
     assert _fused(nbytes=need - 1) == llp.LLP_EWORKSPACE
     assert _fused(ws=None, nbytes=need) == llp.LLP_EWORKSPACE
     assert _fused(N=1 << 31) == llp.LLP_EOVERFLOW
+    assert _fused(dt=BF16, W=FAKE + 2) == E
+    assert _fused(dt=BF16, W=FAKE + 2, dH=None) == E   # bf16 per-token numerators read W as stored too
+    assert _fused(dt=F16, ws=FAKE + 4) == E
     # the fused layout adds the chunk's forward partials and target logits, and
     # always holds the vocab-major buffer; without lse it also holds one
     bq = llp.linear_logp_bwd_workspace_size

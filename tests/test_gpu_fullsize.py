@@ -1,7 +1,8 @@
 """Parity at the workloads' full sizes, in the launch configuration the
 benchmark times, on outputs the FP64 oracle computes one by one: sampled
-tokens (logp, lse, dH) and sampled vocabulary rows (dW, db, which need every
-token's lse), plus properties that hold at any size (bitwise chunk
+tokens (at least 64, both sides of every chunk boundary: logp, lse, dH) and
+sampled vocabulary rows (at least 64: dW, db, which need every token's lse),
+plus properties that hold at any size (bitwise chunk
 invariance of logp / dH, exact power-of-two upstream scaling, requested-output
 subsets equal to the full run, zero workspace beyond the outputs for the
 logits-only op)."""
@@ -12,7 +13,7 @@ import pytest
 import synth
 from oracle import linear_logp as O
 
-from gpu_common import TOL, assert_close, bits_equal, norm_err, say, torch_dtype
+from gpu_common import TOL, HostCase, assert_close, bits_equal, norm_err, sample_tokens, sample_vocab, say, torch_dtype
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -24,25 +25,6 @@ def llp():
     from cross_entropy_lm_amd import llp as m
 
     return m
-
-
-def sample_tokens(N, C):
-    s = {0, 1, N - 1, N // 2, C - 1, min(C, N - 1), min(2 * C - 1, N - 1), N - 2}
-    rng = np.random.default_rng(N)
-    s |= set(int(x) for x in rng.integers(0, N, 6))
-    return np.array(sorted(x for x in s if 0 <= x < N))
-
-
-def sample_vocab(V, t_host):
-    rng = np.random.default_rng(V)
-    s = {0, V - 1, V // 2}
-    s |= set(int(x) for x in t_host[:4])  # rows that take one-hot terms
-    s |= set(int(x) for x in rng.integers(0, V, 6))
-    # a row that is the target of two or more tokens, if there is one
-    vals, cnt = np.unique(t_host, return_counts=True)
-    if (cnt > 1).any():
-        s.add(int(vals[np.argmax(cnt)]))
-    return np.array(sorted(s))
 
 
 def run_linear(w, tdt=None, chunk=None, want=(True, True, True), g=None):
@@ -59,26 +41,6 @@ def run_linear(w, tdt=None, chunk=None, want=(True, True, True), g=None):
     return d, logp, lse, dH, dW, db
 
 
-class HostCase:
-    """Host copies of a workload for the oracle (W is shared by all samples)."""
-
-    def __init__(self, w):
-        say(f"host inputs for {w.name}")
-        self.w = w
-        self.full = synth.make_linear_np(w)
-
-    def tokens(self, rows, g64=None):
-        f = self.full
-        g = f["g64"][rows] if g64 is None else g64[rows]
-        b64 = f["b64"]
-        return O.linear_logp_token_rows(f["h64"][rows], f["W64"], b64, f["t"][rows], g)
-
-    def vocab(self, vrows, g64=None, tok=slice(None)):
-        f = self.full
-        g = f["g64"] if g64 is None else g64
-        return O.linear_logp_vocab_rows(f["h64"][tok], f["W64"], f["b64"], f["t"][tok], g[tok], vrows)
-
-
 def check_linear(w, host, logp, lse, dH, dW, db, tok, vr, g64=None, tdt_budget=None, label=""):
     dt = w.dtype
     tl, tg = TOL[dt]["logp"], TOL[dt]["grad"]
@@ -87,7 +49,9 @@ def check_linear(w, host, logp, lse, dH, dW, db, tok, vr, g64=None, tdt_budget=N
     assert_close(lse[tok], rs, *tl, f"{label} lse")
     if dH is not None:
         assert_close(dH[tok], rh, *tg, f"{label} dH")
-        say(f"{label} dH normalised error {norm_err(dH[tok], rh):.2e}")
+        acc = synth.accuracy(dH[tok].double().cpu().numpy(), rh, dt)
+        say(f"{label} dH max err / max {acc['max_err_over_max']:.2e}, "
+            f"{acc['pct_correctly_rounded']:.4f}% correctly rounded ({acc['elements']} elements)")
     if dW is not None or db is not None:
         rw, rb = host.vocab(vr, g64)
         if dW is not None:
@@ -231,10 +195,13 @@ def test_logits_only_full_size():
     dl2 = L.logp_bwd(d["logits"], d["t"], d["g"], None)
     torch.cuda.synchronize()
     assert bits_equal(dl, dl2)
-    rows = np.array(sorted({0, 1, w.N - 1, w.N // 2} | set(int(x) for x in np.random.default_rng(4).integers(0, w.N, 12))))
+    rows = sample_tokens(w.N, 4096, 64)
     host = synth.make_logits_rows_np(w, rows)
     rlogp, rlse = O.logp_fwd(host["logits64"], host["t"])
     rd = O.logp_bwd(host["logits64"], host["t"], host["g64"])
     assert_close(logp[rows], rlogp, *TOL["bf16"]["logp"], "logp")
     assert_close(lse[rows], rlse, *TOL["bf16"]["logp"], "lse")
     assert_close(dl[rows], rd, *TOL["bf16"]["grad"], "dlogits")
+    acc = synth.accuracy(dl[rows].double().cpu().numpy(), rd, "bf16")
+    say(f"logits-only dlogits max err / max {acc['max_err_over_max']:.2e}, "
+        f"{acc['pct_correctly_rounded']:.4f}% correctly rounded ({acc['elements']} elements)")

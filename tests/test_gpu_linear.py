@@ -8,7 +8,7 @@ import pytest
 import synth
 from oracle import linear_logp as O
 
-from gpu_common import TOL, assert_close, bits_equal, say, torch_dtype
+from gpu_common import TOL, assert_close, bits_equal, chunk_rounding_budget, say, torch_dtype
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -72,27 +72,6 @@ def test_linear_matches_oracle(w):
     assert_close(dW, rdW, *tg, "dW")
     if w.bias:
         assert_close(db, rdb, *tg, "db")
-
-
-def chunk_rounding_budget(w, host, esize_bits):
-    """Bound on the extra error of an operand-dtype table: after each chunk the
-    running table is rounded to the operand dtype, which moves it by at most
-    2^-p |running value| (p = 8 for bf16, 11 for fp16). The running values are
-    the oracle's partial sums over the chunks' tokens."""
-    run_w = np.zeros((w.V, w.D))
-    run_b = np.zeros(w.V)
-    bw = np.zeros((w.V, w.D))
-    bb = np.zeros(w.V)
-    for c0 in range(0, w.N, w.chunk):
-        c1 = min(w.N, c0 + w.chunk)
-        _, dw, db = O.linear_logp_bwd(host["h64"][c0:c1], host["W64"], host["b64"], host["t"][c0:c1],
-                                      host["g64"][c0:c1], False, True, w.bias)
-        run_w += dw
-        bw += np.abs(run_w) * 2.0 ** -esize_bits
-        if w.bias:
-            run_b += db
-            bb += np.abs(run_b) * 2.0 ** -esize_bits
-    return bw, bb
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])

@@ -265,6 +265,21 @@ def test_sampled_helpers_equal_the_full_definition():
     dw, dbb = O.linear_logp_vocab_rows(h, W, b, t, g, vr, token_block=8)
     np.testing.assert_allclose(dw, dW[vr], atol=1e-13)
     np.testing.assert_allclose(dbb, db[vr], atol=1e-13)
+    # with every token's lse passed in (blocked evaluation), the same rows;
+    # out-of-range targets and g = 0 rows keep their +0 columns there too
+    ls_all = O.linear_lse(h, W, b, token_block=5)
+    np.testing.assert_allclose(ls_all, lse, atol=1e-14)
+    t2 = t.copy()
+    t2[[1, 4]] = [-100, 29]
+    g2 = g.copy()
+    g2[7] = 0.0
+    vr2 = np.array([0, int(t[3]), 13, 28])
+    _, dW2, db2 = O.linear_logp_bwd(h, W, b, t2, g2, False, True, True)
+    dw, dbb = O.linear_logp_vocab_rows(h, W, b, t2, g2, vr2, token_block=8, lse=ls_all)
+    np.testing.assert_allclose(dw, dW2[vr2], atol=1e-13)
+    np.testing.assert_allclose(dbb, db2[vr2], atol=1e-13)
+    dw0, _ = O.linear_logp_vocab_rows(h, W, b, t2, np.zeros_like(g2), vr2, lse=ls_all)
+    assert np.all(dw0 == 0) and not np.signbit(dw0).any()
 
 
 def test_logits_only_equals_linear_on_the_same_logits():

@@ -45,3 +45,26 @@ def test_value_recipe():
     bits = synth.f32_to_bf16_bits(np.array([1.0, 1.00390625, 1.01171875, -2.5], np.float32))
     # 1 + 2^-8 is a tie -> rounds to even (1.0); 1 + 3*2^-8 is a tie -> rounds up to 1 + 2^-6
     np.testing.assert_array_equal(synth.bf16_bits_to_f32(bits), [1.0, 1.0, 1.015625, -2.5])
+
+
+def test_correct_rounding_reference():
+    """round_f64_np is one round-to-nearest-even from float64: it equals numpy's
+    own double -> half and double -> float conversions, and for bf16 it picks
+    the nearer bf16 neighbour (ties to the even bit pattern)."""
+    import numpy as np
+
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(100000) * np.exp(rng.uniform(-30, 30, 100000))
+    small = np.abs(x) < 60000
+    assert np.array_equal(synth.round_f64_np(x[small], "f16"), x[small].astype(np.float16).astype(np.float64))
+    assert np.array_equal(synth.round_f64_np(x, "f32"), x.astype(np.float32).astype(np.float64))
+    r = synth.round_f64_np(x, "bf16")
+    u = synth.f32_to_bf16_bits(r.astype(np.float32)).astype(np.int32)
+    assert np.array_equal(synth.bf16_bits_to_f32(u.astype(np.uint16)).astype(np.float64), r)
+    for nb in (u + 1, u - 1):
+        v = synth.bf16_bits_to_f32(nb.astype(np.uint16)).astype(np.float64)
+        assert np.all(np.abs(x - r) <= np.abs(x - v))
+    # exact ties go to the even significand: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    assert synth.round_f64_np(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8]), "bf16").tolist() == [1.0, 1 + 2.0 ** -6]
+    acc = synth.accuracy(r, x, "bf16")
+    assert acc["pct_correctly_rounded"] == 100.0 and acc["max_err_over_max"] <= 2.0 ** -8
