@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 #include <vector>
 
 #include "../../include/llp.h"
@@ -147,6 +148,35 @@ int run_forward(int64_t N, int64_t D, int64_t V, int dtype, const void* h, const
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------- forward without allocation
+// Scratch of linear_logp_fwd_noalloc: the forward's per-block partials and
+// target logits, in a device-global array instead of a caller's workspace
+// (every device the library runs on holds its own copy until the process
+// ends). Host code never uses the array's name as an address: the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[LLP_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with that device current).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LLP_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return LLP_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LLP_OK;
+}
+}  // namespace
 }  // namespace llp
 
 using namespace llp;
@@ -195,6 +225,23 @@ int linear_logp_fwd(int64_t N, int64_t D, int64_t V, int dtype, const void* h, c
   LLP_CHECK_DEVICE(h, W, b, targets, logp, lse, workspace);
   return run_forward(N, D, V, dtype, h, W, b, targets, logp, lse, workspace, fp,
                      static_cast<hipStream_t>(stream));
+}
+
+int linear_logp_fwd_noalloc(int64_t N, int64_t D, int64_t V, int dtype, const void* h, const void* W,
+                            const void* b, const int64_t* targets, float* logp, float* lse, void* stream) {
+  FwdPlan fp;
+  int st = plan_fwd(N, D, V, dtype, &fp);
+  if (st != LLP_OK) return st;
+  if (N == 0) return LLP_OK;
+  if (h == nullptr || W == nullptr || targets == nullptr || logp == nullptr) return LLP_EINVAL;
+  if ((size_t)fp.bytes > (size_t)LLP_SCRATCH_BYTES) return LLP_EWORKSPACE;
+  LLP_CHECK_DEVICE(h, W, b, targets, logp, lse);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != LLP_OK) return st;
+  // every partial and every valid target's logit is written before it is
+  // read, so nothing left by an earlier call needs clearing
+  return run_forward(N, D, V, dtype, h, W, b, targets, logp, lse, ws, fp, static_cast<hipStream_t>(stream));
 }
 
 int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,

@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libllp.so")
 
 LLP_F32, LLP_BF16, LLP_F16 = 0, 1, 2
+LLP_SCRATCH_BYTES = 64 << 20  # the device-global scratch of linear_logp_fwd_noalloc
 LLP_OK, LLP_EINVAL, LLP_EWORKSPACE, LLP_EOVERFLOW, LLP_EHIP = 0, 1, 2, 3, 4
 
 _lib = None
@@ -30,6 +31,7 @@ SIGNATURES = {
     "linear_logp_num_chunks": (_i64, [_i64, _i64, _i64]),
     "linear_logp_fwd_workspace_size": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_sz)]),
     "linear_logp_fwd": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "linear_logp_fwd_noalloc": (_int, [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "linear_logp_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int, _i64, _int, _int, _int, _int,
                                               ctypes.POINTER(_sz)]),
     "linear_logp_bwd": (_int, [_i64, _i64, _i64, _int, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -287,6 +289,27 @@ def linear_logp_fwd(h, W, b, targets, logp=None, lse=None, workspace=None, strea
         st = lib().linear_logp_fwd(N, D, V, dt, _ptr(h), _ptr(W), _ptr(b), _ptr(targets), _ptr(logp),
                                    _ptr(lse), _ptr(ws), _nbytes(ws), st_.ptr)
     _check(st, "linear_logp_fwd")
+    return logp, lse
+
+
+def linear_logp_fwd_noalloc(h, W, b, targets, logp, lse=None, stream=None):
+    """linear_logp_fwd into the caller's logp [N] (and lse [N] or None) with the
+    library's device-global scratch instead of a workspace: nothing is
+    allocated, here or in the library. Calls that overlap on one device race
+    on that scratch."""
+    torch = _torch()
+    N, D, V, odt = _operands(h, W)
+    _expect(b, "b", (V,), (odt,))
+    _expect(targets, "targets", (N,), (torch.int64,))
+    if logp is None:
+        raise ValueError("logp is required (this call allocates nothing)")
+    _expect(logp, "logp", (N,), (torch.float32,))
+    _expect(lse, "lse", (N,), (torch.float32,))
+    dev = _same_device([("h", h), ("W", W), ("b", b), ("targets", targets), ("logp", logp), ("lse", lse)])
+    ptr = _OnStream(stream, dev).ptr
+    st = lib().linear_logp_fwd_noalloc(N, D, V, dtype_code(odt), _ptr(h), _ptr(W), _ptr(b), _ptr(targets),
+                                       _ptr(logp), _ptr(lse), ptr)
+    _check(st, "linear_logp_fwd_noalloc")
     return logp, lse
 
 

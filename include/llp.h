@@ -30,8 +30,8 @@
  *   `workspace`, sized by the matching *_workspace_size query.
  * - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the null
  *   stream) and the call returns without waiting for it. The library keeps no
- *   mutable global state; calls on different streams must not share output
- *   or workspace buffers.
+ *   mutable global state (except the scratch of linear_logp_fwd_noalloc);
+ *   calls on different streams must not share output or workspace buffers.
  * - dtypes: operands h, W, b, logits, dH and dlogits use `dtype` (LLP_F32,
  *   LLP_BF16 or LLP_F16). logp, lse and g are float32. Targets are int64.
  *   Arithmetic accumulates in float32; 16-bit results are rounded to nearest
@@ -118,6 +118,28 @@ LLP_API int linear_logp_fwd(int64_t N, int64_t D, int64_t V, int dtype,
                     const void* h, const void* W, const void* b, const int64_t* targets,
                     float* logp, float* lse,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward without allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): linear_logp_fwd with the same arguments except the workspace,
+ * which is replaced by a device-global scratch array of LLP_SCRATCH_BYTES
+ * built into the library (one per device, held until the process ends; its
+ * device address is looked up on the first call on each device). The call
+ * allocates nothing and calls no allocating routine. Results are bitwise
+ * those of linear_logp_fwd. Shapes whose forward workspace
+ * (linear_logp_fwd_workspace_size) exceeds LLP_SCRATCH_BYTES return
+ * LLP_EWORKSPACE, enqueuing nothing: about N * ceil(V / 256) * 16 bytes, so
+ * N <= 33487 tokens at V = 32000 and N <= 7058 at V = 151936. Every call on
+ * one device shares that device's scratch: calls that may overlap on one
+ * device (different streams, or different threads) race and must be
+ * serialised by the caller. Nothing in the scratch needs to start at zero.
+ * LLP_EHIP if the scratch's address cannot be obtained.
+ */
+#define LLP_SCRATCH_BYTES (64u << 20)
+LLP_API int linear_logp_fwd_noalloc(int64_t N, int64_t D, int64_t V, int dtype,
+                            const void* h, const void* W, const void* b, const int64_t* targets,
+                            float* logp, float* lse, void* stream);
 
 /*
  * Workspace bytes linear_logp_bwd needs. It depends on which outputs are

@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_library_exports_every_declared_symbol():
     names = declared_symbols()
-    assert len(names) == 17
+    assert len(names) == 18
     L = llp.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -124,6 +124,26 @@ def test_fwd_pointer_and_workspace_errors():
         == llp.LLP_EWORKSPACE
     # N = 0 is a no-op that touches nothing, even with null pointers
     assert L.linear_logp_fwd(0, D, V, F32, None, None, None, None, None, None, None, 0, None) == llp.LLP_OK
+
+
+def test_noalloc_forward_argument_errors():
+    """The forward on the library's scratch checks its arguments and the
+    scratch's size before any HIP call."""
+    L = llp.lib()
+    f = L.linear_logp_fwd_noalloc
+    assert f(-1, 128, 1024, F32, FAKE, FAKE, None, FAKE, FAKE, None, None) == llp.LLP_EINVAL
+    assert f(4, 128, 1024, 7, FAKE, FAKE, None, FAKE, FAKE, None, None) == llp.LLP_EINVAL
+    for null in range(4):  # h, W, targets, logp are required
+        p = [FAKE] * 4
+        p[null] = None
+        assert f(256, 128, 1024, F32, p[0], p[1], None, p[2], p[3], None, None) == llp.LLP_EINVAL
+    # 33487 tokens at V = 32000 fit in the 64 MiB scratch, 33488 do not
+    assert llp.linear_logp_fwd_workspace_size(33487, 4096, 32000, BF16) <= llp.LLP_SCRATCH_BYTES
+    assert llp.linear_logp_fwd_workspace_size(33488, 4096, 32000, BF16) > llp.LLP_SCRATCH_BYTES
+    assert f(33488, 4096, 32000, BF16, FAKE, FAKE, None, FAKE, FAKE, None, None) == llp.LLP_EWORKSPACE
+    assert f(7059, 4096, 151936, BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == llp.LLP_EWORKSPACE
+    assert f(0, 128, 1024, F32, None, None, None, None, None, None, None) == llp.LLP_OK
+    assert f(1 << 31, 128, 1024, F32, FAKE, FAKE, None, FAKE, FAKE, None, None) == llp.LLP_EOVERFLOW
 
 
 def _bwd(N=256, D=128, V=1024, dt=F32, chunk=64, h=FAKE, W=FAKE, b=FAKE, t=FAKE, g=FAKE, lse=FAKE,
