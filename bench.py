@@ -192,22 +192,56 @@ def kernel_table(tr, steps, step_flops):
     return kernels
 
 
-def fused_step_flops(N, D, V, C, K, overlap, pairing, pair_dh=False):
+def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
+    """Chunks per dW contraction (G), the library's rule (its workspace plan):
+    with an FP32 table, dW and K >= 2, the single call and (for small chunks:
+    16-bit operands, fewer than 128 dH tiles) the two-call path accumulate dW
+    once per group of G chunks: G = 2, for small chunks up to 2048 group
+    columns and 256 MiB of group buffer, at most K."""
+    few = esize == 2 and -(-C // 256) * -(-D // 256) < 128
+    if not (table_f32 and K >= 2 and (fused or few)):
+        return 1
+    ld = -(-C // 8) * 8
+    g = 2
+    if few:
+        g = max(g, min(2048 // ld, (1 << 28) // (V * ld * esize)))
+    return min(g, K)
+
+
+def schedule(N, D, V, C, K, esize, fused, table_f32=True):
+    """(working chunk, chunks, chunks per dW group, dH per group) of the
+    library's backward schedule: with more than two small chunks per group, an
+    FP32 table and dH on the layout without W^T, a group runs as one working
+    chunk of G C tokens (no further grouping); otherwise the caller's chunks
+    in groups of G."""
+    G = dw_group(N, D, V, C, K, esize, fused, table_f32)
+    ld = -(-C // 8) * 8
+    lim = 0x7FFFFFF0
+    kmajor = esize == 2 and D % 8 == 0 and V * D * esize < lim and V * max(G * ld, 2 * ld) * esize < lim
+    if G > 2 and kmajor:
+        Cw = min(G * C, N)
+        return Cw, -(-N // Cw), 1, False
+    small = esize == 2 and C % 8 == 0 and -(-C // 256) * -(-D // 256) < 128
+    return C, K, G, G > 1 and small and kmajor
+
+
+def fused_step_flops(N, D, V, C, K, overlap, G=1, group_dh=False):
     """Algorithmic flop per step of each contraction launch kind of the single
     call: chunk k's logits tile, dH and (its share of) dW each cost 2 C_k V D.
     With overlap, chunk k + 1's forward tiles ride in chunk k's dH / dW launch
     (dh_dw_fwd) and only chunk 0's forward has a launch of its own; with
-    pairing, the dW of chunks (2j, 2j + 1) runs in the launch of chunk 2j + 1
-    (or of a last chunk without a partner); with pair_dh (small chunks) the dH
-    of a pair runs there too, and a launch left with neither dH nor dW is a
-    forward-only launch (fwd_lse)."""
+    groups of G chunks, the dW of a group runs in the launch of its last chunk;
+    with group_dh (small chunks) the dH of a group runs there too, and a
+    launch left with neither dH nor dW is a forward-only launch (fwd_lse)."""
     ck = [min(C, N - k * C) for k in range(K)]
     f = 2 * V * D
     out = {"fwd_lse": 0, "dh_dw": 0, "dh_dw_fwd": 0}
     for k in range(K):
-        pair = ck[k - 1] + ck[k] if k % 2 == 1 else (ck[k] if k == K - 1 else 0)
-        dw = f * pair if pairing else f * ck[k]
-        dh = f * pair if pair_dh else f * ck[k]
+        kg = k - k % G
+        end = k % G == G - 1 or k == K - 1
+        grp = sum(ck[kg:k + 1]) if end else 0
+        dw = f * grp
+        dh = f * grp if group_dh else f * ck[k]
         if overlap:
             if k == 0:
                 out["fwd_lse"] += f * ck[0]
@@ -288,14 +322,16 @@ def run_linear(w, args, torch, llp):
     peak = PEAK_TFLOPS[w.dtype]
     results = {}
     # the single call overlaps the next chunk's forward with 16-bit operands and
-    # runs dW once per pair of chunks with an FP32 table (K >= 2)
-    pairing = args.table == "f32" and K >= 2
-    overlap = w.dtype in ("bf16", "f16") and pairing
-    pair_dh = overlap and C % 8 == 0 and -(-C // 256) * -(-D // 256) < 128
+    # runs dW once per group of G chunks with an FP32 table (K >= 2); small
+    # chunks with C % 8 == 0 take dH per group too
+    esz = 4 if w.dtype == "f32" else 2
+    Cw, Kw, G, group_dh = schedule(N, D, V, C, K, esz, True, args.table == "f32")
+    overlap = w.dtype in ("bf16", "f16") and Kw >= 2 and D % 8 == 0
+    G_split = schedule(N, D, V, C, K, esz, False, args.table == "f32")
+    split_flops = {"fwd_lse": 2 * N * V * D, "dlogits": 2 * N * V * D, "dh_dw": 4 * N * V * D}
     for name, step, sf in (
-            ("split", split_step, {"fwd_lse": 2 * N * V * D, "dlogits": 2 * N * V * D,
-                                   "dh_dw": 4 * N * V * D}),
-            ("fused", fused_step, fused_step_flops(N, D, V, C, K, overlap, pairing, pair_dh))):
+            ("split", split_step, split_flops),
+            ("fused", fused_step, fused_step_flops(N, D, V, Cw, Kw, overlap, G, group_dh))):
         log(f"{name}: warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
         ms, tr = time_steps(step, args, torch, llp, stream)
         kernels = kernel_table(tr, args.steps, sf)
@@ -347,6 +383,8 @@ def run_linear(w, args, torch, llp):
         "dtype": w.dtype,
         "data": "synthetic (seeded counter-based generator; random-init weights)",
         "config": {"workload": w.name, "N": N, "D": D, "V": V, "chunk": C, "chunks": K,
+                   "working_chunk": (Cw if args.path == "fused" else G_split[0]),
+                   "chunks_per_dW": (G if args.path == "fused" else G_split[2]), "dH_vocab_parts": -(-V // 16384),
                    "bias": w.bias, "g": w.g, "dW_table": args.table, "outputs": "logp,lse,dH,dW" +
                    (",db" if w.bias else ""), "path": PATHS[args.path]},
         "pct_mfma_peak": main["pct_mfma_peak"],

@@ -699,7 +699,104 @@ hipError_t db_t(const void* dSt, int64_t ldSt, int64_t V, int64_t C, const float
   return hipGetLastError();
 }
 
+// dH rows of a split contraction: the S parts summed in increasing order,
+// then the dH tile epilogue's operations (same expressions, same order): the
+// row factor s rowf (0 for a token that takes no part), the one-hot term
+// tcoef W[t] for a valid token, rounding to the output dtype. kVec (D % 8 ==
+// 0): 8 consecutive columns per thread with 16-byte loads, and 16-byte
+// stores where `vec` says the output rows are 16-byte aligned; otherwise one
+// column per thread.
+template <typename T, bool kVec>
+__global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int64_t stride, int S,
+                                                        int64_t M, int64_t D, EpiParams e, int vec) {
+  constexpr int kCols = kVec ? 8 : 1;
+  const int64_t nq = D / kCols;
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t m = q / nq;
+  if (m >= M) return;
+  const int64_t n = (q - m * nq) * kCols;
+  const float* pp = part + m * D + n;
+  float sv[kCols];
+  if constexpr (kVec) {
+    const float4 a = *reinterpret_cast<const float4*>(pp);
+    const float4 b = *reinterpret_cast<const float4*>(pp + 4);
+    sv[0] = a.x, sv[1] = a.y, sv[2] = a.z, sv[3] = a.w, sv[4] = b.x, sv[5] = b.y, sv[6] = b.z, sv[7] = b.w;
+    for (int i = 1; i < S; ++i) {
+      const float4 u = *reinterpret_cast<const float4*>(pp + (int64_t)i * stride);
+      const float4 v = *reinterpret_cast<const float4*>(pp + (int64_t)i * stride + 4);
+      sv[0] += u.x, sv[1] += u.y, sv[2] += u.z, sv[3] += u.w;
+      sv[4] += v.x, sv[5] += v.y, sv[6] += v.z, sv[7] += v.w;
+    }
+  } else {
+    sv[0] = pp[0];
+    for (int i = 1; i < S; ++i) sv[0] += pp[(int64_t)i * stride];
+  }
+  const int64_t tok = e.tok0 + m;
+  const int64_t tg = e.targets[tok];
+  const int64_t t = tg - e.v0;
+  const bool valid = tg >= 0 && tg < e.Vt && t >= 0 && t < e.V && e.g[tok] != 0.0f;
+  const float sc = e.scales[e.chunk].x;
+  const float fr = e.rowf == nullptr ? sc : sc * e.rowf[tok];
+  const float c = valid ? e.tcoef[tok] : 0.0f;
+  const T* w = static_cast<const T*>(e.W) + (valid ? t : 0) * e.ldW + n;
+  float o[kCols];
+#pragma unroll
+  for (int j = 0; j < kCols; ++j) {
+    // a zero factor (a token that takes no part) gives +0, whatever the sign of the sum
+    const float base = fr == 0.0f ? 0.0f : sv[j] * fr;
+    o[j] = valid ? fmaf(c, (float)w[j], base) : base;
+  }
+  if (e.out_dt == DT_F32) {
+    float* out = static_cast<float*>(e.out) + m * e.ldo + n;
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) out[j] = o[j];
+  } else {
+    T* out = static_cast<T*>(e.out) + m * e.ldo + n;
+    if constexpr (kVec && sizeof(T) == 2) {
+      if (vec) {
+        union {
+          T h[8];
+          uint4 u;
+        } pk;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pk.h[j] = (T)o[j];
+        *reinterpret_cast<uint4*>(out) = pk.u;
+        return;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) out[j] = (T)o[j];
+  }
+}
+
+template <typename T>
+hipError_t dh_reduce_t(const float* part, int64_t stride, int S, int64_t M, int64_t D, const EpiParams& e,
+                       hipStream_t s) {
+  const bool v8 = D % 8 == 0;
+  const int64_t n = M * (v8 ? D / 8 : D);
+  if ((n + 255) / 256 > INT32_MAX) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  const int vec = (reinterpret_cast<uintptr_t>(e.out) % 16 == 0) && (e.ldo % 8 == 0);
+  if (v8)
+    dh_reduce_kernel<T, true><<<grid, 256, 0, s>>>(part, stride, S, M, D, e, vec);
+  else
+    dh_reduce_kernel<T, false><<<grid, 256, 0, s>>>(part, stride, S, M, D, e, vec);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_dh_reduce(int dt, const float* part, int64_t stride, int S, int64_t M, int64_t D,
+                            const EpiParams& e, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (S < 1) return hipErrorInvalidValue;
+  switch (dt) {
+    case DT_F32: return dh_reduce_t<float>(part, stride, S, M, D, e, s);
+    case DT_BF16: return dh_reduce_t<__bf16>(part, stride, S, M, D, e, s);
+    case DT_F16: return dh_reduce_t<_Float16>(part, stride, S, M, D, e, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,
                               const int64_t* targets, int64_t V, int64_t N, float* logp,

@@ -71,6 +71,15 @@ constexpr int kStageArr = kOpB;
 static_assert(kNS * kStageArr <= 160 * 1024, "gfx950 LDS per workgroup");
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Swizzle of the K-contiguous slots: chunk c (16 bytes) of row r sits at
+// position c ^ swz_row(r). gfx950's LDS serves a 16-byte read for 16 lanes
+// per cycle from 64 four-byte banks (256 bytes): the 16 rows a fragment read
+// touches in one cycle (rows r0 .. r0 + 15, 128 bytes apart) must cover the
+// 16 distinct 16-byte bank groups, i.e. rows of equal parity need distinct
+// positions. (r & 7) alone repeats at r + 8 (a 2-way conflict); the extra
+// bit (r / 8) & 1 separates them and keeps any 8 consecutive rows distinct.
+__device__ __forceinline__ int swz_row(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 // LDS handed to the epilogues: four regions of kOpB bytes.
 struct EpiLds {
   char* a[4];
@@ -361,6 +370,26 @@ __device__ __forceinline__ bool token_valid(const EpiParams& e, int64_t tok, int
   return tg >= 0 && tg < e.Vt && t >= 0 && t < e.V && e.g[tok] != 0.0f;
 }
 
+// A part of a split dH contraction: the raw fp32 sums of this tile's K range,
+// stored for the reduction, which adds the parts in increasing order and
+// applies the epilogue below. 32 lanes store 32 consecutive columns of a row.
+__device__ __forceinline__ void epi_store_part(const GemmProblem& p, Acc& acc, int part, int64_t m0, int64_t n0,
+                                               const Frag& f) {
+  const EpiParams& e = p.ep;
+  float* P = e.dhp + (int64_t)part * e.dhp_stride;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t m = m0 + f.row(mi, r);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int64_t n = n0 + f.col(ni);
+        if (m < p.M && n < p.N) P[m * e.ldo + n] = acc[mi][ni][r];
+      }
+    }
+}
+
 // dH rows of the chunk: out[m, :] = s C[m, :] + tcoef[m] W[t_m, :]. The
 // tile's per-token (target, coefficient) pairs are staged in LDS first.
 template <typename T>
@@ -615,14 +644,17 @@ __device__ __forceinline__ void epi_accum(const GemmProblem& p, Acc& acc, int64_
 // (K % BK != 0) goes through load_chunk, which zero-fills k >= K.
 template <typename T, bool kFast>
 __device__ __forceinline__ void mainloop(const GemmProblem& p, int64_t m0, int64_t n0, const Frag& f,
-                                         char* smem, Acc& acc) {
+                                         char* smem, Acc& acc, int part = 0) {
   constexpr int per16 = ET<T>::per16;
   constexpr int BK = (kRowBytes / 16) * per16;  // K elements per stage
   const int tid = threadIdx.x;
-  const T* A = static_cast<const T*>(p.A);
-  const T* B = static_cast<const T*>(p.B);
-  const int64_t nfull = kFast ? p.K / BK : 0;              // stages loaded without masks
-  const int64_t nstage = (p.K + BK - 1) / BK;              // >= 1
+  // a split problem's part covers the columns [k0, k0 + Kp) of both operands
+  const int64_t k0 = p.kparts > 1 ? (int64_t)part * p.kpart : 0;
+  const int64_t Kp = p.kparts > 1 ? min(p.K - k0, p.kpart) : p.K;
+  const T* A = static_cast<const T*>(p.A) + k0;
+  const T* B = static_cast<const T*>(p.B) + k0;
+  const int64_t nfull = kFast ? Kp / BK : 0;              // stages loaded without masks
+  const int64_t nstage = (Kp + BK - 1) / BK;              // >= 1
   const int64_t kc = (tid & 7) * per16;                    // this thread's k offset in a stage
 
   const T* pa[kLoadsPerThread];
@@ -649,8 +681,8 @@ __device__ __forceinline__ void mainloop(const GemmProblem& p, int64_t m0, int64
       for (int i = 0; i < kLoadsPerThread; ++i) {
         const int row = (tid >> 3) + i * (kThreads / 8);
         const int64_t k = kt * BK + kc;
-        ra[i] = load_chunk<T>(A, p.lda, m0 + row, p.M, k, p.K, p.a_vec != 0);
-        rb[i] = load_chunk<T>(B, p.ldb, n0 + row, p.N, k, p.K, p.b_vec != 0);
+        ra[i] = load_chunk<T>(A, p.lda, m0 + row, p.M, k, Kp, p.a_vec != 0);
+        rb[i] = load_chunk<T>(B, p.ldb, n0 + row, p.N, k, Kp, p.b_vec != 0);
       }
     }
   };
@@ -755,7 +787,7 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (
 // K-contiguous layout. K rows at or past K read as 0 (past the buffer end).
 template <typename T, bool kMn = false>
 __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, int64_t n0, const Frag& f,
-                                             char* const (&buf)[kNS], Acc& acc) {
+                                             char* const (&buf)[kNS], Acc& acc, int part = 0) {
   static_assert(kTileM == kTileN, "A and B slots have one shape");
   static_assert(!kMn || sizeof(T) == 2, "K-row-major operands are 16-bit");
   constexpr int per16 = ET<T>::per16;
@@ -779,15 +811,26 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(static_cast<const T*>(base) + off), (short)0, nrec,
                                              0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t rsA = kMn ? rsrc_mn(p.A, m0, p.K, p.lda, p.M)
-                                         : rsrc_of(static_cast<const T*>(p.A) + m0 * p.lda, p.M - m0, p.lda);
-  const __amdgpu_buffer_rsrc_t rsB = kMn ? rsrc_mn(p.B, n0, p.K, p.ldb, p.N)
-                                         : rsrc_of(static_cast<const T*>(p.B) + n0 * p.ldb, p.N - n0, p.ldb);
+  // K-row-major problems may be split into fixed K ranges (parts): this
+  // tile's rows [k0, k0 + Kp) of both operands
+  // (K-contiguous operands: the columns [k0, k0 + Kp) of every row; the part
+  // size is a multiple of 8, so no 16-byte piece straddles two parts)
+  int64_t k0 = 0, Kp = p.K;
+  if (p.kparts > 1) {
+    k0 = (int64_t)part * p.kpart;
+    Kp = min(p.K - k0, p.kpart);
+  }
+  const T* const Ak = static_cast<const T*>(p.A) + (kMn ? k0 * p.lda : k0);
+  const T* const Bk = static_cast<const T*>(p.B) + (kMn ? k0 * p.ldb : k0);
+  const __amdgpu_buffer_rsrc_t rsA = kMn ? rsrc_mn(Ak, m0, Kp, p.lda, p.M) : rsrc_of(Ak + m0 * p.lda, p.M - m0, p.lda);
+  const __amdgpu_buffer_rsrc_t rsB = kMn ? rsrc_mn(Bk, n0, Kp, p.ldb, p.N) : rsrc_of(Bk + n0 * p.ldb, p.N - n0, p.ldb);
   // Per-lane offsets of the wave's first DMA instruction of a unit; the
   // others follow at a wave-uniform stride (the swizzle term depends on the
   // lane only), so one register per operand covers all of them.
   uint32_t voA, voB, strA, strB;
-  int kel;  // K-contiguous: first K element of this lane's chunk
+  int kel;            // K-contiguous: first K element of this lane's chunk (even instructions)
+  uint32_t dodd = 0;  // K-contiguous: byte offset of odd instructions' chunk relative to even ones
+  int kel_odd = 0;
   if constexpr (kMn) {
     constexpr int nw = kThreads / 64;
     static_assert(nw % 2 == 0 && kLoads * 2 * nw == 64, "K-row-major placement: two K rows per instruction");
@@ -802,16 +845,24 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
     strB = (uint32_t)(2 * nw * p.ldb * (int64_t)sizeof(T));
     kel = 0;
   } else {
+    // LDS chunk position q of row r holds global chunk q ^ swz(r) (see
+    // swz_row). The first instruction's rows r = 32 w + lane / 8 have r / 8
+    // even; instruction j adds 8 j rows, so odd instructions flip bit 0 of
+    // the chunk: one more per-lane constant, the byte delta to that chunk.
+    static_assert(kRowsPerLoad == 8 && (kLoads * kRowsPerLoad) % 16 == 0, "row blocks of 8, wave blocks of 16");
     const int row = (wave * kLoads) * kRowsPerLoad + (lane >> 3);
-    const int c = (lane & 7) ^ (row & 7);  // LDS chunk lane & 7 holds global chunk c (row & 7 = (lane >> 3) & 7)
+    const int c = (lane & 7) ^ swz_row(row);  // LDS chunk lane & 7 holds global chunk c
+    const int c1 = c ^ 1;                     // the same lane's chunk in odd instructions
     voA = (uint32_t)(row * p.lda * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
     voB = (uint32_t)(row * p.ldb * (int64_t)sizeof(T)) + (uint32_t)(c * 16);
     strA = (uint32_t)(kRowsPerLoad * p.lda * (int64_t)sizeof(T));
     strB = (uint32_t)(kRowsPerLoad * p.ldb * (int64_t)sizeof(T));
     kel = c * per16;
+    kel_odd = c1 * per16;
+    dodd = (uint32_t)((c1 - c) * 16);  // +16 or -16 bytes (modulo 2^32)
   }
   const int lds_off = wave * kLoads * kRowsPerLoad * kSB;
-  const int64_t nst = (p.K + BKE - 1) / BKE;
+  const int64_t nst = (Kp + BKE - 1) / BKE;
 
   // pieces [j0, j1) of unit (stage s, operand O) into `slot`
   auto issue = [&](char* slot, int64_t s, auto Ov, int j0 = 0, int j1 = kLoads) {
@@ -819,12 +870,14 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       if (j < j0 || j >= j1) continue;
-      const uint32_t vo = (O ? voB : voA) + (uint32_t)j * (O ? strB : strA);
+      uint32_t vo = (O ? voB : voA) + (uint32_t)j * (O ? strB : strA);
       uint32_t off;
-      if constexpr (kMn)  // K rows past K lie past the buffer's end and read as 0
+      if constexpr (kMn) {  // K rows past K lie past the buffer's end and read as 0
         off = vo + (uint32_t)(s * BKE * (O ? p.ldb : p.lda) * (int64_t)sizeof(T));
-      else
-        off = (s * BKE + kel < p.K) ? vo + (uint32_t)(s * kSB) : 0xFFFFFFF0u;
+      } else {
+        if (j & 1) vo += dodd;
+        off = (s * BKE + ((j & 1) ? kel_odd : kel) < Kp) ? vo + (uint32_t)(s * kSB) : 0xFFFFFFF0u;
+      }
       // K-row-major: the 1 KiB block of instruction j holds K rows 2w + 2 nw j, +1
       char* const dst = kMn ? slot + wave * 1024 + j * (kThreads / 64) * 1024 : slot + lds_off + j * kRowsPerLoad * kSB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(O ? rsB : rsA, (lds_void_t*)dst, 16, off, 0, 0, 0);
@@ -873,12 +926,12 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       const int row = f.wm * kWaveRowsM + mi * 32 + (lane & 31);
-      fa[mi] = *reinterpret_cast<const u32x4*>(sa + row * kSB + ((c ^ (row & 7)) * 16));
+      fa[mi] = *reinterpret_cast<const u32x4*>(sa + row * kSB + ((c ^ swz_row(row)) * 16));
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int row = f.wn * kWaveColsN + ni * 32 + (lane & 31);
-      fb[ni] = *reinterpret_cast<const u32x4*>(sb + row * kSB + ((c ^ (row & 7)) * 16));
+      fb[ni] = *reinterpret_cast<const u32x4*>(sb + row * kSB + ((c ^ swz_row(row)) * 16));
     }
   };
   auto mma = [&](const u32x4 (&fa)[MI], const u32x4 (&fb)[NI]) {
@@ -947,6 +1000,14 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
 template <typename T, int E, bool kDma, bool kMn = false, int kAcc = ACC_ANY>
 __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* const (&buf)[kNS]) {
   int tm, tn;
+  int part = 0;  // K range of a split problem (part-major tile order)
+  if constexpr (E == EPI_STORE) {
+    if (p.kparts > 1) {
+      const int per = p.tiles_m * p.tiles_n;
+      part = id / per;
+      id -= part * per;
+    }
+  }
   tile_coords(id, p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * kTileM;
   const int64_t n0 = (int64_t)tn * kTileN;
@@ -968,19 +1029,24 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* con
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
   if constexpr (kDma) {
-    mainloop_dma<T, kMn>(p, m0, n0, f, buf, acc);
+    mainloop_dma<T, kMn>(p, m0, n0, f, buf, acc, part);
   } else {
     if (p.a_vec && p.b_vec)
-      mainloop<T, true>(p, m0, n0, f, buf[0], acc);
+      mainloop<T, true>(p, m0, n0, f, buf[0], acc, part);
     else
-      mainloop<T, false>(p, m0, n0, f, buf[0], acc);
+      mainloop<T, false>(p, m0, n0, f, buf[0], acc, part);
   }
   const EpiLds L = {{buf[0], buf[1], buf[2], buf[3]}};
 
   if constexpr (E == EPI_LSE_PARTIAL) epi_lse_partial<T, false>(p, acc, tm, m0, n0, f);
   if constexpr (E == EPI_LSE_Q) epi_lse_partial<T, true>(p, acc, tm, m0, n0, f);
   if constexpr (E == EPI_DLOGITS) epi_dlogits<T>(p, acc, m0, n0, f, L);
-  if constexpr (E == EPI_STORE) epi_store<T>(p, acc, m0, n0, f, L);
+  if constexpr (E == EPI_STORE) {
+    if (p.kparts > 1)
+      epi_store_part(p, acc, part, m0, n0, f);
+    else
+      epi_store<T>(p, acc, m0, n0, f, L);
+  }
   if constexpr (E == EPI_ACCUM) epi_accum<T, kAcc>(p, acc, m0, n0, f, L);
 }
 
@@ -1046,13 +1112,13 @@ hipError_t launch3_t(const GemmProblem& p0, const GemmProblem* p1, const GemmPro
   if constexpr (sizeof(T) != 2) {
     return hipErrorInvalidValue;
   } else {
-    const int nt0 = p0.tiles_m * p0.tiles_n, nt2 = p2.tiles_m * p2.tiles_n;
-    const int nt1 = p1 ? p1->tiles_m * p1->tiles_n : 0;
+    const int nt0 = problem_tiles(p0), nt2 = problem_tiles(p2);
+    const int nt1 = p1 ? problem_tiles(*p1) : 0;
     GemmProblem empty = {};
     const GemmProblem& b = p1 ? *p1 : empty;
     const int acc = p1 == nullptr ? ACC_FAST : !p1->ep.tab_fast ? ACC_ANY : p1->ep.tab_store ? ACC_FRESH : ACC_FAST;
     if (!p0.mn || !p0.dma || !p2.dma || (p1 && !p1->dma) || acc == ACC_ANY || p0.epi != EPI_STORE ||
-        p2.epi != EPI_LSE_Q)
+        p2.epi != EPI_LSE_Q || p2.kparts > 1 || (p1 && p1->kparts > 1))
       return hipErrorInvalidValue;
     dim3 grid(nt0 + nt1 + nt2), block(kThreads);
     if (acc == ACC_FAST) gemm3_kernel<T, ACC_FAST><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
@@ -1063,9 +1129,11 @@ hipError_t launch3_t(const GemmProblem& p0, const GemmProblem* p1, const GemmPro
 
 template <typename T>
 hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s) {
-  const int nt0 = p0 ? p0->tiles_m * p0->tiles_n : 0;
-  const int nt1 = p1 ? p1->tiles_m * p1->tiles_n : 0;
+  const int nt0 = p0 ? problem_tiles(*p0) : 0;
+  const int nt1 = p1 ? problem_tiles(*p1) : 0;
   if (nt0 + nt1 == 0) return hipSuccess;
+  // a split problem (dH, EPI_STORE) comes first; every other problem is unsplit
+  if ((p1 && p1->kparts > 1) || (p0 && p0->kparts > 1 && p0->epi != EPI_STORE)) return hipErrorInvalidValue;
   GemmProblem empty = {};
   const GemmProblem& a = p0 ? *p0 : empty;
   const GemmProblem& b = p1 ? *p1 : empty;

@@ -87,6 +87,11 @@ struct EpiParams {
   void* out;
   int64_t ldo;
   int out_dt;              // dtype of out (EPI_ACCUM table: DT_F32 or the operand dtype)
+  // EPI_STORE of a split contraction (GemmProblem::kparts > 1): the tile of
+  // part p stores its raw fp32 sums at dhp + p dhp_stride + m ldo + n, and
+  // launch_dh_reduce applies the epilogue to their sum
+  float* dhp;
+  int64_t dhp_stride;
   // backward epilogues: scales[chunk] = (multiplier applied to C, divisor of the stored part)
   const float2* scales;
   int chunk;
@@ -105,9 +110,16 @@ struct GemmProblem {
                      //    [K][ldb] (rows of the tile contiguous within a K row) instead of K-contiguous;
                      //    K * ld * esize < 2 GiB for both, ld % 8 == 0, 16-byte aligned
   int tiles_m, tiles_n;
+  // K split into kparts fixed ranges of kpart (a multiple of 8) rows or
+  // columns (STORE problems only; 0 or 1: no split); the grid then holds
+  // tiles_m * tiles_n * kparts tiles, part-major
+  int kparts;
+  int64_t kpart;
   int epi;
   EpiParams ep;
 };
+
+inline int problem_tiles(const GemmProblem& p) { return p.tiles_m * p.tiles_n * (p.kparts > 1 ? p.kparts : 1); }
 
 // Launch one or two independent problems of the same operand dtype in one
 // grid (the second problem's tiles follow the first's). Returns hipError_t.
@@ -208,6 +220,13 @@ struct ChunkPrep {
   int64_t ldS;
 };
 hipError_t launch_chunk_prep(int dt, const ChunkPrep& c, hipStream_t s);
+
+// dH rows of a split contraction: out[m, n] = the EPI_STORE epilogue (row
+// factor s rowf, one-hot term tcoef W[t], rounding to out_dt) applied to
+// sum_{p = 0 .. S - 1} part[p][m][n], summed in increasing p; m < M, n < D. `e` carries the STORE epilogue's parameters (tok0 = the
+// first token of row 0).
+hipError_t launch_dh_reduce(int dt, const float* part, int64_t stride, int S, int64_t M, int64_t D,
+                            const EpiParams& e, hipStream_t s);
 
 // Fill n elements of size esize with +0.
 hipError_t launch_zero(void* p, int64_t n, int esize, hipStream_t s);

@@ -305,21 +305,34 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
 
   const int64_t lim = 0x7FFFFFF0LL;
   const bool tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < lim;
-  // With an FP32 table (both paths): one dW contraction per pair of chunks
-  // (2j, 2j + 1) over the columns of both, which sit side by side in the
-  // vocab-major buffer [V][2 ldSt] and the h^T buffer [D][2 ldSt]: the table
-  // is read and written once per pair. The pair shares one power-of-two scale
-  // (scale index = pair index), so both halves of the contraction agree.
+  // With an FP32 table (both paths): one dW contraction per group of G
+  // consecutive chunks (the plan's G, from the shapes alone) over the columns
+  // of all of them, which sit side by side in the vocab-major buffer
+  // [V][G ldSt] and the h^T buffer [D][G ldSt]: the table is read and written
+  // once per group. The group shares one power-of-two scale (scale index =
+  // group index), so every part of the contraction is in the same units.
   // The two-call path has no forward tiles to fill the launches that carry no
-  // dW, so it pairs only small chunks (16-bit operands, C % 8 == 0, a dH grid
-  // of fewer than 128 tiles), whose dH is then paired too (see pair_dh).
-  // Shapes alone decide, so every subset of outputs accumulates dW alike.
-  const bool small_dh = e == 2 && bp.C % 8 == 0 && ceil_div(bp.C, kTile) * ceil_div(D, kTile) < 128;
-  const bool pairing = want_dW && tab_fast && bp.K >= 2 && bp.ldP == 2 * bp.ldSt && (fused || small_dh);
-  const int64_t ldq = pairing ? bp.ldP : bp.ldSt;  // leading dimension of those buffers
-  auto sidx = [&](int64_t k) { return (int)(pairing ? k >> 1 : k); };
+  // dW, so it groups only small chunks (16-bit operands, a dH grid of fewer
+  // than 128 tiles); with C % 8 == 0 their dH runs once per group too (see
+  // group_dh). Shapes alone decide, so every subset of outputs accumulates dW
+  // alike.
+  // The working schedule: with an FP32 table (dW_dtype, whether or not dW is
+  // requested) and a plan whose working chunk covers a whole group of small
+  // chunks (Cw > C), chunks of Cw tokens and no further grouping; otherwise
+  // the caller's chunks, grouped by the plan's G. (logp, lse and dH do not
+  // depend on the chunking; the FP32 table's additions come in another order.)
+  const bool work = dW_dtype == LLP_F32 && bp.Cw > bp.C;
+  const int64_t C = work ? bp.Cw : bp.C;
+  const int64_t K = work ? ceil_div(N, C) : bp.K;
+  const int64_t ldSt = work ? round_up(C, 8) : bp.ldSt;
+  const bool small_dh = e == 2 && C % 8 == 0 && ceil_div(C, kTile) * ceil_div(D, kTile) < 128;
+  const int64_t G = (want_dW && tab_fast && bp.G > 1 && !work) ? bp.G : 1;
+  const bool grouping = G > 1;
+  const int64_t ldq = grouping ? bp.ldP : ldSt;  // leading dimension of those buffers
+  auto gj = [&](int64_t k) { return k % G; };       // position of chunk k in its group
+  auto sidx = [&](int64_t k) { return (int)(k / G); };
   // the chunk whose launch carries the first dW contraction
-  const int64_t fdw = pairing ? 1 : 0;
+  const int64_t fdw = (G < K ? G : K) - 1;
 
   float2* scales = reinterpret_cast<float2*>(at(workspace, bp.off_scales));
   const float* lse_use = lse;
@@ -358,35 +371,36 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   const bool qtok = bp.qtok;
   int32_t* const qflag = qtok ? reinterpret_cast<int32_t*>(at(workspace, bp.off_qflag)) : nullptr;
   float* const cq = qtok ? reinterpret_cast<float*>(at(workspace, bp.off_cq)) : nullptr;
-  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, pairing ? 2 * bp.C : bp.C, pairing ? ceil_div(bp.K, 2) : bp.K,
-                                              dtype == LLP_F16 ? 15 : 0, scales, s));
+  LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, G * C, ceil_div(K, G), dtype == LLP_F16 ? 15 : 0, scales,
+                                              s));
   if (want_dH && !mn) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
   // Fused path with two numerator / partial buffers: chunk k + 1's forward
   // tiles run in the launch of chunk k's dH / dW (its fast epilogue only).
   const bool overlap = fused && mn && aligned16(h) && bp.off_dSt2 >= 0 && (!want_dW || tab_fast);
   void* const dSt_buf[2] = {dSt, overlap ? at(workspace, bp.off_dSt2) : dSt};
   float2* const part_buf[2] = {part, overlap ? reinterpret_cast<float2*>(at(workspace, bp.off_part2)) : part};
-  // chunk k's numerator / dlogits^T columns: with pairing, half k % 2 of the
-  // buffer of pair k / 2 (the pairs alternate between the two buffers with
-  // overlap); the h^T columns likewise, in the one h^T buffer
+  // chunk k's numerator / dlogits^T columns: with grouping, column block
+  // k % G of the buffer of group k / G (the groups alternate between the two
+  // buffers with overlap); the h^T columns likewise, in the one h^T buffer
   auto qbuf = [&](int64_t k) -> void* {
-    if (!pairing) return dSt_buf[k & 1];
-    return static_cast<char*>(dSt_buf[(k >> 1) & 1]) + (k & 1) * bp.ldSt * e;
+    if (!grouping) return dSt_buf[k & 1];
+    return static_cast<char*>(dSt_buf[(k / G) & 1]) + gj(k) * ldSt * e;
   };
   auto hbuf = [&](int64_t k) -> void* {
-    return pairing ? static_cast<char*>(ht) + (k & 1) * bp.ldSt * e : ht;
+    return grouping ? static_cast<char*>(ht) + gj(k) * ldSt * e : ht;
   };
   if (qtok) LLP_LAUNCH(LLP_K_SMALL, launch_zero(qflag, N, 4, s));
-  // With pairing and the K-row-major dH, a chunk whose dH grid is small (fewer
-  // than 128 tiles: small chunks) takes dH once per pair as well, over both
-  // chunks' columns (contiguous when C % 8 == 0): twice the tiles for the same
-  // contraction over the vocabulary. Every dH element still accumulates over
-  // V in the same order, so dH is bitwise the same either way.
-  const bool pair_dh = pairing && mn && small_dh;
+  // With grouping and the K-row-major dH, a chunk whose dH grid is small
+  // (fewer than 128 tiles: small chunks) takes dH once per group as well,
+  // over all its chunks' columns (contiguous when C % 8 == 0): G times the
+  // tiles for the same contraction over the vocabulary. Every dH element
+  // still accumulates over V in the same order, so dH is bitwise the same
+  // either way.
+  const bool group_dh = grouping && mn && small_dh;
   // the forward tile problem and the combine of chunk kk (fused path)
   auto fwd_problem = [&](int64_t kk) {
-    const int64_t c0 = kk * bp.C;
-    const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
+    const int64_t c0 = kk * C;
+    const int64_t Ck = (N - c0 < C) ? (N - c0) : C;
     GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
     p.ep.bias = b;
     p.ep.targets = targets;
@@ -395,7 +409,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     p.ep.Vt = Vt;
     p.epi = EPI_LSE_Q;
     p.ep.partials = part_buf[kk & 1];
-    p.ep.ldp = bp.C;
+    p.ep.ldp = C;
     p.ep.zt = zt;
     p.ep.dSt = qbuf(kk);
     p.ep.ldSt = ldq;
@@ -404,9 +418,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     return p;
   };
   auto combine = [&](int64_t kk) {
-    const int64_t c0 = kk * bp.C;
-    const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
-    return launch_lse_combine(part_buf[kk & 1], bp.P, bp.C, zt + c0, targets + c0, V, Ck, logp_out + c0,
+    const int64_t c0 = kk * C;
+    const int64_t Ck = (N - c0 < C) ? (N - c0) : C;
+    return launch_lse_combine(part_buf[kk & 1], bp.P, C, zt + c0, targets + c0, V, Ck, logp_out + c0,
                               lse_fused + c0, g + c0, tcoef + c0, s, qtok ? qflag + c0 : nullptr,
                               scales + sidx(kk), qtok ? cq + c0 : nullptr);
   };
@@ -414,9 +428,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   // epilogue (an FP32 table takes its one-hot rows in the chunk preparation)
   const bool lists = want_db || (want_dW && dW_dtype != LLP_F32);
 
-  for (int64_t k = 0; k < bp.K; ++k) {
-    const int64_t c0 = k * bp.C;
-    const int64_t Ck = (N - c0 < bp.C) ? (N - c0) : bp.C;
+  for (int64_t k = 0; k < K; ++k) {
+    const int64_t c0 = k * C;
+    const int64_t Ck = (N - c0 < C) ? (N - c0) : C;
     void* const dSt = qbuf(k);             // this chunk's numerator / dlogits^T columns
     float2* const part = part_buf[k & 1];  // and its forward partials
     GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
@@ -482,7 +496,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       cp.qt = dSt;
       cp.ldq = ldq;
       cp.partials = part;
-      cp.ldp = bp.C;
+      cp.ldp = C;
       cp.lse = lse_fused + c0;
       cp.gc = g + c0;
       cp.tc = targets + c0;
@@ -501,14 +515,16 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, ldq, V, Ck, scales, sidx(k), head, next, targets, g, tcoef,
                               c0, v0, Vt, db, dW_dtype, s, qtok ? cq + c0 : nullptr));
     GemmProblem ph = {}, pw = {};
-    // this launch's dH: chunk k, or with pair_dh the pair (k - 1, k) at odd k
-    // (none at an even k that has a partner)
-    const bool dh_pair = pair_dh && (k & 1);
-    const bool do_dh = want_dH && (!pair_dh || (k & 1) || k == bp.K - 1);
-    const int64_t h0 = dh_pair ? c0 - bp.C : c0;  // first token of this dH
-    const int64_t hM = dh_pair ? bp.C + Ck : Ck;  // its tokens
+    // the group of chunk k: first chunk kg, k is its last chunk (so far)
+    const int64_t kg = k - gj(k);
+    const bool group_end = gj(k) == G - 1 || k == K - 1;
+    // this launch's dH: chunk k, or with group_dh the whole group at its last
+    // chunk (none at the group's other chunks)
+    const bool do_dh = want_dH && (!group_dh || group_end);
+    const int64_t h0 = group_dh ? kg * C : c0;           // first token of this dH
+    const int64_t hM = group_dh ? (k - kg) * C + Ck : Ck;  // its tokens
     if (do_dh && mn) {
-      ph.A = dh_pair ? qbuf(k - 1) : dSt;
+      ph.A = group_dh ? qbuf(kg) : dSt;
       ph.B = W;
       ph.lda = ldq;
       ph.ldb = D;
@@ -548,20 +564,27 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       ph.ep.scales = scales;
       ph.ep.chunk = sidx(k);
       ph.ep.rowf = cq;  // per-token mode: indexed tok0 + row
+      if (bp.dh_parts > 1) {
+        // the vocabulary in fixed parts: one tile per part, fp32 partials,
+        // then the reduction below applies this epilogue to their sum
+        ph.kparts = (int)bp.dh_parts;
+        ph.kpart = kDhPart;
+        ph.ep.dhp = reinterpret_cast<float*>(at(workspace, bp.off_dhp));
+        ph.ep.dhp_stride = bp.dh_rows * D;
+      }
     }
-    // with pairing, the dW contraction of pair j runs in the launch of its
-    // second chunk (or of a last chunk without a partner), over K = ldSt + Ck
-    // columns (the first chunk's padding columns are +0 in both operands)
-    const bool do_dw = want_dW && (!pairing || (k & 1) || k == bp.K - 1);
+    // with grouping, the dW contraction of a group runs in the launch of its
+    // last chunk, over K = (k - kg) ldSt + Ck columns (the earlier chunks'
+    // padding columns are +0 in both operands)
+    const bool do_dw = want_dW && group_end;
     if (do_dw) {
-      const bool second = pairing && (k & 1);
-      pw.A = second ? qbuf(k - 1) : dSt;
-      pw.B = second ? hbuf(k - 1) : hbuf(k);
+      pw.A = qbuf(kg);
+      pw.B = hbuf(kg);
       pw.lda = ldq;
       pw.ldb = ldq;
       pw.M = V;
       pw.N = D;
-      pw.K = second ? bp.ldSt + Ck : Ck;
+      pw.K = (k - kg) * ldSt + Ck;
       pw.a_vec = pw.b_vec = 1;
       pw.dma = dma_ok(pw, e, true);  // dlogits^T and h^T padding columns are written +0
       pw.tiles_m = (int)ceil_div(V, kTile);
@@ -572,7 +595,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.out_dt = dW_dtype;
       pw.ep.targets = targets;
       pw.ep.g = g;
-      pw.ep.tok0 = second ? c0 - bp.C : c0;
+      pw.ep.tok0 = kg * C;
       pw.ep.V = V;
       pw.ep.v0 = v0;
       pw.ep.Vt = Vt;
@@ -587,19 +610,21 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.scales = scales;
       pw.ep.chunk = sidx(k);
     }
-    if (overlap && k + 1 < bp.K) {
+    if (overlap && k + 1 < K) {
       // with the next chunk's forward tiles, then that chunk's combine
       const GemmProblem pf = fwd_problem(k + 1);
       if (do_dh)
         LLP_LAUNCH(LLP_K_DH_DW_FWD, launch_gemm3(dtype, ph, do_dw ? &pw : nullptr, pf, s));
-      else  // pair_dh at an even chunk with a partner: no dH and (pairing) no dW in this launch
+      else  // group_dh before the group's last chunk: no dH and (grouping) no dW in this launch
         LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &pf, nullptr, s));
       LLP_LAUNCH(LLP_K_COMBINE, combine(k + 1));
     } else if (do_dh || do_dw) {
       LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, do_dh ? &ph : nullptr, do_dw ? &pw : nullptr, s));
     }
+    if (do_dh && ph.kparts > 1)
+      LLP_LAUNCH(LLP_K_DH_REDUCE, launch_dh_reduce(dtype, ph.ep.dhp, ph.ep.dhp_stride, ph.kparts, hM, D, ph.ep, s));
   }
-  if (store_first && bp.K == fdw + 1 && dW_dtype == LLP_F32) {
+  if (store_first && K == fdw + 1 && dW_dtype == LLP_F32) {
     // the contraction that stored the table was the last one: the one-hot
     // rows of every chunk follow it
     ChunkPrep cp = {};

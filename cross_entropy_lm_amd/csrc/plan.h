@@ -15,6 +15,8 @@ constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;  // one workgroup per row /
 constexpr int64_t kTile = kTileM;               // contraction tile edge (M and N)
 static_assert(kTileM == kTileN, "square tiles");
 constexpr int64_t kAlign = 256;                 // workspace region alignment (bytes)
+constexpr int64_t kGroupCols = 2048;            // small chunks: columns of a dW group at most
+constexpr int64_t kGroupBytes = int64_t(1) << 28;  // ... and bytes of one group buffer at most
 
 inline bool dtype_ok(int dt) { return dt == LLP_F32 || dt == LLP_BF16 || dt == LLP_F16; }
 inline int64_t esize(int dt) { return dt == LLP_F32 ? 4 : 2; }
@@ -99,10 +101,19 @@ inline int plan_fwd(int64_t N, int64_t D, int64_t V, int dtype, FwdPlan* p) {
 struct BwdPlan {
   int64_t C = 0, K = 0;                  // tokens per chunk, number of chunks
   int64_t ldWt = 0, ldS = 0, ldSt = 0;   // leading dimensions (elements), multiples of 8
-  // leading dimension of the vocab-major and h^T buffers: 2 ldSt where dW is
-  // accumulated once per pair of chunks (dW, K >= 2; the two-call layout only
-  // for small chunks), whose buffers hold a pair (chunk 2j in the columns
-  // [0, C), chunk 2j + 1 from column ldSt), else ldSt
+  // dW is accumulated once per group of G consecutive chunks (G = 1: per
+  // chunk): the single call with dW and K >= 2, and the two-call path for
+  // small chunks (fewer than 128 dH tiles). G = 2, or for small chunks up to
+  // 2048 group columns while one group buffer stays within 256 MiB.
+  int64_t G = 1;
+  // Working chunk. With more than two small chunks per group and the layout
+  // without W^T, a group is processed as one chunk of Cw = min(G C, N)
+  // tokens when the table is FP32: its logits, dH and dW in one pass each,
+  // which fills the 256-token tiles that a 110-token chunk would leave half
+  // empty. Otherwise Cw = C. Buffers are sized for Cw.
+  int64_t Cw = 0;
+  // leading dimension of the vocab-major and h^T buffers: G ldSt (chunk j of
+  // a group in the columns [j ldSt, j ldSt + C)), which also holds round8(Cw)
   int64_t ldP = 0;
   int64_t off_scales = -1;               // float2 [K]
   int64_t off_lse = -1;                  // float [N] when the caller gives no lse
@@ -116,6 +127,12 @@ struct BwdPlan {
   // bf16 single call: per-token numerators (same shape conditions, whether or
   // not dH is asked for, so that every subset of outputs computes alike)
   bool qtok = false;
+  // dH: the vocabulary is cut into dh_parts = ceil(V / kDhPart) fixed parts;
+  // with more than one, each part's fp32 sums go to [dh_parts][dh_rows][D]
+  // (dh_rows: the most rows one dH contraction covers, G C where small chunks group)
+  int64_t dh_parts = 1;
+  int64_t dh_rows = 0;
+  int64_t off_dhp = -1;
   int64_t off_Wt = -1;                   // W^T [D][ldWt]            (dH, not kmajor)
   int64_t off_dS = -1;                   // dlogits [C][ldS]         (dH, not kmajor)
   int64_t off_dSt = -1;                  // dlogits^T [V][ldP]       (dW or db)
@@ -131,6 +148,7 @@ struct BwdPlan {
   int64_t off_cq = -1;                   // float [N]: per-token mode, the tokens' gradient factors
   // second numerator and partial buffers (16-bit operands, dH, K >= 2): the
   // next chunk's forward then runs in the same launch as this chunk's dH / dW
+  // (the groups alternate between the two numerator buffers)
   int64_t off_dSt2 = -1;
   int64_t off_part2 = -1;
   int64_t bytes = 0;
@@ -152,17 +170,46 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   p->ldWt = round_up(V, 8);
   p->ldS = round_up(V, 8);
   p->ldSt = round_up(p->C, 8);
-  // (the two-call layout pairs only small chunks: 16-bit operands, C % 8 == 0
-  // and fewer than 128 tiles of 256 x 256 in a chunk's dH)
-  const bool small = esize(dtype) == 2 && p->C % 8 == 0 && ceil_div(p->C, kTile) * ceil_div(D, kTile) < 128;
-  p->ldP = (want_dW && p->K >= 2 && (fused || small)) ? 2 * p->ldSt : p->ldSt;
+  // small chunks: 16-bit operands and fewer than 128 tiles of 256 x 256 in a
+  // chunk's dH; the two-call layout groups only these
+  const bool few = esize(dtype) == 2 && ceil_div(p->C, kTile) * ceil_div(D, kTile) < 128;
+  // with C % 8 == 0 a group's token rows are contiguous columns, and dH runs once per group
+  const bool small = few && p->C % 8 == 0;
+  // Group size from the shapes alone (which outputs are requested does not
+  // change the schedule): 2 chunks, or for small chunks up to kGroupCols
+  // columns and kGroupBytes of group buffer.
+  int64_t gc = 1;
+  if (p->K >= 2 && (fused || few)) {
+    int64_t g = 2;
+    if (few) {
+      int64_t vb;
+      const int64_t by_cols = kGroupCols / p->ldSt;
+      const int64_t by_bytes = (mul_ok(V, p->ldSt, &vb) && mul_ok(vb, e, &vb) && vb > 0) ? kGroupBytes / vb : 0;
+      const int64_t m = by_cols < by_bytes ? by_cols : by_bytes;
+      if (m > g) g = m;
+    }
+    gc = g < p->K ? g : p->K;
+  }
+  p->G = want_dW ? gc : 1;
+  // 16-bit operands with D % 8 == 0 whose operands (W, and a group's
+  // dlogits^T) each span < 2 GiB: dH reads them as stored (kmajor), the bf16
+  // single call stores per-token numerators (qtok), and a group of more than
+  // two chunks runs as one working chunk (Cw)
+  bool shape;
   {
     const int64_t lim = 0x7FFFFFF0LL;
     int64_t vd, vq;
-    const bool shape = e == 2 && D % 8 == 0 && mul_ok(V, D, &vd) && mul_ok(vd, e, &vd) && vd < lim &&
-                       mul_ok(V, 2 * p->ldSt, &vq) && mul_ok(vq, e, &vq) && vq < lim;
+    const int64_t cols = gc > 2 ? gc * p->ldSt : 2 * p->ldSt;
+    shape = e == 2 && D % 8 == 0 && mul_ok(V, D, &vd) && mul_ok(vd, e, &vd) && vd < lim && mul_ok(V, cols, &vq) &&
+            mul_ok(vq, e, &vq) && vq < lim;
     p->kmajor = want_dH && shape;
     p->qtok = fused && dtype == LLP_BF16 && shape;
+  }
+  p->Cw = (gc > 2 && shape) ? (gc * p->C < N ? gc * p->C : N) : p->C;
+  {
+    const int64_t wcols = round_up(p->Cw, 8);
+    if (!mul_ok(p->G, p->ldSt, &p->ldP)) return LLP_EOVERFLOW;
+    if (wcols > p->ldP) p->ldP = wcols;
   }
   Layout L;
   int64_t n;
@@ -177,11 +224,26 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   }
   if (fused) {
     p->P = kWaveM * ceil_div(V, kTile);
-    if (!mul_ok(p->P, p->C, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
+    if (!mul_ok(p->P, p->Cw, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
     p->off_part = L.add(n);
     p->off_zt = L.add(N * 4);
     p->off_qflag = L.add(N * 4);
     p->off_cq = L.add(N * 4);
+  }
+  if (want_dH) {
+    p->dh_parts = ceil_div(V, kDhPart);
+    // small chunks take dH per group (C % 8 == 0) or per working chunk
+    p->dh_rows = p->Cw > p->C ? p->Cw : (p->kmajor && p->G > 1 && small) ? p->G * p->C : p->C;
+    if (p->dh_parts > 1) {
+      int64_t rd;
+      if (!mul_ok(p->dh_rows, D, &rd) || !mul_ok(rd, p->dh_parts, &n) || !mul_ok(n, 4, &n)) return LLP_EOVERFLOW;
+      if (rd / 4 / 256 + 1 > kMaxRows) return LLP_EOVERFLOW;  // the reduction's grid
+      // the dH tiles of every part, with a chunk's forward and dW tiles, in one grid
+      if ((ceil_div(p->dh_rows, kTile) * ceil_div(D, kTile) * p->dh_parts + 3 * ceil_div(V, kTile) *
+           (ceil_div(D, kTile) + ceil_div(p->Cw, kTile))) > kMaxRows)
+        return LLP_EOVERFLOW;
+      p->off_dhp = L.add(n);
+    }
   }
   if (want_dH && !p->kmajor) {
     if (!mul_ok(D, p->ldWt, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
@@ -194,7 +256,7 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     p->off_dSt = L.add(n);
     if (fused && p->kmajor && p->K >= 2) {
       p->off_dSt2 = L.add(n);
-      if (!mul_ok(p->P, p->C, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
+      if (!mul_ok(p->P, p->Cw, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
       p->off_part2 = L.add(n);
     }
   }
@@ -205,11 +267,11 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   p->off_tcoef = L.add(N * 4);
   if (want_dW || want_db) {
     p->off_head = L.add(V * 4);
-    p->off_next = L.add(p->C * 4);
+    p->off_next = L.add(p->Cw * 4);
   }
   if (!L.ok) return LLP_EOVERFLOW;
-  // the chunk's contraction tiles must fit grid.x too
-  if (ceil_div(p->C, kTile) * ceil_div(V, kTile) > kMaxRows) return LLP_EOVERFLOW;
+  // the working chunk's contraction tiles must fit grid.x too
+  if (ceil_div(p->Cw, kTile) * ceil_div(V, kTile) > kMaxRows) return LLP_EOVERFLOW;
   p->bytes = L.bytes;
   return LLP_OK;
 }

@@ -41,12 +41,13 @@ static std::vector<std::pair<int64_t, int64_t>> regions(const BwdPlan& p, int64_
   add(p.off_dSt, V * p.ldP * e);
   add(p.off_dSt2, V * p.ldP * e);
   add(p.off_ht, D * p.ldP * e);
+  add(p.off_dhp, p.dh_parts * p.dh_rows * D * 4);
   add(p.off_tcoef, N * 4);
   add(p.off_head, V * 4);
-  add(p.off_next, p.C * 4);
+  add(p.off_next, p.Cw * 4);
   if (fused) {
-    add(p.off_part, p.P * p.C * 8);
-    add(p.off_part2, p.P * p.C * 8);
+    add(p.off_part, p.P * p.Cw * 8);
+    add(p.off_part2, p.P * p.Cw * 8);
     add(p.off_zt, N * 4);
     add(p.off_qflag, N * 4);
     add(p.off_cq, N * 4);
@@ -67,10 +68,23 @@ static void check_layout(int64_t N, int64_t D, int64_t V, int dt, int64_t chunk,
     return;
   }
   EXPECT(p.ldSt % 8 == 0 && p.ldSt >= p.C);
-  EXPECT(p.ldP == p.ldSt || p.ldP == 2 * p.ldSt);
+  // dW groups of G chunks: G = 1 or 2, or more for small chunks within the
+  // 2048-column and 256 MiB caps, never more than the chunks
+  EXPECT(p.G >= 1 && p.G <= (p.K > 1 ? p.K : 1) && p.ldP >= p.G * p.ldSt);
+  EXPECT(p.ldP == (p.G * p.ldSt > round_up(p.Cw, 8) ? p.G * p.ldSt : round_up(p.Cw, 8)));
+  if (p.G > 2) EXPECT(p.G * p.ldSt <= 2048 && V * p.ldP * esize(dt) <= (int64_t(1) << 28));
+  if (!dw) EXPECT(p.G == 1);
   // the layout holds only what the requested outputs need
   EXPECT(p.kmajor == (dh && esize(dt) == 2 && D % 8 == 0 && (p.off_Wt < 0)));
   if (p.kmajor) EXPECT(p.off_Wt < 0 && p.off_dS < 0 && p.off_dSt >= 0);
+  if (dh) EXPECT(p.dh_parts == (V + 16383) / 16384);
+  if (dh) EXPECT(p.dh_rows == p.C || p.dh_rows == p.G * p.C || p.dh_rows == p.Cw);
+  // the working chunk: the chunk, or a whole group of more than two chunks (at most N tokens)
+  // (Cw does not depend on which outputs are requested: G is the group of the dW schedule)
+  EXPECT(p.Cw >= p.C && p.Cw <= (N > p.C ? N : p.C) && (p.Cw - p.C) % p.C == 0 || p.Cw == N);
+  if (dw && p.Cw > p.C) EXPECT(p.G > 2 && p.Cw == (p.G * p.C < N ? p.G * p.C : N));
+  EXPECT(round_up(p.Cw, 8) <= p.ldP);
+  EXPECT((p.off_dhp >= 0) == (dh && p.dh_parts > 1));
   if (dh && !p.kmajor) EXPECT(p.off_Wt >= 0 && p.off_dS >= 0);
   if (!dh) EXPECT(p.off_Wt < 0 && p.off_dS < 0 && p.off_dSt2 < 0);
   if (!dw) EXPECT(p.off_ht < 0);

@@ -65,16 +65,25 @@ def test_workspace_queries():
     assert only_dh < full and only_dw <= full and no_lse > full
     # 16-bit operands with D % 8 == 0: dH reads dlogits^T and W as stored, so
     # the chunk workspace is dlogits^T plus h^T of one chunk (no W^T, no
-    # token-major dlogits: nothing the requested outputs do not need)
-    expect = 2048 * 32000 * 2 + 4096 * 2048 * 2
+    # token-major dlogits: nothing the requested outputs do not need), plus
+    # the fp32 sums of dH's ceil(V / 16384) vocabulary parts (2 at V = 32000)
+    parts = lambda V: -(-V // 16384)  # noqa: E731
+    expect = 2048 * 32000 * 2 + 4096 * 2048 * 2 + parts(32000) * 2048 * 4096 * 4
     assert expect <= full < expect + (1 << 20)
-    # small chunks (fewer than 128 dH tiles) pair dW: dlogits^T and h^T of two chunks
+    # small chunks (fewer than 128 dH tiles) group dW and dH: at 512-token
+    # chunks, V = 32768, D = 2048, groups of 4 chunks (2048 columns): dlogits^T
+    # and h^T of four chunks, dH parts over four chunks' rows
     small = b(4096, 2048, 32768, BF16, 512, True, True, False, True)
-    expect_small = 2 * 512 * 32768 * 2 + 2 * 2048 * 512 * 2
+    expect_small = 4 * 512 * 32768 * 2 + 4 * 2048 * 512 * 2 + parts(32768) * 2048 * 2048 * 4
     assert expect_small <= small < expect_small + (1 << 20)
-    # dH alone: the vocab-major dlogits of one chunk
-    expect_dh = 2048 * 32000 * 2
+    # dH alone: the vocab-major dlogits of one chunk and the dH parts
+    expect_dh = 2048 * 32000 * 2 + parts(32000) * 2048 * 4096 * 4
     assert expect_dh <= only_dh < expect_dh + (1 << 20)
+    # V <= 16384: one part, no partial buffer; the schedule depends on the
+    # shapes only, so a dH-only call holds the 2048-token working chunk (4
+    # small chunks) that a call with dW runs
+    one = b(4096, 1024, 8192, BF16, 512, True, False, False, True)
+    assert 2048 * 8192 * 2 <= one < 2048 * 8192 * 2 + (1 << 20)
     # fp32 operands (and D % 8 != 0) keep the transposed path: W^T, both
     # dlogits layouts and h^T
     f32 = b(4096, 1024, 8192, F32, 512, True, True, False, True)
@@ -85,11 +94,44 @@ def test_workspace_queries():
     assert expect_odd <= odd < expect_odd + (1 << 20)
     # the single call at 16384 x 4096 x 32000, bf16, chunk 2048, FP32 table:
     # two pair buffers of numerators [V][2 x 2048], h^T of a pair, two chunks'
-    # forward partials and per-token arrays (about 540 MiB)
+    # forward partials, the dH parts of one chunk and per-token arrays (about
+    # 604 MiB)
     fq = llp.linear_logp_fwd_bwd_workspace_size
     single = fq(16384, 4096, 32000, BF16, 2048, True, True, False, True)
-    expect_single = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 250 * 2048 * 8
+    expect_single = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 250 * 2048 * 8 + 2 * 2048 * 4096 * 4
     assert expect_single <= single < expect_single + (1 << 20)
+    # 110-token chunks at V = 151936: groups of 7 chunks (a 256 MiB group
+    # buffer holds 7 x 112 columns) run as one 770-token working chunk: two
+    # group buffers, h^T of a group, two working chunks' forward partials, 10
+    # dH parts of a working chunk
+    big = fq(8192, 4096, 151936, BF16, 0, True, True, True, True)
+    expect_big = (2 * 151936 * 7 * 112 * 2 + 4096 * 7 * 112 * 2 + 2 * 1188 * 770 * 8 + 10 * 770 * 4096 * 4 +
+                  151936 * 4)
+    assert expect_big <= big < expect_big + (1 << 20)
+
+
+def test_bench_group_rule_matches_the_library():
+    """The benchmark's copy of the dW group rule (for its per-launch flop
+    accounting) agrees with the library's plan, seen through the workspace
+    sizes of shapes that differ only in it."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+
+    fq = llp.linear_logp_fwd_bwd_workspace_size
+    for N, D, V, C in ((8192, 4096, 151936, 110), (4096, 2048, 32768, 512), (16384, 4096, 32000, 2048),
+                       (3000, 512, 50000, 64), (2000, 1024, 4096, 100), (700, 256, 1031, 300)):
+        K = -(-N // C)
+        G = bench.dw_group(N, D, V, C, K, 2, True)
+        ld = -(-C // 8) * 8
+        with_dw = fq(N, D, V, BF16, C, False, True, False, True)
+        # dW alone: the group buffer [V][G ld] and h^T [D][G ld], the forward's
+        # partials of one working chunk (a whole group when G > 2) and
+        # per-token arrays
+        P = 2 * (-(-V // 256))
+        Cw = min(G * C, N) if G > 2 else C
+        core = V * G * ld * 2 + D * G * ld * 2 + P * Cw * 8
+        assert core <= with_dw < core + (1 << 20) + 4 * V + 16 * N + 4 * Cw, (N, D, V, C, G)
 
 
 @pytest.mark.parametrize("args,status", [

@@ -57,30 +57,30 @@ def test_bench_per_launch_kind_flops():
     """The bench's per-kind flop of the single call adds up to three N x V x D
     contractions for every chunking and schedule, and splits as the schedule
     says: with overlap only chunk 0's forward has a launch of its own; with
-    pairing the last launch holds the dW of the last pair (two chunks when K is
-    even, one when K is odd)."""
+    groups of G chunks the last launch holds the dW of the last group."""
     import sys
     sys.path.insert(0, ROOT)
     import bench
 
     D, V = 64, 1000
-    for N, C in ((16384, 2048), (300, 128), (300, 7), (4096, 512), (5, 5), (1000, 300)):
+    for N, C in ((16384, 2048), (300, 128), (300, 7), (4096, 512), (5, 5), (1000, 300), (8192, 110)):
         K = -(-N // C)
-        for overlap, pairing, pair_dh in ((False, False, False), (False, True, False), (True, False, False),
-                                          (True, True, False), (True, True, True), (False, True, True)):
-            f = bench.fused_step_flops(N, D, V, C, K, overlap, pairing, pair_dh)
-            assert sum(f.values()) == 6 * N * V * D, (N, C, overlap, pairing, pair_dh)
-            if not pair_dh:
-                last = min(C, N - (K - 1) * C)
+        ck = [min(C, N - k * C) for k in range(K)]
+        for overlap, G, gdh in ((False, 1, False), (False, 2, False), (True, 1, False), (True, 2, False),
+                                (True, 2, True), (False, 2, True), (True, 4, True), (True, 7, False),
+                                (False, 7, False), (True, 3, True)):
+            f = bench.fused_step_flops(N, D, V, C, K, overlap, G, gdh)
+            assert sum(f.values()) == 6 * N * V * D, (N, C, overlap, G, gdh)
+            if not gdh:
                 if overlap:
                     assert f["fwd_lse"] == 2 * min(C, N) * V * D
-                    if pairing and K >= 2:
-                        pair = last + (C if K % 2 == 0 else 0)
-                        assert f["dh_dw"] == 2 * last * V * D + 2 * pair * V * D
+                    if G > 1 and K >= 2:
+                        grp = sum(ck[K - 1 - (K - 1) % G:])  # the last group's tokens
+                        assert f["dh_dw"] == 2 * ck[-1] * V * D + 2 * grp * V * D
                 else:
                     assert f["fwd_lse"] == 2 * N * V * D and f.get("dh_dw_fwd", 0) == 0
-            elif overlap and K >= 3:
-                # pair dH: chunk 0's forward, and the even chunks' launches carry only
-                # the next (odd) chunk's forward
-                ck = [min(C, N - k * C) for k in range(K)]
-                assert f["fwd_lse"] == 2 * V * D * (ck[0] + sum(ck[j] for j in range(1, K, 2)))
+            elif overlap and K >= 3 and G > 1:
+                # group dH: chunk 0's forward, and the launches of chunks that do
+                # not end a group carry only the next chunk's forward
+                fwd_only = sum(ck[k + 1] for k in range(K - 1) if k % G != G - 1)
+                assert f["fwd_lse"] == 2 * V * D * (ck[0] + fwd_only)

@@ -439,3 +439,32 @@ def test_fused_masked_vocab_blocks(dt):
     assert_close(dW, rdW, *tg, "dW (masked)")
     assert_close(db, rdb, *tg, "db (masked)")
     assert bool((dW[512:] == 0).all()) and bool((db[512:] == 0).all())
+
+
+@pytest.mark.parametrize("chunk", [64, 60])
+def test_dw_groups_of_many_chunks(chunk):
+    """Small chunks accumulate dW once per group of G chunks (G = 32 at
+    64-token chunks: 2048 group columns): 2500 tokens in 40 or 42 chunks make a
+    full group and a partial one. Both paths (single call and two-call), FP32
+    table with bias, against the oracle; dH bitwise equal to the unchunked run
+    (64-token chunks also take dH once per group; 60-token chunks, whose
+    columns are not contiguous, per chunk); each path's dH is compared with its
+    own unchunked run (the two paths round the softmax part differently)."""
+    w = synth.LinearWorkload(f"groups_{chunk}", 2500, 136, 1031, "bf16", True, chunk, "normal")
+    d = synth.make_linear_t(w, DEV)
+    host = synth.make_linear_np(w)
+    rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True, True,
+                                      True)
+    tg = TOL["bf16"]["grad"]
+    ref = fused(w, d, chunk=w.N)
+    got = fused(w, d)
+    assert bits_equal(ref[2], got[2]) and bits_equal(ref[0], got[0])
+    assert_close(got[2], rdH, *tg, "dH")
+    assert_close(got[3], rdW, *tg, "dW (single call)")
+    assert_close(got[4], rdb, *tg, "db (single call)")
+    _, _, sdH, sdW, sdb = split(w, d)
+    _, _, sref, _, _ = split(w, d, chunk=w.N)
+    assert bits_equal(sref, sdH)  # the two-call path's own dH, unchunked
+    assert_close(sdH, rdH, *tg, "dH (two-call)")
+    assert_close(sdW, rdW, *tg, "dW (two-call)")
+    assert_close(sdb, rdb, *tg, "db (two-call)")
