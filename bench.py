@@ -196,7 +196,7 @@ def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
     """Chunks per dW contraction (G), the library's rule (its workspace plan):
     with an FP32 table, dW and K >= 2, the single call and (for small chunks:
     16-bit operands, fewer than 128 dH tiles) the two-call path accumulate dW
-    once per group of G chunks: G = 2, for small chunks up to 2048 group
+    once per group of G chunks: G = 2, for small chunks up to 4096 group
     columns and 256 MiB of group buffer, at most K."""
     few = esize == 2 and -(-C // 256) * -(-D // 256) < 128
     if not (table_f32 and K >= 2 and (fused or few)):
@@ -204,7 +204,7 @@ def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
     ld = -(-C // 8) * 8
     g = 2
     if few:
-        g = max(g, min(2048 // ld, (1 << 28) // (V * ld * esize)))
+        g = max(g, min(4096 // ld, (1 << 28) // (V * ld * esize)))
     return min(g, K)
 
 
@@ -384,7 +384,7 @@ def run_linear(w, args, torch, llp):
         "data": "synthetic (seeded counter-based generator; random-init weights)",
         "config": {"workload": w.name, "N": N, "D": D, "V": V, "chunk": C, "chunks": K,
                    "working_chunk": (Cw if args.path == "fused" else G_split[0]),
-                   "chunks_per_dW": (G if args.path == "fused" else G_split[2]), "dH_vocab_parts": -(-V // 16384),
+                   "chunks_per_dW": (G if args.path == "fused" else G_split[2]), "dH_vocab_parts": -(-V // 32768),
                    "bias": w.bias, "g": w.g, "dW_table": args.table, "outputs": "logp,lse,dH,dW" +
                    (",db" if w.bias else ""), "path": PATHS[args.path]},
         "pct_mfma_peak": main["pct_mfma_peak"],

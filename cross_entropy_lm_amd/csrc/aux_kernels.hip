@@ -628,10 +628,120 @@ __global__ __launch_bounds__(256) void onehot_rows_kernel(OnehotArgs<T> a) {
 // an FP32 dW table (blocks [0, no)), the target lists (next nl blocks), the
 // chunk's h transposed (next nt blocks) and the softmax gradient tiles (next
 // ns blocks). Each part is optional.
+// dH rows of a split contraction: the S parts summed in increasing order,
+// then the dH tile epilogue's operations (same expressions, same order): the
+// row factor s rowf (0 for a token that takes no part), the one-hot term
+// tcoef W[t] for a valid token, rounding to the output dtype. v8 (D % 8 ==
+// 0): 8 consecutive columns per thread with 16-byte loads, and 16-byte
+// stores where vec says the output rows are 16-byte aligned; otherwise one
+// column per thread. 256 threads per block.
+struct DhReduceArgs {
+  const float* part;
+  int64_t stride;
+  int S;
+  int64_t M, D;
+  int v8, vec;
+  EpiParams e;
+};
+
+inline int64_t dh_reduce_blocks(const DhReduceArgs& a) {
+  return a.part == nullptr ? 0 : (a.M * (a.v8 ? a.D / 8 : a.D) + 255) / 256;
+}
+
+template <typename T, bool kVec>
+__device__ __forceinline__ void dh_reduce_elems(int64_t q, const DhReduceArgs& a) {
+  constexpr int kCols = kVec ? 8 : 1;
+  const EpiParams& e = a.e;
+  const int64_t nq = a.D / kCols;
+  const int64_t m = q / nq;
+  if (m >= a.M) return;
+  const int64_t n = (q - m * nq) * kCols;
+  const float* pp = a.part + m * a.D + n;
+  float sv[kCols];
+  if constexpr (kVec) {
+    const float4 x = *reinterpret_cast<const float4*>(pp);
+    const float4 y = *reinterpret_cast<const float4*>(pp + 4);
+    sv[0] = x.x, sv[1] = x.y, sv[2] = x.z, sv[3] = x.w, sv[4] = y.x, sv[5] = y.y, sv[6] = y.z, sv[7] = y.w;
+    for (int i = 1; i < a.S; ++i) {
+      const float4 u = *reinterpret_cast<const float4*>(pp + (int64_t)i * a.stride);
+      const float4 v = *reinterpret_cast<const float4*>(pp + (int64_t)i * a.stride + 4);
+      sv[0] += u.x, sv[1] += u.y, sv[2] += u.z, sv[3] += u.w;
+      sv[4] += v.x, sv[5] += v.y, sv[6] += v.z, sv[7] += v.w;
+    }
+  } else {
+    sv[0] = pp[0];
+    for (int i = 1; i < a.S; ++i) sv[0] += pp[(int64_t)i * a.stride];
+  }
+  const int64_t tok = e.tok0 + m;
+  const int64_t tg = e.targets[tok];
+  const int64_t t = tg - e.v0;
+  const bool valid = tg >= 0 && tg < e.Vt && t >= 0 && t < e.V && e.g[tok] != 0.0f;
+  const float sc = e.scales[e.chunk].x;
+  const float fr = e.rowf == nullptr ? sc : sc * e.rowf[tok];
+  const float c = valid ? e.tcoef[tok] : 0.0f;
+  const T* w = static_cast<const T*>(e.W) + (valid ? t : 0) * e.ldW + n;
+  float o[kCols];
+#pragma unroll
+  for (int j = 0; j < kCols; ++j) {
+    // a zero factor (a token that takes no part) gives +0, whatever the sign of the sum
+    const float base = fr == 0.0f ? 0.0f : sv[j] * fr;
+    o[j] = valid ? fmaf(c, (float)w[j], base) : base;
+  }
+  if (e.out_dt == DT_F32) {
+    float* out = static_cast<float*>(e.out) + m * e.ldo + n;
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) out[j] = o[j];
+  } else {
+    T* out = static_cast<T*>(e.out) + m * e.ldo + n;
+    if constexpr (kVec && sizeof(T) == 2) {
+      if (a.vec) {
+        union {
+          T h[8];
+          uint4 u;
+        } pk;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pk.h[j] = (T)o[j];
+        *reinterpret_cast<uint4*>(out) = pk.u;
+        return;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kCols; ++j) out[j] = (T)o[j];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void dh_reduce_block(int64_t b, const DhReduceArgs& a) {
+  const int64_t q = b * 256 + threadIdx.x;
+  if (a.v8)
+    dh_reduce_elems<T, true>(q, a);
+  else
+    dh_reduce_elems<T, false>(q, a);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dh_reduce_kernel(DhReduceArgs a) {
+  dh_reduce_block<T>(blockIdx.x, a);
+}
+
+DhReduceArgs dh_reduce_args(const float* part, int64_t stride, int S, int64_t M, int64_t D, const EpiParams& e) {
+  DhReduceArgs a;
+  a.part = part;
+  a.stride = stride;
+  a.S = S;
+  a.M = M;
+  a.D = D;
+  a.v8 = D % 8 == 0;
+  a.vec = (reinterpret_cast<uintptr_t>(e.out) % 16 == 0) && (e.ldo % 8 == 0);
+  a.e = e;
+  return a;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(OnehotArgs<T> oa, int64_t no, ListArgs la, int64_t nl,
                                                          TransposeArgs<T> ta, int64_t tgx, int64_t nt,
-                                                         SoftmaxGradArgs<T> sa, int64_t sgx) {
+                                                         SoftmaxGradArgs<T> sa, int64_t sgx, int64_t ns,
+                                                         DhReduceArgs ra) {
   // the one-hot blocks come first: they are latency-bound and short, so the
   // memory-bound parts that follow run beside them
   // one LDS buffer for whichever part this block runs
@@ -653,10 +763,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(OnehotArgs<T> oa, int64
     return;
   }
   b -= nt;
-  if (sa.qflag != nullptr)
-    qfix_tile<T>(b % sgx, b / sgx, sa);
-  else
-    softmax_grad_tile<T>(b % sgx, b / sgx, sa, smem);
+  if (b < ns) {
+    if (sa.qflag != nullptr)
+      qfix_tile<T>(b % sgx, b / sgx, sa);
+    else
+      softmax_grad_tile<T>(b % sgx, b / sgx, sa, smem);
+    return;
+  }
+  b -= ns;
+  // the previous dH contraction's parts (memory-bound, like the rest)
+  dh_reduce_block<T>(b, ra);
 }
 
 __global__ void fill_kernel(uint32_t* __restrict__ p, int64_t nwords, uint32_t word) {
@@ -699,103 +815,22 @@ hipError_t db_t(const void* dSt, int64_t ldSt, int64_t V, int64_t C, const float
   return hipGetLastError();
 }
 
-// dH rows of a split contraction: the S parts summed in increasing order,
-// then the dH tile epilogue's operations (same expressions, same order): the
-// row factor s rowf (0 for a token that takes no part), the one-hot term
-// tcoef W[t] for a valid token, rounding to the output dtype. kVec (D % 8 ==
-// 0): 8 consecutive columns per thread with 16-byte loads, and 16-byte
-// stores where `vec` says the output rows are 16-byte aligned; otherwise one
-// column per thread.
-template <typename T, bool kVec>
-__global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int64_t stride, int S,
-                                                        int64_t M, int64_t D, EpiParams e, int vec) {
-  constexpr int kCols = kVec ? 8 : 1;
-  const int64_t nq = D / kCols;
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t m = q / nq;
-  if (m >= M) return;
-  const int64_t n = (q - m * nq) * kCols;
-  const float* pp = part + m * D + n;
-  float sv[kCols];
-  if constexpr (kVec) {
-    const float4 a = *reinterpret_cast<const float4*>(pp);
-    const float4 b = *reinterpret_cast<const float4*>(pp + 4);
-    sv[0] = a.x, sv[1] = a.y, sv[2] = a.z, sv[3] = a.w, sv[4] = b.x, sv[5] = b.y, sv[6] = b.z, sv[7] = b.w;
-    for (int i = 1; i < S; ++i) {
-      const float4 u = *reinterpret_cast<const float4*>(pp + (int64_t)i * stride);
-      const float4 v = *reinterpret_cast<const float4*>(pp + (int64_t)i * stride + 4);
-      sv[0] += u.x, sv[1] += u.y, sv[2] += u.z, sv[3] += u.w;
-      sv[4] += v.x, sv[5] += v.y, sv[6] += v.z, sv[7] += v.w;
-    }
-  } else {
-    sv[0] = pp[0];
-    for (int i = 1; i < S; ++i) sv[0] += pp[(int64_t)i * stride];
-  }
-  const int64_t tok = e.tok0 + m;
-  const int64_t tg = e.targets[tok];
-  const int64_t t = tg - e.v0;
-  const bool valid = tg >= 0 && tg < e.Vt && t >= 0 && t < e.V && e.g[tok] != 0.0f;
-  const float sc = e.scales[e.chunk].x;
-  const float fr = e.rowf == nullptr ? sc : sc * e.rowf[tok];
-  const float c = valid ? e.tcoef[tok] : 0.0f;
-  const T* w = static_cast<const T*>(e.W) + (valid ? t : 0) * e.ldW + n;
-  float o[kCols];
-#pragma unroll
-  for (int j = 0; j < kCols; ++j) {
-    // a zero factor (a token that takes no part) gives +0, whatever the sign of the sum
-    const float base = fr == 0.0f ? 0.0f : sv[j] * fr;
-    o[j] = valid ? fmaf(c, (float)w[j], base) : base;
-  }
-  if (e.out_dt == DT_F32) {
-    float* out = static_cast<float*>(e.out) + m * e.ldo + n;
-#pragma unroll
-    for (int j = 0; j < kCols; ++j) out[j] = o[j];
-  } else {
-    T* out = static_cast<T*>(e.out) + m * e.ldo + n;
-    if constexpr (kVec && sizeof(T) == 2) {
-      if (vec) {
-        union {
-          T h[8];
-          uint4 u;
-        } pk;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pk.h[j] = (T)o[j];
-        *reinterpret_cast<uint4*>(out) = pk.u;
-        return;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kCols; ++j) out[j] = (T)o[j];
-  }
-}
-
-template <typename T>
-hipError_t dh_reduce_t(const float* part, int64_t stride, int S, int64_t M, int64_t D, const EpiParams& e,
-                       hipStream_t s) {
-  const bool v8 = D % 8 == 0;
-  const int64_t n = M * (v8 ? D / 8 : D);
-  if ((n + 255) / 256 > INT32_MAX) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((n + 255) / 256);
-  const int vec = (reinterpret_cast<uintptr_t>(e.out) % 16 == 0) && (e.ldo % 8 == 0);
-  if (v8)
-    dh_reduce_kernel<T, true><<<grid, 256, 0, s>>>(part, stride, S, M, D, e, vec);
-  else
-    dh_reduce_kernel<T, false><<<grid, 256, 0, s>>>(part, stride, S, M, D, e, vec);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_dh_reduce(int dt, const float* part, int64_t stride, int S, int64_t M, int64_t D,
                             const EpiParams& e, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (S < 1) return hipErrorInvalidValue;
+  const DhReduceArgs a = dh_reduce_args(part, stride, S, M, D, e);
+  const int64_t nb = dh_reduce_blocks(a);
+  if (nb > INT32_MAX) return hipErrorInvalidValue;
   switch (dt) {
-    case DT_F32: return dh_reduce_t<float>(part, stride, S, M, D, e, s);
-    case DT_BF16: return dh_reduce_t<__bf16>(part, stride, S, M, D, e, s);
-    case DT_F16: return dh_reduce_t<_Float16>(part, stride, S, M, D, e, s);
+    case DT_F32: dh_reduce_kernel<float><<<(unsigned)nb, 256, 0, s>>>(a); break;
+    case DT_BF16: dh_reduce_kernel<__bf16><<<(unsigned)nb, 256, 0, s>>>(a); break;
+    case DT_F16: dh_reduce_kernel<_Float16><<<(unsigned)nb, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 hipError_t launch_lse_combine(const float2* partials, int64_t P, int64_t ldp, const float* zt,
@@ -879,7 +914,10 @@ hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
   sa.qflag = c.qflag;  // per-token mode: the fixup of flagged columns instead of the gradient pass
   const int64_t sgx = c.qflag != nullptr ? (c.V + 1023) / 1024 : (c.V + 63) / 64;
   const int64_t ns = c.qt != nullptr ? sgx * ((c.C + 63) / 64) : 0;
-  const int64_t total = no + nl + nt + ns;
+  const DhReduceArgs ra = c.rd_part != nullptr ? dh_reduce_args(c.rd_part, c.rd_stride, c.rd_S, c.rd_M, c.rd_D, c.rd_ep)
+                                               : DhReduceArgs{};
+  const int64_t nr = dh_reduce_blocks(ra);
+  const int64_t total = no + nl + nt + ns + nr;
   if (total == 0) return hipSuccess;
   if (total > INT32_MAX) {  // one launch per part
     if (no) onehot_rows_kernel<T><<<(unsigned)no, 256, 0, s>>>(oa);
@@ -887,14 +925,18 @@ hipError_t chunk_prep_t(const ChunkPrep& c, hipStream_t s) {
     if (nt) transpose_kernel<T><<<dim3((unsigned)tgx, (unsigned)(nt / tgx)), 256, 0, s>>>(ta);
     if (ns && c.qflag != nullptr) return hipErrorInvalidValue;  // the fixup runs in the joint launch only
     if (ns) softmax_grad_kernel<T><<<dim3((unsigned)sgx, (unsigned)(ns / sgx)), 256, 0, s>>>(sa);
+    if (nr) {
+      if (nr > INT32_MAX) return hipErrorInvalidValue;
+      dh_reduce_kernel<T><<<(unsigned)nr, 256, 0, s>>>(ra);
+    }
     return hipGetLastError();
   }
-  chunk_prep_kernel<T><<<(unsigned)total, 256, 0, s>>>(oa, no, la, nl, ta, tgx, nt, sa, sgx);
+  chunk_prep_kernel<T><<<(unsigned)total, 256, 0, s>>>(oa, no, la, nl, ta, tgx, nt, sa, sgx, ns, ra);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_prep(int dt, const ChunkPrep& c, hipStream_t s) {
-  if (c.C == 0 && (c.table == nullptr || c.oh_C == 0)) return hipSuccess;
+  if (c.C == 0 && (c.table == nullptr || c.oh_C == 0) && c.rd_part == nullptr) return hipSuccess;
   switch (dt) {
     case DT_F32: return chunk_prep_t<float>(c, s);
     case DT_BF16: return chunk_prep_t<__bf16>(c, s);

@@ -760,6 +760,28 @@ __device__ __forceinline__ void wait_vm() {
 // expcnt 7 mean no wait on those counters)
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
+// Scheduling of one MFMA step: the next step's kR fragment reads (into the
+// other fragment registers) spread among this step's kM MFMAs, ceil(kR / kM)
+// reads after each MFMA, so that each read has a whole step to land and the two
+// fragment sets stay distinct registers (the scheduler would otherwise sink
+// the reads behind most of the MFMAs and reuse their source registers).
+template <int kPer, int kLeft>
+__device__ __forceinline__ void sched_pairs() {
+  if constexpr (kLeft > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // then kPer DS reads
+    sched_pairs<kPer, kLeft - 1>();
+  }
+}
+template <int kR, int kM>
+__device__ __forceinline__ void interleave_reads_mfma() {
+  constexpr int kPer = (kR + kM - 1) / kM;  // reads after each of the first MFMAs
+  static_assert(kR % kPer == 0 && kR / kPer <= kM, "reads divide evenly");
+  constexpr int kPairs = kR / kPer;
+  sched_pairs<kPer, kPairs>();
+  if constexpr (kM > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kM - kPairs, 0);
+}
+
 // Stage k covers 128 bytes of K (four MFMA steps). Its A tile is unit 2k and
 // its B tile unit 2k + 1; unit u lives in slot u % 5. Every wave moves a
 // quarter-column of 8-row pieces of every unit from global memory to LDS by
@@ -865,18 +887,26 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
   const int64_t nst = (Kp + BKE - 1) / BKE;
 
   // pieces [j0, j1) of unit (stage s, operand O) into `slot`
-  auto issue = [&](char* slot, int64_t s, auto Ov, int j0 = 0, int j1 = kLoads) {
+  // per-stage byte step of each operand (K-row-major: BKE K rows; else kSB
+  // bytes of every row) and the part's K, all below 2^31 (checked by the host)
+  const uint32_t kstA = kMn ? (uint32_t)(BKE * p.lda * (int64_t)sizeof(T)) : (uint32_t)kSB;
+  const uint32_t kstB = kMn ? (uint32_t)(BKE * p.ldb * (int64_t)sizeof(T)) : (uint32_t)kSB;
+  const int Kp32 = (int)Kp;
+  auto issue = [&](char* slot, int64_t s64, auto Ov, int j0 = 0, int j1 = kLoads) {
     constexpr int O = decltype(Ov)::value;
+    const int s = (int)s64;
+    const uint32_t sofs = (uint32_t)s * (O ? kstB : kstA);
+    const int klim = Kp32 - s * BKE;  // K elements of this stage that exist (uniform)
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       if (j < j0 || j >= j1) continue;
       uint32_t vo = (O ? voB : voA) + (uint32_t)j * (O ? strB : strA);
       uint32_t off;
       if constexpr (kMn) {  // K rows past K lie past the buffer's end and read as 0
-        off = vo + (uint32_t)(s * BKE * (O ? p.ldb : p.lda) * (int64_t)sizeof(T));
+        off = vo + sofs;
       } else {
         if (j & 1) vo += dodd;
-        off = (s * BKE + ((j & 1) ? kel_odd : kel) < Kp) ? vo + (uint32_t)(s * kSB) : 0xFFFFFFF0u;
+        off = (((j & 1) ? kel_odd : kel) < klim) ? vo + sofs : 0xFFFFFFF0u;
       }
       // K-row-major: the 1 KiB block of instruction j holds K rows 2w + 2 nw j, +1
       char* const dst = kMn ? slot + wave * 1024 + j * (kThreads / 64) * 1024 : slot + lds_off + j * kRowsPerLoad * kSB;
@@ -940,6 +970,9 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma_step((T*)nullptr, fa[mi], fb[ni], acc[mi][ni]);
   };
+  // LDS read instructions of one step's fragments: one 16-byte read per
+  // block, or two transposed 8-byte reads per block (K-row-major)
+  constexpr int kReadsPerStep = (kMn ? 2 : 1) * (MI + NI);
   using O_A = std::integral_constant<int, 0>;
   using O_B = std::integral_constant<int, 1>;
   u32x4 fa[2][MI], fb[2][NI];  // by step parity
@@ -958,6 +991,7 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
       // DMA keeps the address queues from filling at the barrier
       constexpr int kHalf = kLoads / 2;
       if (j < 2 && k >= 1 && k + 2 < nst) issue(buf[(2 * I + 4) % kNS], k + 2, O_A{}, j * kHalf, (j + 1) * kHalf);
+      if (j + 1 < kSteps) interleave_reads_mfma<kReadsPerStep, MI * NI>();
     }
     // this wave's pieces of stage k + 1 have landed (only the A tile of stage
     // k + 2 may remain in flight) and its reads of stage k have completed
@@ -972,6 +1006,7 @@ __device__ __forceinline__ void mainloop_dma(const GemmProblem& p, int64_t m0, i
     // the last step of stage k multiplies while the next stage's first
     // fragments come from LDS (after the barrier every wave reads at once)
     mma(fa[(kSteps - 1) & 1], fb[(kSteps - 1) & 1]);
+    if (k + 1 < nst) interleave_reads_mfma<kReadsPerStep, MI * NI>();
   };
 
   // units 0 .. 4: stages 0 and 1 and the A tile of stage 2

@@ -218,6 +218,13 @@ struct ChunkPrep {
   int chunk;
   void* dS;
   int64_t ldS;
+  // the previous dH contraction's reduction (as launch_dh_reduce), when
+  // rd_part != null: it runs in the same launch, beside the parts above
+  const float* rd_part;
+  int64_t rd_stride;
+  int rd_S;
+  int64_t rd_M, rd_D;
+  EpiParams rd_ep;
 };
 hipError_t launch_chunk_prep(int dt, const ChunkPrep& c, hipStream_t s);
 

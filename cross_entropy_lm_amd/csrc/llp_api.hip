@@ -428,6 +428,23 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   // epilogue (an FP32 table takes its one-hot rows in the chunk preparation)
   const bool lists = want_db || (want_dW && dW_dtype != LLP_F32);
 
+  // A split dH contraction's reduction runs in the next chunk's preparation
+  // launch when there is one (memory-bound work beside memory-bound work, one
+  // launch fewer), else on its own before the partial buffer is reused.
+  struct Pending {
+    bool on = false;
+    const float* part = nullptr;
+    int64_t stride = 0, M = 0;
+    int S = 1;
+    EpiParams ep = {};
+  } pend;
+  auto flush = [&]() -> int {
+    if (pend.on) {
+      pend.on = false;
+      LLP_LAUNCH(LLP_K_DH_REDUCE, launch_dh_reduce(dtype, pend.part, pend.stride, pend.S, pend.M, D, pend.ep, s));
+    }
+    return LLP_OK;
+  };
   for (int64_t k = 0; k < K; ++k) {
     const int64_t c0 = k * C;
     const int64_t Ck = (N - c0 < C) ? (N - c0) : C;
@@ -509,8 +526,18 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
         cp.qflag = qflag + c0;
       }
     }
-    if (cp.head != nullptr || cp.ht != nullptr || cp.qt != nullptr || cp.table != nullptr)
+    if (cp.head != nullptr || cp.ht != nullptr || cp.qt != nullptr || cp.table != nullptr) {
+      if (pend.on) {  // the previous dH's reduction rides in this launch
+        cp.rd_part = pend.part;
+        cp.rd_stride = pend.stride;
+        cp.rd_S = pend.S;
+        cp.rd_M = pend.M;
+        cp.rd_D = D;
+        cp.rd_ep = pend.ep;
+        pend.on = false;
+      }
       LLP_LAUNCH(fused ? LLP_K_DLOGITS : LLP_K_TRANSPOSE, launch_chunk_prep(dtype, cp, s));
+    }
     if (want_db)
       LLP_LAUNCH(LLP_K_SMALL, launch_db_accum(dtype, dSt, ldq, V, Ck, scales, sidx(k), head, next, targets, g, tcoef,
                               c0, v0, Vt, db, dW_dtype, s, qtok ? cq + c0 : nullptr));
@@ -610,6 +637,11 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.scales = scales;
       pw.ep.chunk = sidx(k);
     }
+    // the partial buffer is about to be rewritten: its previous sums must be reduced
+    if (do_dh && ph.kparts > 1) {
+      st = flush();
+      if (st != LLP_OK) return st;
+    }
     if (overlap && k + 1 < K) {
       // with the next chunk's forward tiles, then that chunk's combine
       const GemmProblem pf = fwd_problem(k + 1);
@@ -621,9 +653,17 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     } else if (do_dh || do_dw) {
       LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, do_dh ? &ph : nullptr, do_dw ? &pw : nullptr, s));
     }
-    if (do_dh && ph.kparts > 1)
-      LLP_LAUNCH(LLP_K_DH_REDUCE, launch_dh_reduce(dtype, ph.ep.dhp, ph.ep.dhp_stride, ph.kparts, hM, D, ph.ep, s));
+    if (do_dh && ph.kparts > 1) {
+      pend.on = true;
+      pend.part = ph.ep.dhp;
+      pend.stride = ph.ep.dhp_stride;
+      pend.S = ph.kparts;
+      pend.M = hM;
+      pend.ep = ph.ep;
+    }
   }
+  st = flush();
+  if (st != LLP_OK) return st;
   if (store_first && K == fdw + 1 && dW_dtype == LLP_F32) {
     // the contraction that stored the table was the last one: the one-hot
     // rows of every chunk follow it

@@ -15,7 +15,7 @@ constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;  // one workgroup per row /
 constexpr int64_t kTile = kTileM;               // contraction tile edge (M and N)
 static_assert(kTileM == kTileN, "square tiles");
 constexpr int64_t kAlign = 256;                 // workspace region alignment (bytes)
-constexpr int64_t kGroupCols = 2048;            // small chunks: columns of a dW group at most
+constexpr int64_t kGroupCols = 4096;            // small chunks: columns of a dW group at most
 constexpr int64_t kGroupBytes = int64_t(1) << 28;  // ... and bytes of one group buffer at most
 
 inline bool dtype_ok(int dt) { return dt == LLP_F32 || dt == LLP_BF16 || dt == LLP_F16; }
@@ -104,7 +104,7 @@ struct BwdPlan {
   // dW is accumulated once per group of G consecutive chunks (G = 1: per
   // chunk): the single call with dW and K >= 2, and the two-call path for
   // small chunks (fewer than 128 dH tiles). G = 2, or for small chunks up to
-  // 2048 group columns while one group buffer stays within 256 MiB.
+  // 4096 group columns while one group buffer stays within 256 MiB.
   int64_t G = 1;
   // Working chunk. With more than two small chunks per group and the layout
   // without W^T, a group is processed as one chunk of Cw = min(G C, N)
@@ -254,7 +254,8 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   if (want_dW || want_db || fused || p->kmajor) {
     if (!mul_ok(V, p->ldP, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_dSt = L.add(n);
-    if (fused && p->kmajor && p->K >= 2) {
+    // (only when the working schedule has two chunks or more)
+    if (fused && p->kmajor && ceil_div(N, p->Cw) >= 2) {
       p->off_dSt2 = L.add(n);
       if (!mul_ok(p->P, p->Cw, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
       p->off_part2 = L.add(n);

@@ -25,6 +25,6 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin to 8 XCDs
 // own whose fp32 partial is added in increasing part order: a chunk's few dH
 // tiles then spread over many CUs, and a token's dH does not depend on the
 // chunking or the batch.
-constexpr long long kDhPart = 16384;
+constexpr long long kDhPart = 32768;
 static_assert(kTileM % (32 * kWaveM) == 0 && kTileN % (32 * kWaveN) == 0, "wave tile must be 32-aligned");
 }  // namespace llp

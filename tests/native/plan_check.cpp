@@ -72,12 +72,12 @@ static void check_layout(int64_t N, int64_t D, int64_t V, int dt, int64_t chunk,
   // 2048-column and 256 MiB caps, never more than the chunks
   EXPECT(p.G >= 1 && p.G <= (p.K > 1 ? p.K : 1) && p.ldP >= p.G * p.ldSt);
   EXPECT(p.ldP == (p.G * p.ldSt > round_up(p.Cw, 8) ? p.G * p.ldSt : round_up(p.Cw, 8)));
-  if (p.G > 2) EXPECT(p.G * p.ldSt <= 2048 && V * p.ldP * esize(dt) <= (int64_t(1) << 28));
+  if (p.G > 2) EXPECT(p.G * p.ldSt <= 4096 && V * p.ldP * esize(dt) <= (int64_t(1) << 28));
   if (!dw) EXPECT(p.G == 1);
   // the layout holds only what the requested outputs need
   EXPECT(p.kmajor == (dh && esize(dt) == 2 && D % 8 == 0 && (p.off_Wt < 0)));
   if (p.kmajor) EXPECT(p.off_Wt < 0 && p.off_dS < 0 && p.off_dSt >= 0);
-  if (dh) EXPECT(p.dh_parts == (V + 16383) / 16384);
+  if (dh) EXPECT(p.dh_parts == (V + 32767) / 32768);
   if (dh) EXPECT(p.dh_rows == p.C || p.dh_rows == p.G * p.C || p.dh_rows == p.Cw);
   // the working chunk: the chunk, or a whole group of more than two chunks (at most N tokens)
   // (Cw does not depend on which outputs are requested: G is the group of the dW schedule)

@@ -65,25 +65,29 @@ def test_workspace_queries():
     assert only_dh < full and only_dw <= full and no_lse > full
     # 16-bit operands with D % 8 == 0: dH reads dlogits^T and W as stored, so
     # the chunk workspace is dlogits^T plus h^T of one chunk (no W^T, no
-    # token-major dlogits: nothing the requested outputs do not need), plus
-    # the fp32 sums of dH's ceil(V / 16384) vocabulary parts (2 at V = 32000)
-    parts = lambda V: -(-V // 16384)  # noqa: E731
-    expect = 2048 * 32000 * 2 + 4096 * 2048 * 2 + parts(32000) * 2048 * 4096 * 4
+    # token-major dlogits: nothing the requested outputs do not need); with
+    # more than one vocabulary part of 32768 rows, the parts' fp32 sums too
+    parts = lambda V: -(-V // 32768)  # noqa: E731
+    dhp = lambda V, rows, D: parts(V) * rows * D * 4 if parts(V) > 1 else 0  # noqa: E731
+    expect = 2048 * 32000 * 2 + 4096 * 2048 * 2 + dhp(32000, 2048, 4096)
     assert expect <= full < expect + (1 << 20)
-    # small chunks (fewer than 128 dH tiles) group dW and dH: at 512-token
-    # chunks, V = 32768, D = 2048, groups of 4 chunks (2048 columns): dlogits^T
-    # and h^T of four chunks, dH parts over four chunks' rows
+    # small chunks (fewer than 128 dH tiles) group dW: at 512-token chunks,
+    # V = 32768, D = 2048, groups of 8 chunks (4096 columns), which run as one
+    # 4096-token working chunk: dlogits^T and h^T of the working chunk
     small = b(4096, 2048, 32768, BF16, 512, True, True, False, True)
-    expect_small = 4 * 512 * 32768 * 2 + 4 * 2048 * 512 * 2 + parts(32768) * 2048 * 2048 * 4
+    expect_small = 4096 * 32768 * 2 + 2048 * 4096 * 2 + dhp(32768, 4096, 2048)
     assert expect_small <= small < expect_small + (1 << 20)
-    # dH alone: the vocab-major dlogits of one chunk and the dH parts
-    expect_dh = 2048 * 32000 * 2 + parts(32000) * 2048 * 4096 * 4
+    # dH alone: the vocab-major dlogits of one chunk
+    expect_dh = 2048 * 32000 * 2 + dhp(32000, 2048, 4096)
     assert expect_dh <= only_dh < expect_dh + (1 << 20)
-    # V <= 16384: one part, no partial buffer; the schedule depends on the
-    # shapes only, so a dH-only call holds the 2048-token working chunk (4
-    # small chunks) that a call with dW runs
+    # the schedule depends on the shapes only, so a dH-only call holds the
+    # 4096-token working chunk (8 small chunks) that a call with dW runs
     one = b(4096, 1024, 8192, BF16, 512, True, False, False, True)
-    assert 2048 * 8192 * 2 <= one < 2048 * 8192 * 2 + (1 << 20)
+    assert 4096 * 8192 * 2 <= one < 4096 * 8192 * 2 + (1 << 20)
+    # 151936 rows: 5 parts of dH sums
+    bigdh = b(2048, 1024, 151936, BF16, 2048, True, False, False, True)
+    expect_bigdh = 2048 * 151936 * 2 + 5 * 2048 * 1024 * 4
+    assert expect_bigdh <= bigdh < expect_bigdh + (1 << 20)
     # fp32 operands (and D % 8 != 0) keep the transposed path: W^T, both
     # dlogits layouts and h^T
     f32 = b(4096, 1024, 8192, F32, 512, True, True, False, True)
@@ -94,18 +98,17 @@ def test_workspace_queries():
     assert expect_odd <= odd < expect_odd + (1 << 20)
     # the single call at 16384 x 4096 x 32000, bf16, chunk 2048, FP32 table:
     # two pair buffers of numerators [V][2 x 2048], h^T of a pair, two chunks'
-    # forward partials, the dH parts of one chunk and per-token arrays (about
-    # 604 MiB)
+    # forward partials and per-token arrays (about 540 MiB)
     fq = llp.linear_logp_fwd_bwd_workspace_size
     single = fq(16384, 4096, 32000, BF16, 2048, True, True, False, True)
-    expect_single = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 250 * 2048 * 8 + 2 * 2048 * 4096 * 4
+    expect_single = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 250 * 2048 * 8
     assert expect_single <= single < expect_single + (1 << 20)
     # 110-token chunks at V = 151936: groups of 7 chunks (a 256 MiB group
     # buffer holds 7 x 112 columns) run as one 770-token working chunk: two
-    # group buffers, h^T of a group, two working chunks' forward partials, 10
+    # group buffers, h^T of a group, two working chunks' forward partials, 5
     # dH parts of a working chunk
     big = fq(8192, 4096, 151936, BF16, 0, True, True, True, True)
-    expect_big = (2 * 151936 * 7 * 112 * 2 + 4096 * 7 * 112 * 2 + 2 * 1188 * 770 * 8 + 10 * 770 * 4096 * 4 +
+    expect_big = (2 * 151936 * 7 * 112 * 2 + 4096 * 7 * 112 * 2 + 2 * 1188 * 770 * 8 + 5 * 770 * 4096 * 4 +
                   151936 * 4)
     assert expect_big <= big < expect_big + (1 << 20)
 

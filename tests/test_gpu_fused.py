@@ -443,14 +443,14 @@ def test_fused_masked_vocab_blocks(dt):
 
 @pytest.mark.parametrize("chunk", [64, 60])
 def test_dw_groups_of_many_chunks(chunk):
-    """Small chunks accumulate dW once per group of G chunks (G = 32 at
-    64-token chunks: 2048 group columns): 2500 tokens in 40 or 42 chunks make a
-    full group and a partial one. Both paths (single call and two-call), FP32
-    table with bias, against the oracle; dH bitwise equal to the unchunked run
-    (64-token chunks also take dH once per group; 60-token chunks, whose
-    columns are not contiguous, per chunk); each path's dH is compared with its
+    """Small chunks accumulate dW once per group of G chunks, and with an FP32
+    table a group runs as one working chunk. At V = 65536 the 256 MiB group
+    buffer caps G at 32 chunks of 64 columns (2048 tokens at chunk 64, 1920 at
+    chunk 60), so 2500 tokens make a full working chunk and a partial one (and
+    dH sums two vocabulary parts). Both paths (single call and two-call), FP32
+    table with bias, against the oracle; each path's dH bitwise equal to its
     own unchunked run (the two paths round the softmax part differently)."""
-    w = synth.LinearWorkload(f"groups_{chunk}", 2500, 136, 1031, "bf16", True, chunk, "normal")
+    w = synth.LinearWorkload(f"groups_{chunk}", 2500, 136, 65536, "bf16", True, chunk, "normal")
     d = synth.make_linear_t(w, DEV)
     host = synth.make_linear_np(w)
     rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True, True,
@@ -468,3 +468,31 @@ def test_dw_groups_of_many_chunks(chunk):
     assert_close(sdH, rdH, *tg, "dH (two-call)")
     assert_close(sdW, rdW, *tg, "dW (two-call)")
     assert_close(sdb, rdb, *tg, "db (two-call)")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_dh_vocabulary_parts(dt):
+    """dH sums the vocabulary in fixed parts of 32768 rows whose fp32 sums are
+    added in increasing order (V = 70000: parts of 32768, 32768 and 4464 rows).
+    Both paths against the oracle (dH, dW, db, logp); each path's dH bitwise
+    the same at every chunking (the parts depend on V alone); bf16 also with
+    D % 8 != 0 (the layout with a transposed W, split the same way)."""
+    for D in ((136, 100) if dt == "bf16" else (136,)):
+        w = synth.LinearWorkload(f"parts_{dt}_{D}", 300, D, 70000, dt, True, 128, "normal")
+        d = synth.make_linear_t(w, DEV)
+        host = synth.make_linear_np(w)
+        rlogp, _ = O.linear_logp_fwd(host["h64"], host["W64"], host["b64"], host["t"])
+        rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True,
+                                          True, True)
+        tl, tg = TOL[dt]["logp"], TOL[dt]["grad"]
+        ref_f = fused(w, d, chunk=w.N)
+        ref_s = split(w, d, chunk=w.N)
+        for chunk in (128, 64, 0):
+            f_out = fused(w, d, chunk=chunk)
+            s_out = split(w, d, chunk=chunk)
+            assert bits_equal(f_out[2], ref_f[2]) and bits_equal(s_out[2], ref_s[2]), (D, chunk)
+            for (logp, _, dH, dW, db), n in ((f_out, "single call"), (s_out, "two-call")):
+                assert_close(logp, rlogp, *tl, f"logp {n} D={D} chunk {chunk}")
+                assert_close(dH, rdH, *tg, f"dH {n} D={D} chunk {chunk}")
+                assert_close(dW, rdW, *tg, f"dW {n} D={D} chunk {chunk}")
+                assert_close(db, rdb, *tg, f"db {n} D={D} chunk {chunk}")
