@@ -195,13 +195,16 @@ def kernel_table(tr, steps, step_flops):
 def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
     """Chunks per dW contraction (G), the library's rule (its workspace plan):
     with an FP32 table, dW and K >= 2, the single call and (for small chunks:
-    16-bit operands, fewer than 128 dH tiles) the two-call path accumulate dW
-    once per group of G chunks: G = 2, for small chunks up to 4096 group
-    columns and 256 MiB of group buffer, at most K."""
+    16-bit operands, fewer than 128 dH tiles; or 16-bit operands with
+    D % 8 == 0) the two-call path accumulate dW once per group of G chunks:
+    G = 2, for small chunks up to 4096 group columns and 256 MiB of group
+    buffer, at most K."""
     few = esize == 2 and -(-C // 256) * -(-D // 256) < 128
-    if not (table_f32 and K >= 2 and (fused or few)):
-        return 1
     ld = -(-C // 8) * 8
+    lim = 0x7FFFFFF0
+    pairable = esize == 2 and D % 8 == 0 and V * D * esize < lim and V * 2 * ld * esize < lim
+    if not (table_f32 and K >= 2 and (fused or few or pairable)):
+        return 1
     g = 2
     if few:
         g = max(g, min(4096 // ld, (1 << 28) // (V * ld * esize)))
@@ -225,17 +228,20 @@ def schedule(N, D, V, C, K, esize, fused, table_f32=True):
     return C, K, G, G > 1 and small and kmajor
 
 
-def fused_step_flops(N, D, V, C, K, overlap, G=1, group_dh=False):
-    """Algorithmic flop per step of each contraction launch kind of the single
-    call: chunk k's logits tile, dH and (its share of) dW each cost 2 C_k V D.
-    With overlap, chunk k + 1's forward tiles ride in chunk k's dH / dW launch
-    (dh_dw_fwd) and only chunk 0's forward has a launch of its own; with
-    groups of G chunks, the dW of a group runs in the launch of its last chunk;
-    with group_dh (small chunks) the dH of a group runs there too, and a
-    launch left with neither dH nor dW is a forward-only launch (fwd_lse)."""
+def chunk_step_flops(N, D, V, C, K, overlap, G=1, group_dh=False, fused=True):
+    """Algorithmic flop per step of each contraction launch kind of the
+    chunked part of a path: chunk k's logits tile (the single call's forward,
+    fwd_lse; the backward's dlogits recompute, dlogits), dH and (its share of)
+    dW each cost 2 C_k V D. With overlap, chunk k + 1's logits tiles ride in
+    chunk k's dH / dW launch (dh_dw_fwd; dh_dw_dlogits) and only chunk 0's
+    logits tile has a launch of its own; with groups of G chunks, the dW of a
+    group runs in the launch of its last chunk; with group_dh (small chunks)
+    the dH of a group runs there too, and a launch left with neither dH nor
+    dW carries logits tiles only."""
     ck = [min(C, N - k * C) for k in range(K)]
     f = 2 * V * D
-    out = {"fwd_lse": 0, "dh_dw": 0, "dh_dw_fwd": 0}
+    lk, ok = ("fwd_lse", "dh_dw_fwd") if fused else ("dlogits", "dh_dw_dlogits")
+    out = {lk: 0, "dh_dw": 0, ok: 0}
     for k in range(K):
         kg = k - k % G
         end = k % G == G - 1 or k == K - 1
@@ -244,17 +250,30 @@ def fused_step_flops(N, D, V, C, K, overlap, G=1, group_dh=False):
         dh = f * grp if group_dh else f * ck[k]
         if overlap:
             if k == 0:
-                out["fwd_lse"] += f * ck[0]
+                out[lk] += f * ck[0]
             if k + 1 < K:
                 if dh == 0 and dw == 0:
-                    out["fwd_lse"] += f * ck[k + 1]
+                    out[lk] += f * ck[k + 1]
                 else:
-                    out["dh_dw_fwd"] += dh + dw + f * ck[k + 1]
+                    out[ok] += dh + dw + f * ck[k + 1]
             else:
                 out["dh_dw"] += dh + dw
         else:
-            out["fwd_lse"] += f * ck[k]
+            out[lk] += f * ck[k]
             out["dh_dw"] += dh + dw
+    return out
+
+
+def fused_step_flops(N, D, V, C, K, overlap, G=1, group_dh=False):
+    """Contraction flop per launch kind of the single call (6 V D per token)."""
+    return chunk_step_flops(N, D, V, C, K, overlap, G, group_dh, fused=True)
+
+
+def split_step_flops(N, D, V, C, K, overlap, G=1, group_dh=False):
+    """Contraction flop per launch kind of linear_logp_fwd (one forward over
+    the batch, fwd_lse) then linear_logp_bwd (8 V D per token)."""
+    out = chunk_step_flops(N, D, V, C, K, overlap, G, group_dh, fused=False)
+    out["fwd_lse"] = 2 * N * V * D
     return out
 
 
@@ -327,10 +346,11 @@ def run_linear(w, args, torch, llp):
     esz = 4 if w.dtype == "f32" else 2
     Cw, Kw, G, group_dh = schedule(N, D, V, C, K, esz, True, args.table == "f32")
     overlap = w.dtype in ("bf16", "f16") and Kw >= 2 and D % 8 == 0
-    G_split = schedule(N, D, V, C, K, esz, False, args.table == "f32")
-    split_flops = {"fwd_lse": 2 * N * V * D, "dlogits": 2 * N * V * D, "dh_dw": 4 * N * V * D}
+    # the backward of the two-call path overlaps alike (the next chunk's dlogits recompute)
+    sCw, sKw, sG, s_gdh = schedule(N, D, V, C, K, esz, False, args.table == "f32")
+    s_overlap = w.dtype in ("bf16", "f16") and sKw >= 2 and D % 8 == 0
     for name, step, sf in (
-            ("split", split_step, split_flops),
+            ("split", split_step, split_step_flops(N, D, V, sCw, sKw, s_overlap, sG, s_gdh)),
             ("fused", fused_step, fused_step_flops(N, D, V, Cw, Kw, overlap, G, group_dh))):
         log(f"{name}: warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
         ms, tr = time_steps(step, args, torch, llp, stream)

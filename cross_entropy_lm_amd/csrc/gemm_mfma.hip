@@ -1120,10 +1120,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmP
 }
 
 // One chunk's dH (K-row-major operands) and dW tiles together with the next
-// chunk's forward tiles (EPI_LSE_Q), which write their own numerator and
-// partial buffers: the launch tails overlap. The dW tiles, the shortest, come
-// last.
-template <typename T, int kAcc>
+// chunk's logits tiles, which write their own buffers: the single call's
+// forward (EPI_LSE_Q: numerators and partials) or the backward's dlogits
+// recompute (EPI_DLOGITS: dlogits^T). The launch tails overlap. The dW tiles,
+// the shortest, come last.
+template <typename T, int kAcc, int E2>
 __global__ __launch_bounds__(kThreads, 1) void gemm3_kernel(GemmProblem p0, GemmProblem p1, GemmProblem p2,
                                                              int nt0, int nt2) {
   __shared__ __attribute__((aligned(16))) char st0[kStageArr];
@@ -1136,7 +1137,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm3_kernel(GemmProblem p0, Gemm
   if (bid < nt0) {
     tile_run<T, EPI_STORE, true, true, kAcc>(p0, xcd_remap(bid, nt0), buf);
   } else if (bid < nt0 + nt2) {
-    tile_run<T, EPI_LSE_Q, true, false, kAcc>(p2, xcd_remap(bid - nt0, nt2), buf);
+    tile_run<T, E2, true, false, kAcc>(p2, xcd_remap(bid - nt0, nt2), buf);
   } else {
     tile_run<T, EPI_ACCUM, true, false, kAcc>(p1, xcd_remap(bid - nt0 - nt2, (int)gridDim.x - nt0 - nt2), buf);
   }
@@ -1153,11 +1154,16 @@ hipError_t launch3_t(const GemmProblem& p0, const GemmProblem* p1, const GemmPro
     const GemmProblem& b = p1 ? *p1 : empty;
     const int acc = p1 == nullptr ? ACC_FAST : !p1->ep.tab_fast ? ACC_ANY : p1->ep.tab_store ? ACC_FRESH : ACC_FAST;
     if (!p0.mn || !p0.dma || !p2.dma || (p1 && !p1->dma) || acc == ACC_ANY || p0.epi != EPI_STORE ||
-        p2.epi != EPI_LSE_Q || p2.kparts > 1 || (p1 && p1->kparts > 1))
+        (p2.epi != EPI_LSE_Q && p2.epi != EPI_DLOGITS) || p2.kparts > 1 || (p1 && p1->kparts > 1))
       return hipErrorInvalidValue;
     dim3 grid(nt0 + nt1 + nt2), block(kThreads);
-    if (acc == ACC_FAST) gemm3_kernel<T, ACC_FAST><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
-    else gemm3_kernel<T, ACC_FRESH><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+    if (p2.epi == EPI_LSE_Q) {
+      if (acc == ACC_FAST) gemm3_kernel<T, ACC_FAST, EPI_LSE_Q><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+      else gemm3_kernel<T, ACC_FRESH, EPI_LSE_Q><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+    } else {
+      if (acc == ACC_FAST) gemm3_kernel<T, ACC_FAST, EPI_DLOGITS><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+      else gemm3_kernel<T, ACC_FRESH, EPI_DLOGITS><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+    }
     return hipGetLastError();
   }
 }

@@ -311,9 +311,10 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   // [V][G ldSt] and the h^T buffer [D][G ldSt]: the table is read and written
   // once per group. The group shares one power-of-two scale (scale index =
   // group index), so every part of the contraction is in the same units.
-  // The two-call path has no forward tiles to fill the launches that carry no
-  // dW, so it groups only small chunks (16-bit operands, a dH grid of fewer
-  // than 128 tiles); with C % 8 == 0 their dH runs once per group too (see
+  // The two-call path groups small chunks (16-bit operands, a dH grid of
+  // fewer than 128 tiles) and pairs the chunks of 16-bit operands with
+  // D % 8 == 0, whose launches without dW carry the next chunk's dlogits
+  // recompute; with C % 8 == 0 small chunks' dH runs once per group too (see
   // group_dh). Shapes alone decide, so every subset of outputs accumulates dW
   // alike.
   // The working schedule: with an FP32 table (dW_dtype, whether or not dW is
@@ -374,11 +375,14 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   LLP_LAUNCH(LLP_K_SMALL, launch_chunk_scales(g, N, G * C, ceil_div(K, G), dtype == LLP_F16 ? 15 : 0, scales,
                                               s));
   if (want_dH && !mn) LLP_LAUNCH(LLP_K_TRANSPOSE, launch_transpose(dtype, W, V, D, D, Wt, bp.ldWt, s));
-  // Fused path with two numerator / partial buffers: chunk k + 1's forward
-  // tiles run in the launch of chunk k's dH / dW (its fast epilogue only).
-  const bool overlap = fused && mn && aligned16(h) && bp.off_dSt2 >= 0 && (!want_dW || tab_fast);
+  // With two numerator / dlogits^T buffers (and, single call, two partial
+  // buffers), chunk k + 1's logits tiles run in the launch of chunk k's dH /
+  // dW (its fast epilogue only): the single call's forward, the backward's
+  // dlogits recompute. The launch tails overlap.
+  const bool overlap = mn && aligned16(h) && bp.off_dSt2 >= 0 && (!want_dW || tab_fast);
   void* const dSt_buf[2] = {dSt, overlap ? at(workspace, bp.off_dSt2) : dSt};
-  float2* const part_buf[2] = {part, overlap ? reinterpret_cast<float2*>(at(workspace, bp.off_part2)) : part};
+  float2* const part_buf[2] = {part, (overlap && fused) ? reinterpret_cast<float2*>(at(workspace, bp.off_part2))
+                                                        : part};
   // chunk k's numerator / dlogits^T columns: with grouping, column block
   // k % G of the buffer of group k / G (the groups alternate between the two
   // buffers with overlap); the h^T columns likewise, in the one h^T buffer
@@ -417,6 +421,29 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     p.ep.qflag = qflag;
     return p;
   };
+  // the dlogits recompute of chunk kk from its logits tile and the saved lse
+  // (backward)
+  auto dl_problem = [&](int64_t kk) {
+    const int64_t c0 = kk * C;
+    const int64_t Ck = (N - c0 < C) ? (N - c0) : C;
+    GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
+    p.ep.bias = b;
+    p.ep.targets = targets;
+    p.ep.tok0 = c0;
+    p.ep.v0 = v0;
+    p.ep.Vt = Vt;
+    p.epi = EPI_DLOGITS;
+    p.ep.g = g;
+    p.ep.lse = lse_use;
+    p.ep.tcoef = tcoef;
+    p.ep.dS = dS;
+    p.ep.ldS = bp.ldS;
+    p.ep.dSt = (want_dW || want_db || mn) ? qbuf(kk) : nullptr;
+    p.ep.ldSt = ldq;
+    p.ep.scales = scales;
+    p.ep.chunk = sidx(kk);
+    return p;
+  };
   auto combine = [&](int64_t kk) {
     const int64_t c0 = kk * C;
     const int64_t Ck = (N - c0 < C) ? (N - c0) : C;
@@ -450,33 +477,17 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
     const int64_t Ck = (N - c0 < C) ? (N - c0) : C;
     void* const dSt = qbuf(k);             // this chunk's numerator / dlogits^T columns
     float2* const part = part_buf[k & 1];  // and its forward partials
-    GemmProblem p = logits_problem(c0, Ck, D, V, dtype, h, W);
-    p.ep.bias = b;
-    p.ep.targets = targets;
-    p.ep.tok0 = c0;
-    p.ep.v0 = v0;
-    p.ep.Vt = Vt;
-    if (fused) {
-      // the chunk's logits tile: lse partials, target logits, softmax numerators
-      // (with overlap, chunks after the first were launched with the previous dH / dW)
-      if (!overlap || k == 0) {
+    // the chunk's logits tile (with overlap, chunks after the first were
+    // launched with the previous chunk's dH / dW)
+    if (!overlap || k == 0) {
+      if (fused) {  // lse partials, target logits, softmax numerators
         const GemmProblem pf = fwd_problem(k);
         LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &pf, nullptr, s));
         LLP_LAUNCH(LLP_K_COMBINE, combine(k));
+      } else {  // dlogits, recomputed from the logits and the saved lse
+        const GemmProblem pd = dl_problem(k);
+        LLP_LAUNCH(LLP_K_DLOGITS, launch_gemm(dtype, &pd, nullptr, s));
       }
-    } else {
-      // dlogits of the chunk, recomputed from the logits tile and the saved lse
-      p.epi = EPI_DLOGITS;
-      p.ep.g = g;
-      p.ep.lse = lse_use;
-      p.ep.tcoef = tcoef;
-      p.ep.dS = dS;
-      p.ep.ldS = bp.ldS;
-      p.ep.dSt = (want_dW || want_db || mn) ? dSt : nullptr;
-      p.ep.ldSt = ldq;
-      p.ep.scales = scales;
-      p.ep.chunk = sidx(k);
-      LLP_LAUNCH(LLP_K_DLOGITS, launch_gemm(dtype, &p, nullptr, s));
     }
     // one launch: target lists, the chunk's h transposed, and (fused) the softmax gradient
     ChunkPrep cp = {};
@@ -643,13 +654,13 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       if (st != LLP_OK) return st;
     }
     if (overlap && k + 1 < K) {
-      // with the next chunk's forward tiles, then that chunk's combine
-      const GemmProblem pf = fwd_problem(k + 1);
+      // with the next chunk's logits tiles (single call: then that chunk's combine)
+      const GemmProblem pn = fused ? fwd_problem(k + 1) : dl_problem(k + 1);
       if (do_dh)
-        LLP_LAUNCH(LLP_K_DH_DW_FWD, launch_gemm3(dtype, ph, do_dw ? &pw : nullptr, pf, s));
+        LLP_LAUNCH(fused ? LLP_K_DH_DW_FWD : LLP_K_DH_DW_DL, launch_gemm3(dtype, ph, do_dw ? &pw : nullptr, pn, s));
       else  // group_dh before the group's last chunk: no dH and (grouping) no dW in this launch
-        LLP_LAUNCH(LLP_K_FWD_LSE, launch_gemm(dtype, &pf, nullptr, s));
-      LLP_LAUNCH(LLP_K_COMBINE, combine(k + 1));
+        LLP_LAUNCH(fused ? LLP_K_FWD_LSE : LLP_K_DLOGITS, launch_gemm(dtype, &pn, nullptr, s));
+      if (fused) LLP_LAUNCH(LLP_K_COMBINE, combine(k + 1));
     } else if (do_dh || do_dw) {
       LLP_LAUNCH(LLP_K_DH_DW, launch_gemm(dtype, do_dh ? &ph : nullptr, do_dw ? &pw : nullptr, s));
     }

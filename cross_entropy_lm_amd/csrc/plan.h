@@ -103,8 +103,9 @@ struct BwdPlan {
   int64_t ldWt = 0, ldS = 0, ldSt = 0;   // leading dimensions (elements), multiples of 8
   // dW is accumulated once per group of G consecutive chunks (G = 1: per
   // chunk): the single call with dW and K >= 2, and the two-call path for
-  // small chunks (fewer than 128 dH tiles). G = 2, or for small chunks up to
-  // 4096 group columns while one group buffer stays within 256 MiB.
+  // small chunks (fewer than 128 dH tiles) or 16-bit operands with
+  // D % 8 == 0. G = 2, or for small chunks up to 4096 group columns while one
+  // group buffer stays within 256 MiB.
   int64_t G = 1;
   // Working chunk. With more than two small chunks per group and the layout
   // without W^T, a group is processed as one chunk of Cw = min(G C, N)
@@ -171,15 +172,25 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   p->ldS = round_up(V, 8);
   p->ldSt = round_up(p->C, 8);
   // small chunks: 16-bit operands and fewer than 128 tiles of 256 x 256 in a
-  // chunk's dH; the two-call layout groups only these
+  // chunk's dH
   const bool few = esize(dtype) == 2 && ceil_div(p->C, kTile) * ceil_div(D, kTile) < 128;
   // with C % 8 == 0 a group's token rows are contiguous columns, and dH runs once per group
   const bool small = few && p->C % 8 == 0;
   // Group size from the shapes alone (which outputs are requested does not
   // change the schedule): 2 chunks, or for small chunks up to kGroupCols
-  // columns and kGroupBytes of group buffer.
+  // columns and kGroupBytes of group buffer. 16-bit operands with D % 8 == 0 whose W and pair of chunk columns each
+  // span < 2 GiB (the layout the overlapped backward reads as stored): the
+  // two-call path pairs chunks too, its next chunk's dlogits recompute filling
+  // the launches that carry no dW
+  bool pairable;
+  {
+    const int64_t lim = 0x7FFFFFF0LL;
+    int64_t vd, vq;
+    pairable = e == 2 && D % 8 == 0 && mul_ok(V, D, &vd) && mul_ok(vd, e, &vd) && vd < lim &&
+               mul_ok(V, 2 * p->ldSt, &vq) && mul_ok(vq, e, &vq) && vq < lim;
+  }
   int64_t gc = 1;
-  if (p->K >= 2 && (fused || few)) {
+  if (p->K >= 2 && (fused || few || pairable)) {
     int64_t g = 2;
     if (few) {
       int64_t vb;
@@ -254,11 +265,15 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   if (want_dW || want_db || fused || p->kmajor) {
     if (!mul_ok(V, p->ldP, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
     p->off_dSt = L.add(n);
-    // (only when the working schedule has two chunks or more)
-    if (fused && p->kmajor && ceil_div(N, p->Cw) >= 2) {
+    // a second one, so that chunk k + 1's logits tiles (the single call's
+    // forward, the backward's dlogits recompute) run in the launch of chunk
+    // k's dH / dW (only when the working schedule has two chunks or more)
+    if (p->kmajor && ceil_div(N, p->Cw) >= 2) {
       p->off_dSt2 = L.add(n);
-      if (!mul_ok(p->P, p->Cw, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
-      p->off_part2 = L.add(n);
+      if (fused) {
+        if (!mul_ok(p->P, p->Cw, &n) || !mul_ok(n, 8, &n)) return LLP_EOVERFLOW;
+        p->off_part2 = L.add(n);
+      }
     }
   }
   if (want_dW) {

@@ -53,7 +53,7 @@ SIGNATURES = {
 
 # kernel kinds of the launch trace (llp_kernel_kind)
 TRACE_KINDS = ["fwd_lse", "combine", "dlogits", "dh_dw", "transpose", "small", "rows_fwd", "rows_bwd", "dh_dw_fwd",
-               "dh_reduce"]
+               "dh_reduce", "dh_dw_dlogits"]
 
 
 class LlpError(RuntimeError):

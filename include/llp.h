@@ -317,7 +317,8 @@ typedef enum {
   LLP_K_ROWS_BWD = 7,   /* logits-only backward */
   LLP_K_DH_DW_FWD = 8,  /* fused path: a chunk's dH / dW with the next chunk's forward tiles (one grid) */
   LLP_K_DH_REDUCE = 9,  /* sum of a dH contraction's vocabulary parts, in fixed order, and its epilogue */
-  LLP_K_COUNT = 10
+  LLP_K_DH_DW_DL = 10,  /* backward: a chunk's dH / dW with the next chunk's dlogits recompute (one grid) */
+  LLP_K_COUNT = 11
 } llp_kernel_kind;
 LLP_API int llp_trace_enable(int on);
 LLP_API int llp_trace_read(double* ms, int64_t* count, int n);

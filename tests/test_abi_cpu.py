@@ -63,22 +63,26 @@ def test_workspace_queries():
     only_dw = b(16384, 4096, 32000, BF16, 2048, False, True, False, True)
     no_lse = b(16384, 4096, 32000, BF16, 2048, True, True, False, False)
     assert only_dh < full and only_dw <= full and no_lse > full
-    # 16-bit operands with D % 8 == 0: dH reads dlogits^T and W as stored, so
-    # the chunk workspace is dlogits^T plus h^T of one chunk (no W^T, no
-    # token-major dlogits: nothing the requested outputs do not need); with
-    # more than one vocabulary part of 32768 rows, the parts' fp32 sums too
+    # 16-bit operands with D % 8 == 0: dH reads dlogits^T and W as stored (no
+    # W^T, no token-major dlogits); dW pairs chunks, and the next chunk's
+    # dlogits recompute runs beside a chunk's dH / dW, so the workspace is two
+    # pair buffers of dlogits^T [V][2 x 2048] plus h^T of a pair; with more
+    # than one vocabulary part of 32768 rows, the parts' fp32 sums too
     parts = lambda V: -(-V // 32768)  # noqa: E731
     dhp = lambda V, rows, D: parts(V) * rows * D * 4 if parts(V) > 1 else 0  # noqa: E731
-    expect = 2048 * 32000 * 2 + 4096 * 2048 * 2 + dhp(32000, 2048, 4096)
+    expect = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + dhp(32000, 2048, 4096)
     assert expect <= full < expect + (1 << 20)
+    # dW alone: no dH, so no second buffer (nothing overlaps); still pairs
+    expect_dw = 32000 * 4096 * 2 + 4096 * 4096 * 2
+    assert expect_dw <= only_dw < expect_dw + (1 << 20)
     # small chunks (fewer than 128 dH tiles) group dW: at 512-token chunks,
     # V = 32768, D = 2048, groups of 8 chunks (4096 columns), which run as one
     # 4096-token working chunk: dlogits^T and h^T of the working chunk
     small = b(4096, 2048, 32768, BF16, 512, True, True, False, True)
     expect_small = 4096 * 32768 * 2 + 2048 * 4096 * 2 + dhp(32768, 4096, 2048)
     assert expect_small <= small < expect_small + (1 << 20)
-    # dH alone: the vocab-major dlogits of one chunk
-    expect_dh = 2048 * 32000 * 2 + dhp(32000, 2048, 4096)
+    # dH alone: the vocab-major dlogits of one chunk, twice (no pairs without dW)
+    expect_dh = 2 * 2048 * 32000 * 2 + dhp(32000, 2048, 4096)
     assert expect_dh <= only_dh < expect_dh + (1 << 20)
     # the schedule depends on the shapes only, so a dH-only call holds the
     # 4096-token working chunk (8 small chunks) that a call with dW runs
@@ -122,19 +126,22 @@ def test_bench_group_rule_matches_the_library():
     import bench
 
     fq = llp.linear_logp_fwd_bwd_workspace_size
+    bq = llp.linear_logp_bwd_workspace_size
     for N, D, V, C in ((8192, 4096, 151936, 110), (4096, 2048, 32768, 512), (16384, 4096, 32000, 2048),
-                       (3000, 512, 50000, 64), (2000, 1024, 4096, 100), (700, 256, 1031, 300)):
+                       (3000, 512, 50000, 64), (2000, 1024, 4096, 100), (700, 256, 1031, 300),
+                       (4096, 1020, 8192, 2048), (1000, 512, 2000, 1000)):
         K = -(-N // C)
-        G = bench.dw_group(N, D, V, C, K, 2, True)
         ld = -(-C // 8) * 8
-        with_dw = fq(N, D, V, BF16, C, False, True, False, True)
-        # dW alone: the group buffer [V][G ld] and h^T [D][G ld], the forward's
-        # partials of one working chunk (a whole group when G > 2) and
-        # per-token arrays
         P = 2 * (-(-V // 256))
-        Cw = min(G * C, N) if G > 2 else C
-        core = V * G * ld * 2 + D * G * ld * 2 + P * Cw * 8
-        assert core <= with_dw < core + (1 << 20) + 4 * V + 16 * N + 4 * Cw, (N, D, V, C, G)
+        for fused, q in ((True, fq), (False, bq)):
+            G = bench.dw_group(N, D, V, C, K, 2, fused)
+            with_dw = q(N, D, V, BF16, C, False, True, False, True)
+            # dW alone: the group buffer [V][G ld] and h^T [D][G ld], (single
+            # call) the forward's partials of one working chunk (a whole group
+            # when G > 2), and per-token arrays
+            Cw = min(G * C, N) if G > 2 else C
+            core = V * G * ld * 2 + D * G * ld * 2 + (P * Cw * 8 if fused else 0)
+            assert core <= with_dw < core + (1 << 20) + 4 * V + 16 * N + 4 * Cw, (N, D, V, C, G, fused)
 
 
 @pytest.mark.parametrize("args,status", [
