@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -74,10 +75,41 @@ def traffic_from_profiles(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-# rocprofv3 kernel names -> the launch-trace kinds of the library
-PMC_KERNELS = {"dh_dw": ("Li3ELi4E",), "dlogits": ("Li2ELi0E",), "fwd_lse": ("Li1ELi0E", "gemm_kernel<bool _Accum"),
-               "dh_dw_fwd": ("gemm3_kernel",), "rows_fwd": ("rows_fwd_kernel",), "rows_bwd": ("rows_bwd_kernel",)}
+# launch-trace kinds of the library -> the names of their kernels (one name
+# per role); "vendor_gemm" is the vendor library's GEMM of gemm_reference
+PMC_KERNELS = {"dh_dw": ("dh_dw_kernel",), "dlogits": ("dlogits_kernel",),
+               "fwd_lse": ("lse_partial_kernel", "lse_q_kernel"), "dh_dw_fwd": ("dh_dw_fwd_kernel",),
+               "dh_dw_dlogits": ("dh_dw_dlogits_kernel",), "rows_fwd": ("rows_fwd_kernel",),
+               "rows_bwd": ("rows_bwd_kernel",), "vendor_gemm": ("Cijk_",),
+               # the two forward roles apart: over the batch (linear_logp_fwd), and
+               # the single call's first chunk
+               "lse_partial": ("lse_partial_kernel",), "lse_q": ("lse_q_kernel",)}
 COPY_BYTES = 1 << 30  # bytes read (and written) by one calibration copy
+
+
+def kernel_ident(name: str) -> str:
+    """The unqualified function name of a kernel as rocprofv3 writes it:
+    mangled (_ZN3llp12_GLOBAL__N_114dlogits_kernelI...) or demangled (whose
+    template arguments the demangler may garble), or a plain symbol."""
+    if name.startswith("_ZN"):
+        i, last = 3, ""
+        while i < len(name) and name[i].isdigit():
+            j = i
+            while name[j].isdigit():
+                j += 1
+            n = int(name[i:j])
+            last, i = name[j:j + n], j + n
+        return last
+    head = re.split(r"[<(]", name.replace("(anonymous namespace)", "_"), maxsplit=1)[0]
+    return head.split("::")[-1].split(" ")[-1]
+
+
+def kernel_matcher(kind: str):
+    """Predicate on rocprofv3 kernel names: the kernels of a launch kind."""
+    pats = PMC_KERNELS[kind]
+    if kind == "vendor_gemm":
+        return lambda n: any(p in n for p in pats)
+    return lambda n: kernel_ident(n) in pats
 
 
 def pmc_per_dispatch(path: str, match) -> tuple[float, int]:
@@ -102,9 +134,7 @@ def summarize_pmc(args):
     (a plain device copy of COPY_BYTES), whose readings give the scale from the
     counters' units to bytes."""
     fetch, write, cfetch, cwrite = args.summarize_pmc
-    pats = PMC_KERNELS[args.pmc_kernel]
-    rows = args.pmc_kernel.startswith("rows")
-    is_k = lambda n: (rows or "gemm_kernel" in n or "gemm3_kernel" in n) and any(x in n for x in pats)  # noqa: E731
+    is_k = kernel_matcher(args.pmc_kernel)
     is_copy = lambda n: "copyBuffer" in n or "copy_kernel" in n  # noqa: E731
     f_val, f_n = pmc_per_dispatch(fetch, is_k)
     w_val, w_n = pmc_per_dispatch(write, is_k)
@@ -119,6 +149,41 @@ def summarize_pmc(args):
         "hbm_read_bytes_per_launch": f_val * kf, "hbm_write_bytes_per_launch": w_val * kw,
         "hbm_bytes_per_launch": f_val * kf + w_val * kw,
     }
+    print(json.dumps(out, indent=1))
+
+
+def summarize_mfma(args):
+    """MFMA-pipe utilisation and clock per launch kind from one rocprofv3
+    --pmc run of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE. rocprofv3
+    writes each counter summed over its instances: MFMA busy cycles over the
+    1024 SIMDs, GUI-active cycles over the 8 XCDs. Per dispatch: clock =
+    (GUI-active / 8) / duration; MFMA utilisation = busy / ((GUI-active / 8)
+    x 1024 SIMDs), rocprofv3's MfmaUtil; a 16-bit MFMA retires 1024 flop per
+    busy SIMD cycle, so busy x 1024 is the flop the pipes executed."""
+    import csv
+    import collections
+
+    per = collections.defaultdict(dict)
+    meta = {}
+    with open(args.summarize_mfma) as f:
+        for r in csv.DictReader(f):
+            d = r["Dispatch_Id"]
+            per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            meta[d] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {"source_hash": kernel_source_hash(), "workload": args.workload, "kernels": {}}
+    for kind in PMC_KERNELS:
+        match = kernel_matcher(kind)
+        ds = [d for d in per if match(meta[d][0]) and "SQ_VALU_MFMA_BUSY_CYCLES" in per[d]]
+        if not ds:
+            continue
+        n = len(ds)
+        busy = sum(per[d]["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds) / n
+        gui = sum(per[d]["GRBM_GUI_ACTIVE"] for d in ds) / n / 8
+        ns = sum(meta[d][1] for d in ds) / n
+        out["kernels"][kind] = {
+            "dispatches": n, "avg_duration_us": ns / 1e3, "mfma_busy_cycles": busy, "gui_active_cycles_per_xcd": gui,
+            "clock_ghz": gui / ns, "mfma_util_pct": 100.0 * busy / (gui * 1024), "mfma_flop_executed": busy * 1024,
+            "tflops_at_that_clock_and_util": busy * 1024 / (ns * 1e-9) / 1e12}
     print(json.dumps(out, indent=1))
 
 
@@ -600,12 +665,18 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="print the HBM traffic summary of --pmc-kernel from rocprofv3 counter CSVs")
     ap.add_argument("--pmc-kernel", default="dh_dw", choices=sorted(PMC_KERNELS))
+    ap.add_argument("--summarize-mfma", metavar="CSV",
+                    help="print MFMA utilisation and clock per launch kind from a rocprofv3 counter CSV of "
+                         "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
     ap.add_argument("--no-lse-free", action="store_true",
                     help="logits-only workload: leave out the extra timing of the backward without a saved lse "
                          "(so that every rows_bwd dispatch of a profiled run is the saved-lse one)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a "

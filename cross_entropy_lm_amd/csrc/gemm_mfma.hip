@@ -1097,9 +1097,10 @@ __device__ __forceinline__ void gemm_dispatch(const GemmProblem& p0, const GemmP
   }
 }
 
-// kMn0: the first problem's operands are K-row-major (DMA pipeline only)
+// The body of a one- or two-problem launch. kMn0: the first problem's
+// operands are K-row-major (DMA pipeline only).
 template <typename T, int E0, int E1, bool kDma, bool kMn0 = false, int kAcc = ACC_ANY>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmProblem p1, int ntiles0) {
+__device__ __forceinline__ void gemm_entry(const GemmProblem& p0, const GemmProblem& p1, int ntiles0) {
   if constexpr (kDma) {
     // distinct LDS objects per slot (see kNS)
     __shared__ __attribute__((aligned(16))) char st0[kStageArr];
@@ -1119,14 +1120,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmProblem p0, GemmP
   }
 }
 
+// One kernel name per role, so that traces and counter runs tell them apart
+// by name alone: the forward's logits tiles with lse partials (over a batch)
+// or with the single call's numerators, the backward's dlogits recompute,
+// and a chunk's dH (first problem) and dW (second) contractions.
+template <typename T, bool kDma>
+__global__ __launch_bounds__(kThreads, 1) void lse_partial_kernel(GemmProblem p0, int ntiles0) {
+  gemm_entry<T, EPI_LSE_PARTIAL, EPI_NONE, kDma>(p0, p0, ntiles0);
+}
+template <typename T, bool kDma>
+__global__ __launch_bounds__(kThreads, 1) void lse_q_kernel(GemmProblem p0, int ntiles0) {
+  gemm_entry<T, EPI_LSE_Q, EPI_NONE, kDma>(p0, p0, ntiles0);
+}
+template <typename T, bool kDma>
+__global__ __launch_bounds__(kThreads, 1) void dlogits_kernel(GemmProblem p0, int ntiles0) {
+  gemm_entry<T, EPI_DLOGITS, EPI_NONE, kDma>(p0, p0, ntiles0);
+}
+template <typename T, bool kDma, bool kMn0 = false, int kAcc = ACC_ANY>
+__global__ __launch_bounds__(kThreads, 1) void dh_dw_kernel(GemmProblem p0, GemmProblem p1, int ntiles0) {
+  gemm_entry<T, EPI_STORE, EPI_ACCUM, kDma, kMn0, kAcc>(p0, p1, ntiles0);
+}
+
 // One chunk's dH (K-row-major operands) and dW tiles together with the next
 // chunk's logits tiles, which write their own buffers: the single call's
 // forward (EPI_LSE_Q: numerators and partials) or the backward's dlogits
 // recompute (EPI_DLOGITS: dlogits^T). The launch tails overlap. The dW tiles,
 // the shortest, come last.
 template <typename T, int kAcc, int E2>
-__global__ __launch_bounds__(kThreads, 1) void gemm3_kernel(GemmProblem p0, GemmProblem p1, GemmProblem p2,
-                                                             int nt0, int nt2) {
+__device__ __forceinline__ void gemm3_entry(const GemmProblem& p0, const GemmProblem& p1, const GemmProblem& p2,
+                                            int nt0, int nt2) {
   __shared__ __attribute__((aligned(16))) char st0[kStageArr];
   __shared__ __attribute__((aligned(16))) char st1[kStageArr];
   __shared__ __attribute__((aligned(16))) char st2[kStageArr];
@@ -1141,6 +1163,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm3_kernel(GemmProblem p0, Gemm
   } else {
     tile_run<T, EPI_ACCUM, true, false, kAcc>(p1, xcd_remap(bid - nt0 - nt2, (int)gridDim.x - nt0 - nt2), buf);
   }
+}
+template <typename T, int kAcc>
+__global__ __launch_bounds__(kThreads, 1) void dh_dw_fwd_kernel(GemmProblem p0, GemmProblem p1, GemmProblem p2,
+                                                                 int nt0, int nt2) {
+  gemm3_entry<T, kAcc, EPI_LSE_Q>(p0, p1, p2, nt0, nt2);
+}
+template <typename T, int kAcc>
+__global__ __launch_bounds__(kThreads, 1) void dh_dw_dlogits_kernel(GemmProblem p0, GemmProblem p1,
+                                                                     GemmProblem p2, int nt0, int nt2) {
+  gemm3_entry<T, kAcc, EPI_DLOGITS>(p0, p1, p2, nt0, nt2);
 }
 
 template <typename T>
@@ -1158,11 +1190,11 @@ hipError_t launch3_t(const GemmProblem& p0, const GemmProblem* p1, const GemmPro
       return hipErrorInvalidValue;
     dim3 grid(nt0 + nt1 + nt2), block(kThreads);
     if (p2.epi == EPI_LSE_Q) {
-      if (acc == ACC_FAST) gemm3_kernel<T, ACC_FAST, EPI_LSE_Q><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
-      else gemm3_kernel<T, ACC_FRESH, EPI_LSE_Q><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+      if (acc == ACC_FAST) dh_dw_fwd_kernel<T, ACC_FAST><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+      else dh_dw_fwd_kernel<T, ACC_FRESH><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
     } else {
-      if (acc == ACC_FAST) gemm3_kernel<T, ACC_FAST, EPI_DLOGITS><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
-      else gemm3_kernel<T, ACC_FRESH, EPI_DLOGITS><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+      if (acc == ACC_FAST) dh_dw_dlogits_kernel<T, ACC_FAST><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
+      else dh_dw_dlogits_kernel<T, ACC_FRESH><<<grid, block, 0, s>>>(p0, b, p2, nt0, nt2);
     }
     return hipGetLastError();
   }
@@ -1183,14 +1215,14 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
   dim3 grid(nt0 + nt1), block(kThreads);
   const bool dma = (p0 == nullptr || p0->dma) && (p1 == nullptr || p1->dma);
   if (e0 == EPI_LSE_PARTIAL && e1 == EPI_NONE) {
-    if (dma) gemm_kernel<T, EPI_LSE_PARTIAL, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
-    else gemm_kernel<T, EPI_LSE_PARTIAL, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
+    if (dma) lse_partial_kernel<T, true><<<grid, block, 0, s>>>(a, nt0);
+    else lse_partial_kernel<T, false><<<grid, block, 0, s>>>(a, nt0);
   } else if (e0 == EPI_LSE_Q && e1 == EPI_NONE) {
-    if (dma) gemm_kernel<T, EPI_LSE_Q, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
-    else gemm_kernel<T, EPI_LSE_Q, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
+    if (dma) lse_q_kernel<T, true><<<grid, block, 0, s>>>(a, nt0);
+    else lse_q_kernel<T, false><<<grid, block, 0, s>>>(a, nt0);
   } else if (e0 == EPI_DLOGITS && e1 == EPI_NONE) {
-    if (dma) gemm_kernel<T, EPI_DLOGITS, EPI_NONE, true><<<grid, block, 0, s>>>(a, b, nt0);
-    else gemm_kernel<T, EPI_DLOGITS, EPI_NONE, false><<<grid, block, 0, s>>>(a, b, nt0);
+    if (dma) dlogits_kernel<T, true><<<grid, block, 0, s>>>(a, nt0);
+    else dlogits_kernel<T, false><<<grid, block, 0, s>>>(a, nt0);
   } else if ((e0 == EPI_STORE || e0 == EPI_NONE) && (e1 == EPI_ACCUM || e1 == EPI_NONE)) {
     const bool mn = p0 != nullptr && p0->mn;
     // the dW epilogue of this launch (any mode serves when there are no dW tiles)
@@ -1200,19 +1232,19 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
                                        : ACC_FAST;
     if (mn && !(sizeof(T) == 2 && dma)) return hipErrorInvalidValue;  // K-row-major: 16-bit, DMA pipeline
     if (!dma) {
-      gemm_kernel<T, EPI_STORE, EPI_ACCUM, false><<<grid, block, 0, s>>>(a, b, nt0);
+      dh_dw_kernel<T, false><<<grid, block, 0, s>>>(a, b, nt0);
     } else if (mn) {
       if constexpr (sizeof(T) == 2) {
-        if (acc == ACC_FAST) gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, true, ACC_FAST><<<grid, block, 0, s>>>(a, b, nt0);
+        if (acc == ACC_FAST) dh_dw_kernel<T, true, true, ACC_FAST><<<grid, block, 0, s>>>(a, b, nt0);
         else if (acc == ACC_FRESH)
-          gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, true, ACC_FRESH><<<grid, block, 0, s>>>(a, b, nt0);
-        else gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, true, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
+          dh_dw_kernel<T, true, true, ACC_FRESH><<<grid, block, 0, s>>>(a, b, nt0);
+        else dh_dw_kernel<T, true, true, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
       }
     } else {
-      if (acc == ACC_FAST) gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, false, ACC_FAST><<<grid, block, 0, s>>>(a, b, nt0);
+      if (acc == ACC_FAST) dh_dw_kernel<T, true, false, ACC_FAST><<<grid, block, 0, s>>>(a, b, nt0);
       else if (acc == ACC_FRESH)
-        gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, false, ACC_FRESH><<<grid, block, 0, s>>>(a, b, nt0);
-      else gemm_kernel<T, EPI_STORE, EPI_ACCUM, true, false, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
+        dh_dw_kernel<T, true, false, ACC_FRESH><<<grid, block, 0, s>>>(a, b, nt0);
+      else dh_dw_kernel<T, true, false, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
     }
   } else {
     return hipErrorInvalidValue;
