@@ -225,21 +225,88 @@ PATHS = {
 }
 
 
-def time_steps(step, args, torch, llp, stream):
+def time_steps(step, args, torch, llp, stream, per_step=None):
     """W untimed steps, then K steps bracketed by HIP events on the launch
-    stream; returns (ms per step, {kind: (total ms, launches)})."""
+    stream (one more event between consecutive steps); returns (ms per step,
+    {kind: (total ms, launches)}) and fills `per_step` with the K step times."""
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     llp.llp_trace_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     llp.llp_trace_enable(False)
-    return e0.elapsed_time(e1) / args.steps, llp.llp_trace_read()
+    if per_step is not None:
+        per_step[:] = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    return ev[0].elapsed_time(ev[-1]) / args.steps, llp.llp_trace_read()
+
+
+def step_stats(times):
+    """Median, 20th and 80th percentile of per-step times (ms)."""
+    if not times:
+        return None
+    q = np.percentile(np.asarray(times, dtype=np.float64), [50, 20, 80])
+    return {"median": float(q[0]), "p20": float(q[1]), "p80": float(q[2]), "samples": len(times)}
+
+
+def measure_ceilings(torch):
+    """Same-box ceilings from the microbenchmarks in libllp_ceilings.so (None
+    if that library is not built): the MFMA rate of back-to-back bf16 MFMAs on
+    register operands, and the HBM streaming rates of a 16-byte-per-lane copy
+    (read + write) and read, each the best of 3 timed runs after one warm-up."""
+    import ctypes
+
+    path = os.path.join(ROOT, "cross_entropy_lm_amd", "libllp_ceilings.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.llpc_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.llpc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.llpc_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.llpc_read_out_len.argtypes = [ctypes.c_int64]
+    lib.llpc_read_out_len.restype = ctypes.c_int64
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError(f"ceilings microbenchmark failed (hipError {st})")
+
+    blocks, iters = 2048, 30000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    ms = best(lambda: ok(lib.llpc_mfma_loop(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp)))
+    mfma = blocks * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12
+    nbytes = 1 << 31
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ms_c = best(lambda: ok(lib.llpc_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                         nbytes, sp)))
+    red = torch.empty(lib.llpc_read_out_len(nbytes), dtype=torch.int32, device="cuda:0")
+    ms_r = best(lambda: ok(lib.llpc_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(red.data_ptr()),
+                                         sp)))
+    del src, dst, red, out
+    return {"mfma_loop_tflops": mfma, "copy_GBps": 2 * nbytes / (ms_c * 1e-3) / 1e9,
+            "read_GBps": nbytes / (ms_r * 1e-3) / 1e9,
+            "what": "same-box microbenchmarks (libllp_ceilings.so): back-to-back v_mfma_f32_32x32x16_bf16 on "
+                    "register operands (2048 workgroups x 4 waves x 30000 x 8 MFMAs); a 2 GiB 16-byte-per-lane "
+                    "copy (read + write bytes) and read; best of 3 runs"}
 
 
 def kernel_table(tr, steps, step_flops):
@@ -418,11 +485,12 @@ def run_linear(w, args, torch, llp):
             ("split", split_step, split_step_flops(N, D, V, sCw, sKw, s_overlap, sG, s_gdh)),
             ("fused", fused_step, fused_step_flops(N, D, V, Cw, Kw, overlap, G, group_dh))):
         log(f"{name}: warmup {args.warmup}, timed {args.steps} steps (C={C}, K={K})")
-        ms, tr = time_steps(step, args, torch, llp, stream)
+        per_step = []
+        ms, tr = time_steps(step, args, torch, llp, stream, per_step)
         kernels = kernel_table(tr, args.steps, sf)
         mfma = {k: v for k, v in kernels.items() if "tflops" in v}
         results[name] = {
-            "ms_per_step": ms, "tokens_per_s": A.tokens_per_s(N, ms),
+            "ms_per_step": ms, "tokens_per_s": A.tokens_per_s(N, ms), "step_ms": step_stats(per_step),
             # the flop this path executes: 3 contractions (single call) or 4 (split)
             "executed_flop_per_step": exec_flops[name],
             "pct_mfma_peak": 100.0 * exec_flops[name] / (ms * 1e-3) / (peak * 1e12),
@@ -448,10 +516,17 @@ def run_linear(w, args, torch, llp):
     del z
     gemm_ref = {"ms": ms_gemm, "tflops": 2 * N * V * D / (ms_gemm * 1e-3) / 1e12,
                 "what": f"torch.matmul h [{N},{D}] x W^T -> [{N},{V}] logits ({w.dtype}), vendor GEMM, no epilogue"}
+    ceil = measure_ceilings(torch)
     main = results[args.path]
     other = "split" if args.path == "fused" else "fused"
     dom = main["dominant"]
     achieved = main["kernels"][dom]["tflops"]
+    roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic_from_profiles(dom, w.name)}
+    if ceil is not None and w.dtype in ("bf16", "f16"):
+        # the same box's sustained 16-bit MFMA rate (no memory traffic)
+        roof["measured_ceiling"] = ceil["mfma_loop_tflops"]
+        roof["frac_of_measured"] = achieved / ceil["mfma_loop_tflops"]
     tokens_s = main["tokens_per_s"]
     return {
         "metric": METRIC if w.name == "flce_bf16" else f"fwd+bwd tokens/s linear_logp {w.name}",
@@ -468,8 +543,8 @@ def run_linear(w, args, torch, llp):
         "dtype": w.dtype,
         "data": "synthetic (seeded counter-based generator; random-init weights)",
         "config": {"workload": w.name, "N": N, "D": D, "V": V, "chunk": C, "chunks": K,
-                   "working_chunk": (Cw if args.path == "fused" else G_split[0]),
-                   "chunks_per_dW": (G if args.path == "fused" else G_split[2]), "dH_vocab_parts": -(-V // 32768),
+                   "working_chunk": (Cw if args.path == "fused" else sCw),
+                   "chunks_per_dW": (G if args.path == "fused" else sG), "dH_vocab_parts": -(-V // 32768),
                    "bias": w.bias, "g": w.g, "dW_table": args.table, "outputs": "logp,lse,dH,dW" +
                    (",db" if w.bias else ""), "path": PATHS[args.path]},
         "pct_mfma_peak": main["pct_mfma_peak"],
@@ -478,10 +553,11 @@ def run_linear(w, args, torch, llp):
         **({"pct_mfma_peak_8vd_equivalent": main["pct_mfma_peak_8vd_equivalent"]} if args.path == "fused" else {}),
         "memory": memory,
         **({"accuracy": accuracy[args.path]} if args.path in accuracy else {}),
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic_from_profiles(dom, w.name)},
+        "step_ms": main["step_ms"],
+        "roofline": roof,
         "kernels": main["kernels"],
         "gemm_reference": gemm_ref,
+        **({"ceilings": ceil} if ceil is not None else {}),
         other: {"path": PATHS[other], **results[other],
                 **({"accuracy": accuracy[other]} if other in accuracy else {})},
         **({"cpu_baseline": {k: v for k, v in cpu.items() if not k.startswith("_")}}
@@ -577,15 +653,17 @@ def run_logits(w, args, torch, llp):
     torch.cuda.synchronize()
     llp.llp_trace_enable(True)
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     llp.llp_trace_enable(False)
     tr = llp.llp_trace_read()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    e0, e1 = ev[0], ev[-1]  # reused by the references below
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     nbytes = {"rows_fwd": N * V * 2, "rows_bwd": 2 * N * V * 2}
     kernels = {}
     for k, (tms, cnt) in tr.items():
@@ -594,16 +672,24 @@ def run_logits(w, args, torch, llp):
                           "GBps": nbytes[k] / (tms / cnt * 1e-3) / 1e9}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     total = A.logits_only_bytes(N, V, 2)
+    ceil = measure_ceilings(torch)
+    roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBps"], "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": kernels[dom]["GBps"] / PEAK_HBM_GBS,
+            "traffic": traffic_from_profiles(dom, w.name)}
+    if ceil is not None:
+        # the same box's streaming rate for this kernel's access mix
+        roof["measured_ceiling"] = ceil["copy_GBps"] if dom == "rows_bwd" else ceil["read_GBps"]
+        roof["frac_of_measured"] = kernels[dom]["GBps"] / roof["measured_ceiling"]
     out = {
         "metric": "fwd+bwd logits-only logp N32768 V151936 bf16; GB/s",
         "value": total / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded counter-based generator)",
         "config": {"workload": w.name, "N": N, "V": V, "peak_extra_bytes": peak_extra},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBps"], "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": kernels[dom]["GBps"] / PEAK_HBM_GBS,
-                     "traffic": traffic_from_profiles(dom, w.name)},
+        "step_ms": step_stats(per_step),
+        "roofline": roof,
         "kernels": kernels,
+        **({"ceilings": ceil} if ceil is not None else {}),
         "accuracy": acc,
         "cpu_baseline": {"value": S * V * 3 * 2 / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                          "sample": f"first {S} rows: FP64 numpy oracle logp + dlogits, {dt:.2f} s",

@@ -19,6 +19,10 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libllp.so")
 SOURCES = ["gemm_mfma.hip", "aux_kernels.hip", "rows.hip", "llp_api.hip"]
+# the benchmark's same-box ceilings (MFMA loop, stream copy / read): a library
+# of its own, no part of the operators
+CEILINGS_SRC = os.path.join(HERE, "ceilings.hip")
+CEILINGS_LIB = os.path.join(HERE, "libllp_ceilings.so")
 ARCH = os.environ.get("LLP_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -61,7 +65,21 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    if os.path.exists(CEILINGS_SRC):
+        build_ceilings(verbose)
     return LIB
+
+
+def build_ceilings(verbose: bool = True) -> str:
+    tmp = CEILINGS_LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-shared", CEILINGS_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for ceilings.hip:\n{r.stderr}")
+    os.replace(tmp, CEILINGS_LIB)
+    if verbose:
+        print(f"built {CEILINGS_LIB}")
+    return CEILINGS_LIB
 
 
 if __name__ == "__main__":

@@ -312,3 +312,29 @@ def test_header_documents_each_entry_point():
     for n in declared_symbols():
         i = text.index(n + "(")
         assert "*/" in text[max(0, i - 1500):i], n  # a comment precedes every declaration
+
+
+def test_ceilings_library_checks_its_arguments():
+    """The benchmark's same-box ceilings library (MFMA loop, stream copy and
+    read) exports its entry points and rejects bad arguments before any launch
+    (hipErrorInvalidValue = 1), so these calls need no GPU."""
+    path = os.path.join(ROOT, "cross_entropy_lm_amd", "libllp_ceilings.so")
+    if not os.path.exists(path):
+        pytest.skip("libllp_ceilings.so is not built")
+    lib = ctypes.CDLL(path)
+    lib.llpc_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.llpc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.llpc_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.llpc_read_out_len.argtypes = [ctypes.c_int64]
+    lib.llpc_read_out_len.restype = ctypes.c_int64
+    fake = ctypes.c_void_p(1 << 40)
+    assert lib.llpc_mfma_loop(0, 10, fake, None) == 1
+    assert lib.llpc_mfma_loop(8, 0, fake, None) == 1
+    assert lib.llpc_mfma_loop(8, 10, None, None) == 1
+    assert lib.llpc_copy(fake, fake, 15, None) == 1
+    assert lib.llpc_copy(ctypes.c_void_p((1 << 40) + 8), fake, 16, None) == 1
+    assert lib.llpc_read(fake, 0, fake, None) == 1
+    # one workgroup of 256 threads per 256 KiB chunk
+    assert lib.llpc_read_out_len(1 << 31) == 8192 * 256
+    assert lib.llpc_read_out_len(16 * 100) == 256
+    assert lib.llpc_read_out_len(0) == 0
