@@ -173,43 +173,76 @@ struct Frag {
 // partial (m log2 e, sum of 2^(z log2 e - m log2 e)) and, for the row holding
 // the token's target, the target logit. With kQ (the fused forward + backward)
 // each summand q = 2^(z log2 e - m log2 e), in (0, 1], is also stored
-// vocab-major in the operand dtype, so that the softmax gradient can be
-// formed once the token's lse is known.
+// vocab-major in the operand dtype (per-token mode: 2^(z log2 e) itself), so
+// that the softmax gradient can be formed once the token's lse is known.
+// No per-element branches: tile-local 32-bit row indices; rows past M become
+// -inf by a select; the target logit is picked by a select and stored once
+// per column; the numerators leave through buffer stores whose offsets fall
+// out of range for rows past M and columns at or past round8(N), which the
+// hardware drops (the whole offset is in the vector operand, which the range
+// check covers), and the per-token mode's +0 at a token's target is one more
+// store after the row loop. Each wave's 128-row block has its own buffer
+// range, so a row of the vocab-major buffer must stay below 2^24 bytes (the
+// plan checks it).
 template <typename T, bool kQ>
-__device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, int tm, int64_t m0,
-                                int64_t n0, const Frag& f) {
+__device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, int tm, int64_t m0, int64_t n0,
+                                                const Frag& f) {
   const EpiParams& e = p.ep;
   const T* bias = static_cast<const T*>(e.bias);
-  int64_t tgt[NI];
-  float mx[NI];
+  const int64_t mleft = p.M - m0;
+  const int mr = mleft < kTileM ? (int)mleft : kTileM;  // rows of this tile that exist
+  const int rl0 = f.wm * kWaveRowsM + (f.lane >> 5) * 4;  // tile row of (mi = 0, r = 0) in this lane
+  int tl[NI];    // tile row of the column's target, or -1 outside [0, mr)
+  bool hit[NI];  // this lane holds that row
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     const int64_t n = n0 + f.col(ni);
-    tgt[ni] = (n < p.N) ? e.targets[e.tok0 + n] - e.v0 : -1;  // local row; matches only in this share
+    const int64_t d = (n < p.N) ? e.targets[e.tok0 + n] - e.v0 - m0 : -1;
+    tl[ni] = (d >= 0 && d < mr) ? (int)d : -1;
+    const int u = tl[ni] - rl0;
+    hit[ni] = tl[ni] >= 0 && u >= 0 && u < kWaveRowsM && (u & 4) == 0;
+  }
+  float mx[NI], zsel[NI];
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
     mx[ni] = -INFINITY;
+    zsel[ni] = -INFINITY;
   }
+  auto pass1 = [&](auto has_bias) {
+    constexpr bool kB = decltype(has_bias)::value;
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t v = m0 + f.row(mi, r);
-      const bool vv = v < p.M;
-      const float bv = (bias != nullptr && vv) ? ld_f32(bias, v) : 0.0f;
+      for (int r = 0; r < 16; ++r) {
+        const int rl = rl0 + mi * 32 + (r >> 2) * 8 + (r & 3);
+        const bool vv = rl < mr;
+        const float bv = kB ? ld_f32(bias + m0, vv ? rl : 0) : 0.0f;
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const float z = vv ? acc[mi][ni][r] + bv : -INFINITY;
-        acc[mi][ni][r] = z;
-        mx[ni] = fmaxf(mx[ni], z);
-        if (vv && v == tgt[ni]) e.zt[e.tok0 + n0 + f.col(ni)] = z;
+        for (int ni = 0; ni < NI; ++ni) {
+          const float z = vv ? acc[mi][ni][r] + bv : -INFINITY;
+          acc[mi][ni][r] = z;
+          mx[ni] = fmaxf(mx[ni], z);
+          zsel[ni] = (rl == tl[ni]) ? z : zsel[ni];
+        }
       }
+      // keeps the bias loads of later row groups from all being hoisted
+      // here (their registers would spill)
+      if constexpr (kB) __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  float m2[NI], s[NI];
+  };
+  if (bias != nullptr)
+    pass1(std::true_type{});
+  else
+    pass1(std::false_type{});
+  float m2[NI], m2e[NI], s[NI];
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     mx[ni] = fmaxf(mx[ni], __shfl_xor(mx[ni], 32));
     m2[ni] = mx[ni] * kLog2e;
+    // a block whose rows all lie past V or are -inf: its q are +0, not 2^(-inf - (-inf))
+    m2e[ni] = (m2[ni] == -INFINITY) ? 0.0f : m2[ni];
     s[ni] = 0.0f;
+    if (hit[ni]) e.zt[e.tok0 + n0 + f.col(ni)] = zsel[ni];
   }
   if constexpr (!kQ) {
 #pragma unroll
@@ -217,47 +250,63 @@ __device__ __forceinline__ void epi_lse_partial(const GemmProblem& p, Acc& acc, 
 #pragma unroll
       for (int r = 0; r < 16; ++r)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          s[ni] += __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2[ni]));
+        for (int ni = 0; ni < NI; ++ni) s[ni] += __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2e[ni]));
   } else {
+    constexpr int es = (int)sizeof(T);
+    constexpr uint32_t kOut = 0x80000000u;  // a column offset that puts every store out of range
     const int64_t npad = (p.N + 7) & ~int64_t(7);
-    T* col[NI];     // this lane's column of the tile in the vocab-major buffer
-    bool keep[NI];  // the column lies in [0, round8(N)); past N it stores +0
-    bool live[NI];
-    float mul[NI];  // stored value = q mul (per-token mode: 2^m for a block in range)
+    const int64_t rowb = e.ldSt * es;       // bytes per row, below 2^24
+    const int64_t w0 = m0 + f.wm * kWaveRowsM;  // first row of this wave's block
+    const int64_t wleft = p.M - w0;             // rows of the block that exist (may be <= 0)
+    const int64_t span = wleft > 0 ? wleft * rowb : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(e.dSt) + (wleft > 0 ? w0 * rowb : 0), (short)0,
+        span < 0x7FFFFFF0LL ? (int)span : 0x7FFFFFF0, 0x00020000);
+    uint32_t coff[NI];  // this lane's row half and column, or kOut at or past round8(N)
+    float mul[NI];      // stored value = q mul: 2^m in the per-token mode, +0 past N or for a -inf block
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int64_t n = n0 + f.col(ni);
-      col[ni] = static_cast<T*>(e.dSt) + n;
-      keep[ni] = n < npad;
-      live[ni] = n < p.N;
-      mul[ni] = 1.0f;
-      // every row of the block is -inf (masked, or past V): its q are 0, not
-      // 2^(-inf - (-inf))
-      if (m2[ni] == -INFINITY) live[ni] = false;
+      coff[ni] = n < npad ? (uint32_t)((f.lane >> 5) * 4 * rowb + f.col(ni) * es) : kOut;
+      const bool live = n < p.N && m2[ni] != -INFINITY;
+      mul[ni] = live ? 1.0f : 0.0f;
       if (e.qtok) {
         const bool inr = m2[ni] >= kQtokLo && m2[ni] <= kQtokHi;
-        if (inr) mul[ni] = __builtin_amdgcn_exp2f(m2[ni]);
+        if (inr && live) mul[ni] = __builtin_amdgcn_exp2f(m2[ni]);
         // lanes l and l + 32 hold the same column and block: one of them flags it
         if (!inr && m2[ni] != -INFINITY && f.lane < 32 && n < p.N) e.qflag[e.tok0 + n] = 1;
       }
     }
+    // the buffer starts at column n0's row w0 entry minus the tile's first column
+    const uint32_t cbase = (uint32_t)(n0 * es);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int ni = 0; ni < NI; ++ni)
+      if (coff[ni] != kOut) coff[ni] += cbase;
+    auto put = [&](uint32_t off, float v) {
+      if constexpr (es == 2)
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (T)v), rs, off, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, off, 0, 0);
+    };
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t v = m0 + f.row(mi, r);
-        const int64_t off = v * e.ldSt;
+        const uint32_t roff = (uint32_t)((mi * 32 + (r >> 2) * 8 + (r & 3)) * rowb);
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          // a block whose rows all lie past V has m = -inf; its rows are not stored
-          const float q = __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2[ni]));
+          const float q = __builtin_amdgcn_exp2f(fmaf(acc[mi][ni][r], kLog2e, -m2e[ni]));
           s[ni] += q;
-          // per-token mode: the target's entry is +0 (its one-hot part is exact elsewhere)
-          const bool st = live[ni] && !(e.qtok && v == tgt[ni]);
-          if (v < p.M && keep[ni]) col[ni][off] = (T)(st ? q * mul[ni] : 0.0f);
+          put(coff[ni] + roff, q * mul[ni]);
         }
       }
+    }
+    if (e.qtok) {
+      // per-token mode: the target's entry is +0 (its one-hot part is exact elsewhere)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        if (hit[ni]) put(coff[ni] + (uint32_t)((tl[ni] - rl0) * rowb), 0.0f);
+    }
   }
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {

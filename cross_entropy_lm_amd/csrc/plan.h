@@ -221,6 +221,9 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     const int64_t wcols = round_up(p->Cw, 8);
     if (!mul_ok(p->G, p->ldSt, &p->ldP)) return LLP_EOVERFLOW;
     if (wcols > p->ldP) p->ldP = wcols;
+    // the single call's forward tiles store numerators with 32-bit offsets
+    // inside 128-row blocks: a row of that buffer stays below 2^24 bytes
+    if (fused && p->ldP * e >= (int64_t(1) << 24)) return LLP_EOVERFLOW;
   }
   Layout L;
   int64_t n;

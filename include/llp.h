@@ -220,6 +220,10 @@ LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t 
  * workspace must be 16-byte aligned even when dH is not requested.
  * With dH, dW and db all NULL this is linear_logp_fwd (and the workspace
  * query returns the forward's size). Deterministic.
+ * Limit: a row of the numerator buffer (the group's columns times the operand
+ * size) must stay below 2^24 bytes, i.e. fewer than 2^23 tokens per chunk
+ * group in 16-bit operands; beyond that LLP_EOVERFLOW (linear_logp_fwd +
+ * linear_logp_bwd have no such limit).
  */
 LLP_API int linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
                                        int want_dH, int want_dW, int want_db, int have_lse,

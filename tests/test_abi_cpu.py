@@ -265,6 +265,16 @@ def test_fused_argument_errors_and_workspace():
     # N = 0 with accumulate: nothing to do, null pointers allowed
     assert llp.lib().linear_logp_fwd_bwd(0, 128, 1024, F32, 0, None, None, None, None, None, None, None, None,
                                          None, F32, None, 1, None, 0, None) == llp.LLP_OK
+    # the single call keeps a row of its numerator buffer below 2^24 bytes (its
+    # stores use 32-bit offsets inside 128-row blocks): a 2^23-token chunk in
+    # bf16 (2^24 bytes per row) is refused, the two-call path takes it
+    out = ctypes.c_size_t(0)
+    assert llp.lib().linear_logp_fwd_bwd_workspace_size(1 << 23, 8, 2, BF16, 1 << 23, 1, 0, 0, 1,
+                                                        ctypes.byref(out)) == llp.LLP_EOVERFLOW
+    assert llp.lib().linear_logp_fwd_bwd_workspace_size((1 << 23) - 8, 8, 2, BF16, (1 << 23) - 8, 1, 0, 0, 1,
+                                                        ctypes.byref(out)) == llp.LLP_OK
+    assert llp.lib().linear_logp_bwd_workspace_size(1 << 23, 8, 2, BF16, 1 << 23, 1, 0, 0, 1,
+                                                    ctypes.byref(out)) == llp.LLP_OK
 
 
 def _sfwd(N=256, D=128, Vs=400, v0=400, Vt=1031, dt=F32, h=FAKE, W=FAKE, b=FAKE, t=FAKE, lse=FAKE, zt=FAKE,
