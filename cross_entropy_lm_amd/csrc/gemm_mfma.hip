@@ -345,30 +345,77 @@ __device__ __forceinline__ void epi_dlogits(const GemmProblem& p, Acc& acc, int6
     gs[ni] = gv[ni] * inv;
     l2[ni] = nv ? e.lse[tok] * kLog2e : 0.0f;
   }
-  // softmax part in place of the logits (0 past V / past the chunk)
+  // softmax part in place of the logits (0 past V / past the chunk), with one
+  // per-element branch left, the rarely taken store of a target's exact part:
+  // tile-local 32-bit rows; the vocab-major copy leaves through buffer
+  // stores, one buffer range per 8-row group (its
+  // 64-bit base in scalar registers), whose offsets fall out of range for rows
+  // past M and columns at or past round8(N) (the hardware drops those; the
+  // whole offset is in the range-checked vector operand). Values are formed
+  // as before, so the results are the same bits. A row of the vocab-major
+  // buffer stays below 2^28 bytes (the plan checks it).
+  constexpr int es = (int)sizeof(T);
+  constexpr uint32_t kOut = 0x80000000u;  // a column offset that puts every store out of range
+  const int64_t mleft = p.M - m0;
+  const int mr = mleft < kTileM ? (int)mleft : kTileM;  // rows of this tile that exist
+  const int rl0 = f.wm * kWaveRowsM + (f.lane >> 5) * 4;  // tile row of (mi = 0, r = 0) in this lane
+  const int64_t rowb = e.ldSt * es;
+  const int64_t npad = (p.N + 7) & ~int64_t(7);
+  int tl[NI];         // tile row of the column's target, or -1 outside [0, mr)
+  uint32_t coff[NI];  // this lane's row half and column inside an 8-row group, or kOut
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    const int64_t n = n0 + f.col(ni);
+    const int64_t d = rv[ni] ? tgt[ni] - m0 : -1;
+    tl[ni] = (d >= 0 && d < mr) ? (int)d : -1;
+    coff[ni] = n < npad ? (uint32_t)((f.lane >> 5) * 4 * rowb + n * es) : kOut;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t v = m0 + f.row(mi, r);
-      const bool vv = v < p.M;
-      const float bv = (bias != nullptr) ? ld_f32(bias, vv ? v : 0) : 0.0f;
+    for (int g8 = 0; g8 < 4; ++g8) {
+      // rows m0 + wm 128 + mi 32 + g8 8 + [0, 8) of the buffer (this lane: half 4 + [0, 4))
+      const int64_t R = m0 + f.wm * kWaveRowsM + mi * 32 + g8 * 8;
+      const int64_t left = p.M - R;
+      const int64_t span = left > 0 ? left * rowb : 0;
+      // (not used without a vocab-major copy: the stores below are skipped then)
+      const uintptr_t base = reinterpret_cast<uintptr_t>(dSt) + (uintptr_t)(left > 0 ? R * rowb : 0);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>(base), (short)0, span < 0x7FFFFFF0LL ? (int)span : 0x7FFFFFF0, 0x00020000);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int64_t n = n0 + f.col(ni);
-        const float z = acc[mi][ni][r] + bv;
-        const float pr = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -l2[ni]));
-        float d = 0.0f;  // +0 for a row that takes no part
-        if (rv[ni] && vv) {
-          if (v == tgt[ni])
-            e.tcoef[e.tok0 + n] = fmaf(-gv[ni], pr, gv[ni]);  // g (1 - p_t), the exact part
-          else
-            d = -gs[ni] * pr;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int r = g8 * 4 + r4;
+        const int rl = rl0 + mi * 32 + g8 * 8 + r4;
+        const bool vv = rl < mr;
+        const float bv = (bias != nullptr) ? ld_f32(bias + m0, vv ? rl : 0) : 0.0f;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const float z = acc[mi][ni][r] + bv;
+          const float pr = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, -l2[ni]));
+          if (rl == tl[ni]) e.tcoef[e.tok0 + n0 + f.col(ni)] = fmaf(-gv[ni], pr, gv[ni]);  // g (1 - p_t)
+          // +0 for a row that takes no part, and at the target (its part is exact)
+          const bool part = rv[ni] && vv && rl != tl[ni];
+          const float d = part ? -gs[ni] * pr : 0.0f;
+          acc[mi][ni][r] = d;
+          // columns [N, round8(N)) get +0: a 16-byte K chunk that straddles the
+          // chunk's end then contributes nothing to the dW contraction
+          if (dSt != nullptr) {
+            const uint32_t off = coff[ni] + (uint32_t)(r4 * rowb);
+            if constexpr (std::is_same<T, _Float16>::value) {
+              // fp16: the product p (-g/s) rounded once, straight to fp16
+              // (a mixed-precision FMA with fp32 sources and a +0 addend),
+              // not rounded to fp32 first
+              uint32_t hv = 0;
+              const float ng = -gs[ni];
+              asm("v_fma_mixlo_f16 %0, %1, %2, 0" : "+v"(hv) : "v"(pr), "v"(ng));
+              __builtin_amdgcn_raw_buffer_store_b16(part ? (unsigned short)hv : (unsigned short)0, rs, off, 0, 0);
+            } else if constexpr (es == 2) {
+              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (T)d), rs, off, 0, 0);
+            } else {
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, d), rs, off, 0, 0);
+            }
+          }
         }
-        acc[mi][ni][r] = d;
-        // columns [N, round8(N)) get +0: a 16-byte K chunk that straddles the
-        // chunk's end then contributes nothing to the dW contraction
-        if (dSt != nullptr && vv && n < ((p.N + 7) & ~int64_t(7))) dSt[v * e.ldSt + n] = (T)d;
       }
     }
   }

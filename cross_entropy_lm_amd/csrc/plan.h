@@ -267,6 +267,9 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   }
   if (want_dW || want_db || fused || p->kmajor) {
     if (!mul_ok(V, p->ldP, &n) || !mul_ok(n, e, &n)) return LLP_EOVERFLOW;
+    // the backward's dlogits tiles store into this buffer with 32-bit offsets
+    // inside 8-row groups: a row stays below 2^28 bytes
+    if (p->ldP * e >= (int64_t(1) << 28)) return LLP_EOVERFLOW;
     p->off_dSt = L.add(n);
     // a second one, so that chunk k + 1's logits tiles (the single call's
     // forward, the backward's dlogits recompute) run in the launch of chunk

@@ -183,6 +183,8 @@ LLP_API int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int 
  * transpose, see the workspace query) W and the workspace must be 16-byte
  * aligned, else LLP_EINVAL (nothing is enqueued).
  * Deterministic: the same inputs give bit-identical outputs on every call.
+ * Limit: a row of the dlogits^T buffer (the chunk group's columns times the
+ * operand size) stays below 2^28 bytes, else LLP_EOVERFLOW.
  */
 LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
                     const void* h, const void* W, const void* b, const int64_t* targets,
@@ -222,8 +224,8 @@ LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t 
  * query returns the forward's size). Deterministic.
  * Limit: a row of the numerator buffer (the group's columns times the operand
  * size) must stay below 2^24 bytes, i.e. fewer than 2^23 tokens per chunk
- * group in 16-bit operands; beyond that LLP_EOVERFLOW (linear_logp_fwd +
- * linear_logp_bwd have no such limit).
+ * group in 16-bit operands; beyond that LLP_EOVERFLOW (linear_logp_bwd's
+ * limit is 2^28 bytes per row of its dlogits^T buffer).
  */
 LLP_API int linear_logp_fwd_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
                                        int want_dH, int want_dW, int want_db, int have_lse,

@@ -275,6 +275,12 @@ def test_fused_argument_errors_and_workspace():
                                                         ctypes.byref(out)) == llp.LLP_OK
     assert llp.lib().linear_logp_bwd_workspace_size(1 << 23, 8, 2, BF16, 1 << 23, 1, 0, 0, 1,
                                                     ctypes.byref(out)) == llp.LLP_OK
+    # the two-call backward's dlogits^T rows stay below 2^28 bytes (32-bit
+    # offsets inside 8-row groups): 2^27 bf16 columns are refused
+    assert llp.lib().linear_logp_bwd_workspace_size(1 << 27, 8, 1, BF16, 1 << 27, 1, 0, 0, 1,
+                                                    ctypes.byref(out)) == llp.LLP_EOVERFLOW
+    assert llp.lib().linear_logp_bwd_workspace_size((1 << 27) - 8, 8, 1, BF16, (1 << 27) - 8, 1, 0, 0, 1,
+                                                    ctypes.byref(out)) == llp.LLP_OK
 
 
 def _sfwd(N=256, D=128, Vs=400, v0=400, Vt=1031, dt=F32, h=FAKE, W=FAKE, b=FAKE, t=FAKE, lse=FAKE, zt=FAKE,
