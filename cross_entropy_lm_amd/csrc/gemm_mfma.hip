@@ -608,7 +608,10 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
 // table[v, :] += s C[v, :]. The tile goes through LDS (free once the K loop
 // has ended) in two halves of 128 rows x 256 columns, four 32-row regions
 // each; every thread then reads and writes whole 16-byte pieces of table rows
-// with buffer instructions whose row offsets are scalar. The old values of
+// with buffer instructions. The whole offset (row and column) is in the
+// vector operand, which the range check covers (the scalar offset may not
+// be), so the rows of a last tile that lie past the table's end read as 0
+// instead of reading past the allocation; their stores are skipped. The old values of
 // half 1 are in flight while half 0 is added and stored, so a tile waits for
 // about one table round trip. Requires D % 4 == 0, a 16-byte aligned table
 // and a 256-row tile span below 2 GiB (EpiParams::tab_fast).
@@ -629,7 +632,7 @@ __device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, i
   const float sc = e.scales[e.chunk].x;
   const int tid = threadIdx.x;
   float* tb0 = static_cast<float*>(e.out) + m0 * e.ldo + n0;
-  const int64_t span = (p.M - m0) * e.ldo * 4;  // bytes from the tile's first row to the table's end
+  const int64_t span = ((p.M - m0) * e.ldo - n0) * 4;  // bytes from the tile's first element to the table's end
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(tb0, (short)0, span < 0x7FFFFFF0LL ? (int)span : 0x7FFFFFF0, 0x00020000);
   const int wrow = tid >> 6;             // this wave's row inside a kRpp-row group (wave-uniform)
@@ -651,7 +654,7 @@ __device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, i
         o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       else
         o[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             rs, vbase, row_of(h, 2 * kPpr * k + j) * (int)e.ldo * 4, 2 /* nt */));
+                                             rs, vbase + row_of(h, 2 * kPpr * k + j) * (int)e.ldo * 4, 0, 2 /* nt */));
     }
   };
   auto to_lds = [&](int h) {
@@ -680,8 +683,8 @@ __device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, i
       const f32x4 add = *reinterpret_cast<const f32x4*>(reg + rr * 256 + (c ^ tab_swz(rr)));
       const int row = row_of(h, i) + wrow;
       if (colok && m0 + row < p.M)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[j] + add), rs, vbase,
-                                               row_of(h, i) * (int)e.ldo * 4, 2 /* nt */);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[j] + add), rs,
+                                               vbase + row_of(h, i) * (int)e.ldo * 4, 0, 2 /* nt */);
     }
   };
   // the scheduling barriers keep the loads of half 1 where they are issued
