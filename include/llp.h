@@ -32,6 +32,9 @@
  *   stream) and the call returns without waiting for it. The library keeps no
  *   mutable global state (except the scratch of linear_logp_fwd_noalloc);
  *   calls on different streams must not share output or workspace buffers.
+ *   A call only launches kernels on `stream` (no allocation, copy, memset or
+ *   synchronisation), so it may be captured into a HIP graph; a replay
+ *   produces the eager call's bits.
  * - dtypes: operands h, W, b, logits, dH and dlogits use `dtype` (LLP_F32,
  *   LLP_BF16 or LLP_F16). logp, lse and g are float32. Targets are int64.
  *   Arithmetic accumulates in float32; 16-bit results are rounded to nearest
