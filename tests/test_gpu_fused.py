@@ -496,3 +496,44 @@ def test_dh_vocabulary_parts(dt):
                 assert_close(dH, rdH, *tg, f"dH {n} D={D} chunk {chunk}")
                 assert_close(dW, rdW, *tg, f"dW {n} D={D} chunk {chunk}")
                 assert_close(db, rdb, *tg, f"db {n} D={D} chunk {chunk}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_fast_table_tails_in_both_dimensions(dt):
+    """The FP32 table's read-modify-write epilogue on ragged tiles in both
+    dimensions: V = 1031 leaves a last row tile of 7 rows, and D = 520 spreads
+    each row tile over three column tiles, the last holding 8 columns. Every
+    table access of such a tile must stay inside a buffer range that ends at
+    the table's last element. Both paths are checked against the oracle,
+    storing the table and accumulating into a given one (which makes every
+    contraction read the old values)."""
+    w = synth.LinearWorkload(f"tails_{dt}", 300, 520, 1031, dt, True, 64, "normal")
+    d = synth.make_linear_t(w, DEV)
+    host = synth.make_linear_np(w)
+    rlogp, _ = O.linear_logp_fwd(host["h64"], host["W64"], host["b64"], host["t"])
+    rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True,
+                                      True, True)
+    tl, tg = TOL[dt]["logp"], TOL[dt]["grad"]
+    for (logp, _, dH, dW, db), n in ((fused(w, d), "single call"), (split(w, d), "two-call")):
+        assert dW.dtype == torch.float32 and db.dtype == torch.float32
+        assert_close(logp, rlogp, *tl, f"logp {n}")
+        assert_close(dH, rdH, *tg, f"dH {n}")
+        assert_close(dW, rdW, *tg, f"dW {n}")
+        assert_close(db, rdb, *tg, f"db {n}")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    t0 = torch.randn(w.V, w.D, generator=gen, device=DEV)
+    b0 = torch.randn(w.V, generator=gen, device=DEV)
+    base_w, base_b = t0.double().cpu().numpy(), b0.double().cpu().numpy()
+    dW, db = t0.clone(), b0.clone()
+    fused(w, d, accumulate=True, dW=dW, db=db)
+    assert_close(dW, base_w + rdW, *tg, "dW single call, accumulate")
+    assert_close(db, base_b + rdb, *tg, "db single call, accumulate")
+    dW, db = t0.clone(), b0.clone()
+    L = llp()
+    _, lse = L.linear_logp_fwd(d["h"], d["W"], d["b"], d["t"])
+    L.linear_logp_bwd(d["h"], d["W"], d["b"], d["t"], d["g"], lse, True, True, True, chunk=w.chunk,
+                      accumulate=True, dW=dW, db=db)
+    torch.cuda.synchronize()
+    assert_close(dW, base_w + rdW, *tg, "dW two-call, accumulate")
+    assert_close(db, base_b + rdb, *tg, "db two-call, accumulate")
