@@ -158,8 +158,10 @@ def summarize_mfma(args):
     writes each counter summed over its instances: MFMA busy cycles over the
     1024 SIMDs, GUI-active cycles over the 8 XCDs. Per dispatch: clock =
     (GUI-active / 8) / duration; MFMA utilisation = busy / ((GUI-active / 8)
-    x 1024 SIMDs), rocprofv3's MfmaUtil; a 16-bit MFMA retires 1024 flop per
-    busy SIMD cycle, so busy x 1024 is the flop the pipes executed."""
+    x 1024 SIMDs), rocprofv3's MfmaUtil. A 16-bit MFMA retires 1024 flop per
+    busy SIMD cycle and an fp32 one 64 (the dense peaks 2.5 PFLOP/s and
+    157.3 TFLOP/s over 1024 SIMDs at 2.4 GHz), so busy x that figure is the
+    flop the pipes executed."""
     import csv
     import collections
 
@@ -170,7 +172,9 @@ def summarize_mfma(args):
             d = r["Dispatch_Id"]
             per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             meta[d] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    out = {"source_hash": kernel_source_hash(), "workload": args.workload, "kernels": {}}
+    fpc = 64 if WORKLOADS[args.workload].dtype == "f32" else 1024  # flop per busy SIMD cycle
+    out = {"source_hash": kernel_source_hash(), "workload": args.workload, "flop_per_busy_cycle": fpc,
+           "kernels": {}}
     for kind in PMC_KERNELS:
         match = kernel_matcher(kind)
         ds = [d for d in per if match(meta[d][0]) and "SQ_VALU_MFMA_BUSY_CYCLES" in per[d]]
@@ -182,8 +186,8 @@ def summarize_mfma(args):
         ns = sum(meta[d][1] for d in ds) / n
         out["kernels"][kind] = {
             "dispatches": n, "avg_duration_us": ns / 1e3, "mfma_busy_cycles": busy, "gui_active_cycles_per_xcd": gui,
-            "clock_ghz": gui / ns, "mfma_util_pct": 100.0 * busy / (gui * 1024), "mfma_flop_executed": busy * 1024,
-            "tflops_at_that_clock_and_util": busy * 1024 / (ns * 1e-9) / 1e12}
+            "clock_ghz": gui / ns, "mfma_util_pct": 100.0 * busy / (gui * 1024), "mfma_flop_executed": busy * fpc,
+            "tflops_at_that_clock_and_util": busy * fpc / (ns * 1e-9) / 1e12}
     print(json.dumps(out, indent=1))
 
 
