@@ -548,7 +548,7 @@ def run_linear(w, args, torch, llp):
         "data": "synthetic (seeded counter-based generator; random-init weights)",
         "config": {"workload": w.name, "N": N, "D": D, "V": V, "chunk": C, "chunks": K,
                    "working_chunk": (Cw if args.path == "fused" else sCw),
-                   "chunks_per_dW": (G if args.path == "fused" else sG), "dH_vocab_parts": -(-V // 32768),
+                   "chunks_per_dW": (G if args.path == "fused" else sG), "dH_vocab_parts": -(-V // (8192 if w.dtype == "f32" else 32768)),
                    "bias": w.bias, "g": w.g, "dW_table": args.table, "outputs": "logp,lse,dH,dW" +
                    (",db" if w.bias else ""), "path": PATHS[args.path]},
         "pct_mfma_peak": main["pct_mfma_peak"],

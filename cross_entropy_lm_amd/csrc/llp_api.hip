@@ -606,7 +606,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
         // the vocabulary in fixed parts: one tile per part, fp32 partials,
         // then the reduction below applies this epilogue to their sum
         ph.kparts = (int)bp.dh_parts;
-        ph.kpart = kDhPart;
+        ph.kpart = bp.dh_part;
         ph.ep.dhp = reinterpret_cast<float*>(at(workspace, bp.off_dhp));
         ph.ep.dhp_stride = bp.dh_rows * D;
       }

@@ -128,9 +128,11 @@ struct BwdPlan {
   // bf16 single call: per-token numerators (same shape conditions, whether or
   // not dH is asked for, so that every subset of outputs computes alike)
   bool qtok = false;
-  // dH: the vocabulary is cut into dh_parts = ceil(V / kDhPart) fixed parts;
-  // with more than one, each part's fp32 sums go to [dh_parts][dh_rows][D]
+  // dH: the vocabulary is cut into dh_parts = ceil(V / dh_part) fixed parts
+  // of dh_part rows (kDhPart, or kDhPartF32 for fp32 operands); with more
+  // than one, each part's fp32 sums go to [dh_parts][dh_rows][D]
   // (dh_rows: the most rows one dH contraction covers, G C where small chunks group)
+  int64_t dh_part = kDhPart;
   int64_t dh_parts = 1;
   int64_t dh_rows = 0;
   int64_t off_dhp = -1;
@@ -245,7 +247,8 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     p->off_cq = L.add(N * 4);
   }
   if (want_dH) {
-    p->dh_parts = ceil_div(V, kDhPart);
+    p->dh_part = e == 4 ? kDhPartF32 : kDhPart;
+    p->dh_parts = ceil_div(V, p->dh_part);
     // small chunks take dH per group (C % 8 == 0) or per working chunk
     p->dh_rows = p->Cw > p->C ? p->Cw : (p->kmajor && p->G > 1 && small) ? p->G * p->C : p->C;
     if (p->dh_parts > 1) {

@@ -158,8 +158,9 @@ LLP_API int linear_logp_fwd_noalloc(int64_t N, int64_t D, int64_t V, int dtype,
  * columns; with 16-bit operands and D % 8 == 0 (V D and V x the group's
  * columns each below 2^30 elements) dH reads W as stored, no transposed copy
  * of W is held, and a second softmax-part buffer lets the next chunk's
- * logits recompute run beside a chunk's dH / dW; with V > 32768 dH's fp32
- * sums over vocabulary parts of 32768 rows are held too.
+ * logits recompute run beside a chunk's dH / dW; with V above one
+ * vocabulary part (32768 rows for 16-bit operands, 8192 for fp32) dH's fp32
+ * sums over the parts are held too.
  */
 LLP_API int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
                                    int want_dH, int want_dW, int want_db, int have_lse,

@@ -77,7 +77,7 @@ static void check_layout(int64_t N, int64_t D, int64_t V, int dt, int64_t chunk,
   // the layout holds only what the requested outputs need
   EXPECT(p.kmajor == (dh && esize(dt) == 2 && D % 8 == 0 && (p.off_Wt < 0)));
   if (p.kmajor) EXPECT(p.off_Wt < 0 && p.off_dS < 0 && p.off_dSt >= 0);
-  if (dh) EXPECT(p.dh_parts == (V + 32767) / 32768);
+  if (dh) EXPECT(p.dh_part == (esize(dt) == 4 ? 8192 : 32768) && p.dh_parts == (V + p.dh_part - 1) / p.dh_part);
   if (dh) EXPECT(p.dh_rows == p.C || p.dh_rows == p.G * p.C || p.dh_rows == p.Cw);
   // the working chunk: the chunk, or a whole group of more than two chunks (at most N tokens)
   // (Cw does not depend on which outputs are requested: G is the group of the dW schedule)

@@ -472,8 +472,9 @@ def test_dw_groups_of_many_chunks(chunk):
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_dh_vocabulary_parts(dt):
-    """dH sums the vocabulary in fixed parts of 32768 rows whose fp32 sums are
-    added in increasing order (V = 70000: parts of 32768, 32768 and 4464 rows).
+    """dH sums the vocabulary in fixed parts whose fp32 sums are added in
+    increasing order (V = 70000: parts of 32768, 32768 and 4464 rows for
+    16-bit operands; eight of 8192 and one of 4464 for fp32).
     Both paths against the oracle (dH, dW, db, logp); each path's dH bitwise
     the same at every chunking (the parts depend on V alone); bf16 also with
     D % 8 != 0 (the layout with a transposed W, split the same way)."""
