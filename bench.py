@@ -333,7 +333,7 @@ def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
     with an FP32 table, dW and K >= 2, the single call and (for small chunks:
     16-bit operands, fewer than 128 dH tiles; or 16-bit operands with
     D % 8 == 0) the two-call path accumulate dW once per group of G chunks:
-    G = 2, for small chunks up to 4096 group columns and 256 MiB of group
+    G = 2, for small chunks up to 4096 group columns and 1 GiB of group
     buffer, at most K."""
     few = esize == 2 and -(-C // 256) * -(-D // 256) < 128
     ld = -(-C // 8) * 8
@@ -343,7 +343,7 @@ def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
         return 1
     g = 2
     if few:
-        g = max(g, min(4096 // ld, (1 << 28) // (V * ld * esize)))
+        g = max(g, min(4096 // ld, (1 << 30) // (V * ld * esize)))
     return min(g, K)
 
 

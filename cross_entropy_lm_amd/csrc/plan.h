@@ -16,7 +16,7 @@ constexpr int64_t kTile = kTileM;               // contraction tile edge (M and 
 static_assert(kTileM == kTileN, "square tiles");
 constexpr int64_t kAlign = 256;                 // workspace region alignment (bytes)
 constexpr int64_t kGroupCols = 4096;            // small chunks: columns of a dW group at most
-constexpr int64_t kGroupBytes = int64_t(1) << 28;  // ... and bytes of one group buffer at most
+constexpr int64_t kGroupBytes = int64_t(1) << 30;  // ... and bytes of one group buffer at most
 
 inline bool dtype_ok(int dt) { return dt == LLP_F32 || dt == LLP_BF16 || dt == LLP_F16; }
 inline int64_t esize(int dt) { return dt == LLP_F32 ? 4 : 2; }
@@ -105,7 +105,7 @@ struct BwdPlan {
   // chunk): the single call with dW and K >= 2, and the two-call path for
   // small chunks (fewer than 128 dH tiles) or 16-bit operands with
   // D % 8 == 0. G = 2, or for small chunks up to 4096 group columns while one
-  // group buffer stays within 256 MiB.
+  // group buffer stays within 1 GiB.
   int64_t G = 1;
   // Working chunk. With more than two small chunks per group and the layout
   // without W^T, a group is processed as one chunk of Cw = min(G C, N)

@@ -69,10 +69,10 @@ static void check_layout(int64_t N, int64_t D, int64_t V, int dt, int64_t chunk,
   }
   EXPECT(p.ldSt % 8 == 0 && p.ldSt >= p.C);
   // dW groups of G chunks: G = 1 or 2, or more for small chunks within the
-  // 4096-column and 256 MiB caps, never more than the chunks
+  // 4096-column and 1 GiB caps, never more than the chunks
   EXPECT(p.G >= 1 && p.G <= (p.K > 1 ? p.K : 1) && p.ldP >= p.G * p.ldSt);
   EXPECT(p.ldP == (p.G * p.ldSt > round_up(p.Cw, 8) ? p.G * p.ldSt : round_up(p.Cw, 8)));
-  if (p.G > 2) EXPECT(p.G * p.ldSt <= 4096 && V * p.ldP * esize(dt) <= (int64_t(1) << 28));
+  if (p.G > 2) EXPECT(p.G * p.ldSt <= 4096 && V * p.ldP * esize(dt) <= (int64_t(1) << 30));
   if (!dw) EXPECT(p.G == 1);
   // the layout holds only what the requested outputs need
   EXPECT(p.kmajor == (dh && esize(dt) == 2 && D % 8 == 0 && (p.off_Wt < 0)));

@@ -444,13 +444,13 @@ def test_fused_masked_vocab_blocks(dt):
 @pytest.mark.parametrize("chunk", [64, 60])
 def test_dw_groups_of_many_chunks(chunk):
     """Small chunks accumulate dW once per group of G chunks, and with an FP32
-    table a group runs as one working chunk. At V = 65536 the 256 MiB group
-    buffer caps G at 32 chunks of 64 columns (2048 tokens at chunk 64, 1920 at
-    chunk 60), so 2500 tokens make a full working chunk and a partial one (and
+    table a group runs as one working chunk. At V = 65536 the 4096-column cap
+    holds G to 64 chunks of 64 columns (4096 tokens at chunk 64, 3840 at
+    chunk 60), so 5000 tokens make a full working chunk and a partial one (and
     dH sums two vocabulary parts). Both paths (single call and two-call), FP32
     table with bias, against the oracle; each path's dH bitwise equal to its
     own unchunked run (the two paths round the softmax part differently)."""
-    w = synth.LinearWorkload(f"groups_{chunk}", 2500, 136, 65536, "bf16", True, chunk, "normal")
+    w = synth.LinearWorkload(f"groups_{chunk}", 5000, 136, 65536, "bf16", True, chunk, "normal")
     d = synth.make_linear_t(w, DEV)
     host = synth.make_linear_np(w)
     rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True, True,
