@@ -80,9 +80,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // bit (r / 8) & 1 separates them and keeps any 8 consecutive rows distinct.
 __device__ __forceinline__ int swz_row(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// LDS handed to the epilogues: four regions of kOpB bytes.
+// LDS handed to the epilogues: four regions of kOpB bytes, and with the DMA
+// pipeline a fifth one (its fifth operand slot; null otherwise).
 struct EpiLds {
   char* a[4];
+  char* x;
 };
 
 template <typename T> struct ET;
@@ -619,6 +621,27 @@ __device__ __forceinline__ void epi_accum_t(const GemmProblem& p, Acc& acc, int6
 // so the two 32-lane row groups of an accumulator write fall on distinct banks.
 __device__ __forceinline__ int tab_swz(int rr) { return ((rr >> 2) & 1) << 5; }
 
+// Half h of the tile (rows of mi = 2 h and 2 h + 1 in both wave rows), times
+// s, into the four LDS regions: region 2 wm + mh holds the 32 rows of
+// mi = 2 h + mh of wave row wm, row rr and column c at float rr * 256 +
+// (c ^ tab_swz(rr)).
+__device__ __forceinline__ void tab_stage_half(const Acc& acc, int h, float sc, const Frag& f, const EpiLds& L) {
+#pragma unroll
+  for (int mh = 0; mh < 2; ++mh) {
+    // the region pointer is chosen without a runtime index into L.a (which
+    // would place the pointer array in private memory)
+    float* reg = reinterpret_cast<float*>(f.wm ? L.a[2 + mh] : L.a[mh]);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = (r >> 2) * 8 + (f.lane >> 5) * 4 + (r & 3);
+        const int col = f.wn * kWaveColsN + ni * 32 + (f.lane & 31);
+        reg[rr * 256 + (col ^ tab_swz(rr))] = acc[2 * h + mh][ni][r] * sc;
+      }
+  }
+}
+
 // kFresh: the table holds no values yet (first chunk without accumulate): +0
 // stands in for the old values, which are not read.
 template <bool kFresh>
@@ -657,22 +680,7 @@ __device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, i
                                              rs, vbase + row_of(h, 2 * kPpr * k + j) * (int)e.ldo * 4, 0, 2 /* nt */));
     }
   };
-  auto to_lds = [&](int h) {
-#pragma unroll
-    for (int mh = 0; mh < 2; ++mh) {
-      // the region pointer is chosen without a runtime index into L.a (which
-      // would place the pointer array in private memory)
-      float* reg = reinterpret_cast<float*>(f.wm ? L.a[2 + mh] : L.a[mh]);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rr = (r >> 2) * 8 + (f.lane >> 5) * 4 + (r & 3);
-          const int col = f.wn * kWaveColsN + ni * 32 + (f.lane & 31);
-          reg[rr * 256 + (col ^ tab_swz(rr))] = acc[2 * h + mh][ni][r] * sc;
-        }
-    }
-  };
+  auto to_lds = [&](int h) { tab_stage_half(acc, h, sc, f, L); };
   auto store_q = [&](int h, int k, const f32x4 (&o)[2 * kPpr]) {
 #pragma unroll
     for (int j = 0; j < 2 * kPpr; ++j) {
@@ -710,12 +718,115 @@ __device__ __forceinline__ void epi_accum_fast(const GemmProblem& p, Acc& acc, i
   store_q(1, 1, qb);
 }
 
+// dW rows of an operand-dtype (16-bit) table: each element becomes
+//     round(old + (s C + sum, in list order, of tcoef[n] h[n, col]))
+// over the chunk's valid tokens n with that row as target, the same
+// operations in the same order as epi_accum_t (so the same bits). The tile
+// goes through LDS as in epi_accum_fast (two halves of 128 rows, s C in fp32)
+// and every thread reads and writes whole 16-byte pieces (8 elements) of table
+// rows with buffer instructions whose whole offset is in the vector operand:
+// rows of a last tile past the table's end read as 0 and are not stored. The
+// old values of half 1 are in flight while half 0 is finished. The tile's
+// validated list heads sit in the fifth LDS region (DMA pipeline only).
+// Requires D % 8 == 0, a 16-byte aligned table and h, and a 256-row tile span
+// below 2 GiB (EpiParams::tab_fast16).
+template <typename T>
+__device__ __forceinline__ void epi_accum_fast16(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
+                                                 const Frag& f, const EpiLds& L) {
+  static_assert(sizeof(T) == 2, "a 16-bit table");
+  static_assert(MI == 4 && kWaveM == 2 && kTileN == 256, "two halves of four 32-row regions");
+  constexpr int kPpr = kTileN / 8;           // 16-byte pieces per tile row
+  constexpr int kRowStep = kThreads / kPpr;  // rows covered by one pass of all threads
+  constexpr int kPieces = 128 / kRowStep;    // pieces per thread and half
+  static_assert(kPieces * kRowStep == 128 && 32 % kRowStep == 0, "threads divide a half and a region");
+  typedef T t8 __attribute__((ext_vector_type(8)));
+  const EpiParams& e = p.ep;
+  const float sc = e.scales[e.chunk].x;
+  const int tid = threadIdx.x;
+  const T* h = static_cast<const T*>(e.h);
+  T* tb0 = static_cast<T*>(e.out) + m0 * e.ldo + n0;
+  const int64_t span = ((p.M - m0) * e.ldo - n0) * 2;  // bytes from the tile's first element to the table's end
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(tb0, (short)0, span < 0x7FFFFFF0LL ? (int)span : 0x7FFFFFF0, 0x00020000);
+  const int pc = tid % kPpr;             // this thread's columns [8 pc, 8 pc + 8) of the tile
+  const int r0 = tid / kPpr;             // its first local row; piece q adds q kRowStep rows
+  const bool colok = n0 + 8 * pc < p.N;  // D % 8 == 0: a piece lies in [0, N) or past it
+  int32_t* hs = reinterpret_cast<int32_t*>(L.x);
+  for (int i = tid; i < kTileM; i += kThreads) {
+    const int64_t m = m0 + i;
+    int32_t j = (m < p.M && e.head != nullptr) ? e.head[m] : -1;
+    int64_t t;
+    if (!(j >= 0 && j < e.ntok && token_valid(e, e.tok0 + j, t) && t == m)) j = -1;
+    hs[i] = j;
+  }
+  // piece q of half hf: local row r0 + q kRowStep, in region (q kRowStep) / 32
+  // (r0 < kRowStep, so the region does not depend on the thread and no
+  // runtime index into L.a is needed), which holds the 32 tile rows of wave
+  // row region / 2 and block mi = 2 hf + region % 2
+  auto region = [](int q) { return (q * kRowStep) >> 5; };
+  auto tile_row = [&](int hf, int q) {
+    const int g = region(q);
+    return (g >> 1) * 128 + (2 * hf + (g & 1)) * 32 + ((q * kRowStep) & 31) + r0;
+  };
+  auto load_old = [&](int hf, u32x4 (&o)[kPieces]) {
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      const int row = tile_row(hf, q);
+      if (e.tab_store)
+        o[q] = u32x4{0u, 0u, 0u, 0u};
+      else
+        o[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, (row * (int)e.ldo + 8 * pc) * 2, 0, 2 /* nt */);
+    }
+  };
+  auto finish = [&](int hf, const u32x4 (&o)[kPieces]) {
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      const int row = tile_row(hf, q);
+      const int rr = ((q * kRowStep) & 31) + r0;
+      const float* reg = reinterpret_cast<const float*>(L.a[region(q)]);
+      const float* src = reg + rr * 256 + ((8 * pc) ^ tab_swz(rr));
+      float v[8];
+      *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(src);
+      *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(src + 4);
+      // the one-hot part, at most ntok steps: the walk ends even if the list were malformed
+      int32_t j = hs[row];
+      for (int64_t it = 0; colok && it < e.ntok && j >= 0 && j < e.ntok; ++it) {
+        const float c = e.tcoef[e.tok0 + j];
+        const t8 x = *reinterpret_cast<const t8*>(h + (e.tok0 + j) * e.ldh + n0 + 8 * pc);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = fmaf(c, (float)x[k], v[k]);
+        j = e.next[j];
+      }
+      const t8 old = __builtin_bit_cast(t8, o[q]);
+      t8 out;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) out[k] = (T)((float)old[k] + v[k]);
+      if (colok && m0 + row < p.M)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rs, (row * (int)e.ldo + 8 * pc) * 2, 0,
+                                               2 /* nt */);
+    }
+  };
+  u32x4 qa[kPieces], qb[kPieces];
+  load_old(0, qa);
+  tab_stage_half(acc, 0, sc, f, L);
+  __syncthreads();  // the list heads and half 0 are in LDS
+  __builtin_amdgcn_sched_barrier(0);
+  load_old(1, qb);
+  __builtin_amdgcn_sched_barrier(0);
+  finish(0, qa);
+  __syncthreads();  // half 0 has been read
+  tab_stage_half(acc, 1, sc, f, L);
+  __syncthreads();
+  finish(1, qb);
+}
+
 // Which dW epilogue a kernel carries (one per kernel keeps the code small: the
 // dH and dW tiles' loops run side by side and share the instruction cache):
 // ACC_FAST and ACC_FRESH are epi_accum_fast (an FP32 table whose one-hot rows
-// are added beforehand; FRESH for a first chunk without accumulate), ACC_ANY
+// are added beforehand; FRESH for a first chunk without accumulate),
+// ACC_FAST16 is epi_accum_fast16 (a 16-bit operand-dtype table), ACC_ANY
 // decides at run time among the list-walking epilogues.
-enum AccMode : int { ACC_ANY = 0, ACC_FAST = 1, ACC_FRESH = 2 };
+enum AccMode : int { ACC_ANY = 0, ACC_FAST = 1, ACC_FRESH = 2, ACC_FAST16 = 3 };
 
 template <typename T, int kAcc>
 __device__ __forceinline__ void epi_accum(const GemmProblem& p, Acc& acc, int64_t m0, int64_t n0,
@@ -724,6 +835,8 @@ __device__ __forceinline__ void epi_accum(const GemmProblem& p, Acc& acc, int64_
     epi_accum_fast<false>(p, acc, m0, n0, f, L);
   } else if constexpr (kAcc == ACC_FRESH) {
     epi_accum_fast<true>(p, acc, m0, n0, f, L);
+  } else if constexpr (kAcc == ACC_FAST16) {
+    if constexpr (sizeof(T) == 2) epi_accum_fast16<T>(p, acc, m0, n0, f, L);
   } else {
     if (p.ep.out_dt == DT_F32)
       epi_accum_t<T, float>(p, acc, m0, n0, f, L);
@@ -1170,7 +1283,7 @@ __device__ __forceinline__ void tile_run(const GemmProblem& p, int id, char* con
     else
       mainloop<T, false>(p, m0, n0, f, buf[0], acc, part);
   }
-  const EpiLds L = {{buf[0], buf[1], buf[2], buf[3]}};
+  const EpiLds L = {{buf[0], buf[1], buf[2], buf[3]}, kDma ? buf[4] : nullptr};
 
   if constexpr (E == EPI_LSE_PARTIAL) epi_lse_partial<T, false>(p, acc, tm, m0, n0, f);
   if constexpr (E == EPI_LSE_Q) epi_lse_partial<T, true>(p, acc, tm, m0, n0, f);
@@ -1326,6 +1439,7 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
     const bool mn = p0 != nullptr && p0->mn;
     // the dW epilogue of this launch (any mode serves when there are no dW tiles)
     const int acc = p1 == nullptr ? ACC_FAST
+                    : p1->ep.tab_fast16 && sizeof(T) == 2 && p1->ep.out_dt != DT_F32 ? ACC_FAST16
                     : !p1->ep.tab_fast ? ACC_ANY
                     : p1->ep.tab_store ? ACC_FRESH
                                        : ACC_FAST;
@@ -1337,13 +1451,17 @@ hipError_t launch_t(const GemmProblem* p0, const GemmProblem* p1, hipStream_t s)
         if (acc == ACC_FAST) dh_dw_kernel<T, true, true, ACC_FAST><<<grid, block, 0, s>>>(a, b, nt0);
         else if (acc == ACC_FRESH)
           dh_dw_kernel<T, true, true, ACC_FRESH><<<grid, block, 0, s>>>(a, b, nt0);
+        else if (acc == ACC_FAST16)
+          dh_dw_kernel<T, true, true, ACC_FAST16><<<grid, block, 0, s>>>(a, b, nt0);
         else dh_dw_kernel<T, true, true, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
       }
     } else {
       if (acc == ACC_FAST) dh_dw_kernel<T, true, false, ACC_FAST><<<grid, block, 0, s>>>(a, b, nt0);
       else if (acc == ACC_FRESH)
         dh_dw_kernel<T, true, false, ACC_FRESH><<<grid, block, 0, s>>>(a, b, nt0);
-      else dh_dw_kernel<T, true, false, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
+      else if (acc == ACC_FAST16) {
+        if constexpr (sizeof(T) == 2) dh_dw_kernel<T, true, false, ACC_FAST16><<<grid, block, 0, s>>>(a, b, nt0);
+      } else dh_dw_kernel<T, true, false, ACC_ANY><<<grid, block, 0, s>>>(a, b, nt0);
     }
   } else {
     return hipErrorInvalidValue;

@@ -81,6 +81,7 @@ struct EpiParams {
   const int32_t* next;     // [C] next chunk token with the same target, -1 at the end
   int64_t ntok;            // tokens in the chunk
   int tab_fast;            // FP32 table without one-hot part, D % 4 == 0, 16-byte aligned, tile span < 2 GiB
+  int tab_fast16;          // operand-dtype (16-bit) table: D % 8 == 0, table and h 16-byte aligned, tile span < 2 GiB
   int tab_store;           // the table holds no values yet (first chunk, no accumulate): +0 stands in for
                            // the old values, which are not read (so no zero fill is needed)
   // EPI_STORE and EPI_ACCUM

@@ -643,6 +643,9 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
       pw.ep.head = dW_dtype == LLP_F32 ? nullptr : head;  // null: one-hot rows already added
       pw.ep.next = next;
       pw.ep.tab_fast = dW_dtype == LLP_F32 && D % 4 == 0 && aligned16(dW) && kTile * D * 4 < 0x7FFFFFF0LL;
+      // an operand-dtype table in 16-byte pieces (the list heads and next links are built for it)
+      pw.ep.tab_fast16 = dW_dtype == dtype && e == 2 && D % 8 == 0 && aligned16(dW) && aligned16(h) &&
+                         kTile * D * 2 < 0x7FFFFFF0LL;
       pw.ep.tab_store = (store_first && k == fdw) ? 1 : 0;
       pw.ep.ntok = Ck;
       pw.ep.scales = scales;
