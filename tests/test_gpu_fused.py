@@ -204,20 +204,23 @@ def test_fused_operand_dtype_table(dt):
     """The single call's operand-dtype dW / db tables against the oracle: the
     stated gradient tolerance plus the table's own re-rounding after every
     chunk (an operand-dtype table is rounded once per chunk, as a same-dtype
-    addmm_ would be), from the oracle's per-chunk partial sums."""
-    w = synth.LinearWorkload(f"optable_{dt}", 300, 136, 1031, dt, True, 128, "normal")
-    d = synth.make_linear_t(w, DEV)
-    logp, lse, dH, dW, db = fused(w, d, tdt=torch_dtype(dt))
-    assert dW.dtype == torch_dtype(dt) and db.dtype == torch_dtype(dt)
-    host = synth.make_linear_np(w)
-    rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True, True,
-                                      True)
-    bw, bb = chunk_rounding_budget(w, host, 8 if dt == "bf16" else 11)
-    atol, rtol = TOL[dt]["grad"]
-    assert_close(dH, rdH, atol, rtol, "dH")
-    assert_within(dW, rdW, atol, rtol, bw, "dW (operand-dtype table)")
-    assert_within(db, rdb, atol, rtol, bb, "db (operand-dtype table)")
-    say(f"fused {dt} table: dW normalised error {norm_err(dW, rdW):.2e}, db {norm_err(db, rdb):.2e}")
+    addmm_ would be), from the oracle's per-chunk partial sums. D = 136 takes
+    the table epilogue in 16-byte pieces, D = 100 (D % 8 != 0) the one that
+    walks the lists per element."""
+    for D in (136, 100):
+        w = synth.LinearWorkload(f"optable_{dt}_{D}", 300, D, 1031, dt, True, 128, "normal")
+        d = synth.make_linear_t(w, DEV)
+        logp, lse, dH, dW, db = fused(w, d, tdt=torch_dtype(dt))
+        assert dW.dtype == torch_dtype(dt) and db.dtype == torch_dtype(dt)
+        host = synth.make_linear_np(w)
+        rdH, rdW, rdb = O.linear_logp_bwd(host["h64"], host["W64"], host["b64"], host["t"], host["g64"], True,
+                                          True, True)
+        bw, bb = chunk_rounding_budget(w, host, 8 if dt == "bf16" else 11)
+        atol, rtol = TOL[dt]["grad"]
+        assert_close(dH, rdH, atol, rtol, f"dH D={D}")
+        assert_within(dW, rdW, atol, rtol, bw, f"dW (operand-dtype table) D={D}")
+        assert_within(db, rdb, atol, rtol, bb, f"db (operand-dtype table) D={D}")
+        say(f"fused {dt} table D={D}: dW normalised error {norm_err(dW, rdW):.2e}, db {norm_err(db, rdb):.2e}")
 
 
 # ----------------------------------------------------------------------------- full size
