@@ -476,15 +476,16 @@ def run_linear(w, args, torch, llp):
     exec_flops = {"fused": A.linear_model_flops(N, D, V), "split": flops8}
     peak = PEAK_TFLOPS[w.dtype]
     results = {}
-    # the single call overlaps the next chunk's forward with 16-bit operands and
-    # runs dW once per group of G chunks with an FP32 table (K >= 2); small
-    # chunks with C % 8 == 0 take dH per group too
+    # the single call overlaps the next chunk's forward with 16-bit operands
+    # (D % 8 == 0) and an FP32 table (an operand-dtype table keeps separate
+    # launches), and runs dW once per group of G chunks with an FP32 table
+    # (K >= 2); small chunks with C % 8 == 0 take dH per group too
     esz = 4 if w.dtype == "f32" else 2
     Cw, Kw, G, group_dh = schedule(N, D, V, C, K, esz, True, args.table == "f32")
-    overlap = w.dtype in ("bf16", "f16") and Kw >= 2 and D % 8 == 0
+    overlap = w.dtype in ("bf16", "f16") and Kw >= 2 and D % 8 == 0 and args.table == "f32"
     # the backward of the two-call path overlaps alike (the next chunk's dlogits recompute)
     sCw, sKw, sG, s_gdh = schedule(N, D, V, C, K, esz, False, args.table == "f32")
-    s_overlap = w.dtype in ("bf16", "f16") and sKw >= 2 and D % 8 == 0
+    s_overlap = w.dtype in ("bf16", "f16") and sKw >= 2 and D % 8 == 0 and args.table == "f32"
     for name, step, sf in (
             ("split", split_step, split_step_flops(N, D, V, sCw, sKw, s_overlap, sG, s_gdh)),
             ("fused", fused_step, fused_step_flops(N, D, V, Cw, Kw, overlap, G, group_dh))):
