@@ -349,15 +349,15 @@ def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
 
 def schedule(N, D, V, C, K, esize, fused, table_f32=True):
     """(working chunk, chunks, chunks per dW group, dH per group) of the
-    library's backward schedule: with more than two small chunks per group, an
-    FP32 table and dH on the layout without W^T, a group runs as one working
-    chunk of G C tokens (no further grouping); otherwise the caller's chunks
-    in groups of G."""
+    library's backward schedule: with two or more chunks per group, an FP32
+    table and dH on the layout without W^T, a group runs as one working chunk
+    of G C tokens (no further grouping); otherwise the caller's chunks in
+    groups of G."""
     G = dw_group(N, D, V, C, K, esize, fused, table_f32)
     ld = -(-C // 8) * 8
     lim = 0x7FFFFFF0
     kmajor = esize == 2 and D % 8 == 0 and V * D * esize < lim and V * max(G * ld, 2 * ld) * esize < lim
-    if G > 2 and kmajor:
+    if G >= 2 and kmajor:
         Cw = min(G * C, N)
         return Cw, -(-N // Cw), 1, False
     small = esize == 2 and C % 8 == 0 and -(-C // 256) * -(-D // 256) < 128

@@ -318,7 +318,7 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   // group_dh). Shapes alone decide, so every subset of outputs accumulates dW
   // alike.
   // The working schedule: with an FP32 table (dW_dtype, whether or not dW is
-  // requested) and a plan whose working chunk covers a whole group of small
+  // requested) and a plan whose working chunk covers a whole group of
   // chunks (Cw > C), chunks of Cw tokens and no further grouping; otherwise
   // the caller's chunks, grouped by the plan's G. (logp, lse and dH do not
   // depend on the chunking; the FP32 table's additions come in another order.)

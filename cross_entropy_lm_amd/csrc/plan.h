@@ -107,11 +107,13 @@ struct BwdPlan {
   // D % 8 == 0. G = 2, or for small chunks up to 4096 group columns while one
   // group buffer stays within 1 GiB.
   int64_t G = 1;
-  // Working chunk. With more than two small chunks per group and the layout
-  // without W^T, a group is processed as one chunk of Cw = min(G C, N)
-  // tokens when the table is FP32: its logits, dH and dW in one pass each,
-  // which fills the 256-token tiles that a 110-token chunk would leave half
-  // empty. Otherwise Cw = C. Buffers are sized for Cw.
+  // Working chunk. With more than two small chunks per group, or a pair of
+  // chunks when dW or db is requested, and the layout without W^T, a group
+  // is processed as one chunk of Cw = min(G C, N) tokens when the table is
+  // FP32: its logits, dH and dW in one pass each, which fills the 256-token
+  // tiles that a 110-token chunk would leave half empty and, for a pair of
+  // large chunks, halves the launches in the same group buffer. Otherwise
+  // Cw = C. Buffers are sized for Cw.
   int64_t Cw = 0;
   // leading dimension of the vocab-major and h^T buffers: G ldSt (chunk j of
   // a group in the columns [j ldSt, j ldSt + C)), which also holds round8(Cw)
@@ -206,8 +208,8 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   p->G = want_dW ? gc : 1;
   // 16-bit operands with D % 8 == 0 whose operands (W, and a group's
   // dlogits^T) each span < 2 GiB: dH reads them as stored (kmajor), the bf16
-  // single call stores per-token numerators (qtok), and a group of more than
-  // two chunks runs as one working chunk (Cw)
+  // single call stores per-token numerators (qtok), and a group runs as one
+  // working chunk (Cw)
   bool shape;
   {
     const int64_t lim = 0x7FFFFFF0LL;
@@ -218,7 +220,9 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
     p->kmajor = want_dH && shape;
     p->qtok = fused && dtype == LLP_BF16 && shape;
   }
-  p->Cw = (gc > 2 && shape) ? (gc * p->C < N ? gc * p->C : N) : p->C;
+  // (a pair of chunks only when dW or db is requested: their group buffer is
+  // then there anyway, and logp, lse and dH do not depend on the chunking)
+  p->Cw = (shape && (gc > 2 || (gc == 2 && (want_dW || want_db)))) ? (gc * p->C < N ? gc * p->C : N) : p->C;
   {
     const int64_t wcols = round_up(p->Cw, 8);
     if (!mul_ok(p->G, p->ldSt, &p->ldP)) return LLP_EOVERFLOW;

@@ -79,10 +79,14 @@ static void check_layout(int64_t N, int64_t D, int64_t V, int dt, int64_t chunk,
   if (p.kmajor) EXPECT(p.off_Wt < 0 && p.off_dS < 0 && p.off_dSt >= 0);
   if (dh) EXPECT(p.dh_part == (esize(dt) == 4 ? 8192 : 32768) && p.dh_parts == (V + p.dh_part - 1) / p.dh_part);
   if (dh) EXPECT(p.dh_rows == p.C || p.dh_rows == p.G * p.C || p.dh_rows == p.Cw);
-  // the working chunk: the chunk, or a whole group of more than two chunks (at most N tokens)
+  // the working chunk: the chunk, or a whole group of two or more chunks (at most N tokens)
   // (Cw does not depend on which outputs are requested: G is the group of the dW schedule)
   EXPECT(p.Cw >= p.C && p.Cw <= (N > p.C ? N : p.C) && (p.Cw - p.C) % p.C == 0 || p.Cw == N);
-  if (dw && p.Cw > p.C) EXPECT(p.G > 2 && p.Cw == (p.G * p.C < N ? p.G * p.C : N));
+  if (dw && p.Cw > p.C) EXPECT(p.G >= 2 && p.Cw == (p.G * p.C < N ? p.G * p.C : N));
+  // a group of two or more chunks on the layout without W^T runs as one working chunk
+  if (dw && p.G >= 2 && esize(dt) == 2 && D % 8 == 0 && V * D * 2 < 0x7FFFFFF0LL &&
+      V * p.ldP * 2 < 0x7FFFFFF0LL)
+    EXPECT(p.Cw == (p.G * p.C < N ? p.G * p.C : N));
   EXPECT(round_up(p.Cw, 8) <= p.ldP);
   EXPECT((p.off_dhp >= 0) == (dh && p.dh_parts > 1));
   if (dh && !p.kmajor) EXPECT(p.off_Wt >= 0 && p.off_dS >= 0);

@@ -101,11 +101,12 @@ def test_workspace_queries():
     expect_odd = 1020 * 8192 * 2 + 512 * 8192 * 2
     assert expect_odd <= odd < expect_odd + (1 << 20)
     # the single call at 16384 x 4096 x 32000, bf16, chunk 2048, FP32 table:
-    # two pair buffers of numerators [V][2 x 2048], h^T of a pair, two chunks'
-    # forward partials and per-token arrays (about 540 MiB)
+    # each pair of chunks runs as one 4096-token working chunk, so two pair
+    # buffers of numerators [V][2 x 2048], h^T of a pair, two working chunks'
+    # forward partials and per-token arrays (about 548 MiB)
     fq = llp.linear_logp_fwd_bwd_workspace_size
     single = fq(16384, 4096, 32000, BF16, 2048, True, True, False, True)
-    expect_single = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 250 * 2048 * 8
+    expect_single = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 250 * 4096 * 8
     assert expect_single <= single < expect_single + (1 << 20)
     # 110-token chunks at V = 151936: groups of 31 chunks (a 1 GiB group
     # buffer holds 31 x 112 columns) run as one 3410-token working chunk: two
@@ -138,8 +139,8 @@ def test_bench_group_rule_matches_the_library():
             with_dw = q(N, D, V, BF16, C, False, True, False, True)
             # dW alone: the group buffer [V][G ld] and h^T [D][G ld], (single
             # call) the forward's partials of one working chunk (a whole group
-            # when G > 2), and per-token arrays
-            Cw = min(G * C, N) if G > 2 else C
+            # when G >= 2 on the layout without W^T), and per-token arrays
+            Cw = min(G * C, N) if G >= 2 and D % 8 == 0 else C
             core = V * G * ld * 2 + D * G * ld * 2 + (P * Cw * 8 if fused else 0)
             assert core <= with_dw < core + (1 << 20) + 4 * V + 16 * N + 4 * Cw, (N, D, V, C, G, fused)
 
