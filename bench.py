@@ -349,17 +349,19 @@ def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
 
 def schedule(N, D, V, C, K, esize, fused, table_f32=True):
     """(working chunk, chunks, chunks per dW group, dH per group) of the
-    library's backward schedule: with two or more chunks per group, an FP32
-    table and dH on the layout without W^T, a group runs as one working chunk
-    of G C tokens (no further grouping); otherwise the caller's chunks in
-    groups of G."""
-    G = dw_group(N, D, V, C, K, esize, fused, table_f32)
+    library's backward schedule with dW requested: with two or more chunks in
+    the plan's group (from the shapes alone, whatever the table's dtype) and
+    dH on the layout without W^T, a group runs as one working chunk of G C
+    tokens (no further grouping); otherwise the caller's chunks in groups of
+    G (an FP32 table's rule)."""
+    gp = dw_group(N, D, V, C, K, esize, fused, True)
     ld = -(-C // 8) * 8
     lim = 0x7FFFFFF0
-    kmajor = esize == 2 and D % 8 == 0 and V * D * esize < lim and V * max(G * ld, 2 * ld) * esize < lim
-    if G >= 2 and kmajor:
-        Cw = min(G * C, N)
+    kmajor = esize == 2 and D % 8 == 0 and V * D * esize < lim and V * max(gp * ld, 2 * ld) * esize < lim
+    if gp >= 2 and kmajor:
+        Cw = min(gp * C, N)
         return Cw, -(-N // Cw), 1, False
+    G = dw_group(N, D, V, C, K, esize, fused, table_f32)
     small = esize == 2 and C % 8 == 0 and -(-C // 256) * -(-D // 256) < 128
     return C, K, G, G > 1 and small and kmajor
 

@@ -317,12 +317,13 @@ int backward_impl(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, con
   // recompute; with C % 8 == 0 small chunks' dH runs once per group too (see
   // group_dh). Shapes alone decide, so every subset of outputs accumulates dW
   // alike.
-  // The working schedule: with an FP32 table (dW_dtype, whether or not dW is
-  // requested) and a plan whose working chunk covers a whole group of
-  // chunks (Cw > C), chunks of Cw tokens and no further grouping; otherwise
+  // The working schedule: with a plan whose working chunk covers a whole
+  // group of chunks (Cw > C; the buffers are sized for it whatever the
+  // table's dtype), chunks of Cw tokens and no further grouping; otherwise
   // the caller's chunks, grouped by the plan's G. (logp, lse and dH do not
-  // depend on the chunking; the FP32 table's additions come in another order.)
-  const bool work = dW_dtype == LLP_F32 && bp.Cw > bp.C;
+  // depend on the chunking; dW and db come in another order of additions,
+  // and an operand-dtype table is rounded once per working chunk.)
+  const bool work = bp.Cw > bp.C;
   const int64_t C = work ? bp.Cw : bp.C;
   const int64_t K = work ? ceil_div(N, C) : bp.K;
   const int64_t ldSt = work ? round_up(C, 8) : bp.ldSt;

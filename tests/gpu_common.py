@@ -200,7 +200,9 @@ def chunk_rounding_budget(w, host, esize_bits):
     """Bound on the extra error of an operand-dtype table: after each chunk the
     running table is rounded to the operand dtype, which moves it by at most
     2^-p |running value| (p = 8 for bf16, 11 for fp16). The running values are
-    the oracle's partial sums over the chunks' tokens."""
+    the oracle's partial sums over the chunks' tokens. The library rounds once
+    per working chunk (a run of consecutive chunks), at a subset of these
+    points, so the sum over every chunk bounds it too."""
     from oracle import linear_logp as O
 
     run_w = np.zeros((w.V, w.D))

@@ -142,7 +142,8 @@ def test_flce_bf16_operand_dtype_table():
     host = HostCase(w)
     vr = sample_vocab(w.V, host.full["t"])
     g64 = -np.ones(w.N)
-    # rounding budget of the bf16 table: 2^-8 |running value| after every chunk
+    # rounding budget of the bf16 table: 2^-8 |running value| after every chunk (the
+    # table is rounded once per working chunk of consecutive chunks, a subset of these)
     run = np.zeros((vr.size, w.D))
     budget = np.zeros((vr.size, w.D))
     for c0 in range(0, w.N, w.chunk):

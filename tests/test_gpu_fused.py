@@ -202,9 +202,10 @@ def test_fused_empty_batch_and_accumulate():
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_fused_operand_dtype_table(dt):
     """The single call's operand-dtype dW / db tables against the oracle: the
-    stated gradient tolerance plus the table's own re-rounding after every
-    chunk (an operand-dtype table is rounded once per chunk, as a same-dtype
-    addmm_ would be), from the oracle's per-chunk partial sums. D = 136 takes
+    stated gradient tolerance plus the table's own re-rounding (an
+    operand-dtype table is rounded once per working chunk, as a same-dtype
+    addmm_ would be per chunk), bounded from the oracle's per-chunk partial
+    sums. D = 136 takes
     the table epilogue in 16-byte pieces, D = 100 (D % 8 != 0) the one that
     walks the lists per element."""
     for D in (136, 100):
@@ -266,9 +267,10 @@ def test_fused_flce_full_size(dt):
 
 def test_fused_flce_bf16_operand_dtype_table_full_size():
     """16384 x 4096 x 32000, bf16 operands, bf16 dW table (one rounding of the
-    table per 2048-token chunk), g = -1: sampled vocabulary rows against the
-    oracle within the stated tolerance plus the per-chunk rounding budget of
-    the running table, and sampled dH rows at the stated tolerance."""
+    table per 4096-token working chunk), g = -1: sampled vocabulary rows
+    against the oracle within the stated tolerance plus the rounding budget of
+    the running table summed over the 2048-token chunks (a superset of the
+    points where it is rounded), and sampled dH rows at the stated tolerance."""
     w = synth.FLCE
     d = synth.make_linear_t(w, DEV)
     g1 = torch.full((w.N,), -1.0, device=DEV)
