@@ -12,7 +12,7 @@ import synth
 from oracle import linear_logp as O
 
 from gpu_common import (TOL, HostCase, assert_close, assert_within, bits_equal, chunk_rounding_budget, norm_err,
-                        propagated_bound, sample_tokens, sample_vocab, say, torch_dtype)
+                        propagated_bound, sample_tokens, sample_vocab, say, to64, torch_dtype)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -315,11 +315,13 @@ def test_fused_bias_big_vocab_default_chunk():
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_fused_dw_chunk_pairs(dt):
-    """The FP32 table takes one dW contraction per pair of chunks: K = 2 (the
-    pair's store is the last contraction and the one-hot rows of both chunks
-    follow it), K = 3 (a last chunk without a partner), K = 4 with a ragged
-    last chunk, and K = 5 with accumulate; dW and db against the oracle, dH
-    bitwise equal to the unchunked run's."""
+    """The FP32 table takes one dW contraction per group of chunks. fp32
+    operands keep pairs of chunks: K = 2 (the pair's store is the last
+    contraction and the one-hot rows of both chunks follow it), K = 3 (a last
+    chunk without a partner), K = 4 with a ragged last chunk, and K = 5 with
+    accumulate; bf16 operands (D % 8 == 0) run each group as one working
+    chunk. dW and db against the oracle, dH bitwise equal to the unchunked
+    run's."""
     w = synth.LinearWorkload(f"pairs_{dt}", 300, 136, 1031, dt, True, 128, "normal")
     d = synth.make_linear_t(w, DEV)
     host = synth.make_linear_np(w)
@@ -473,6 +475,54 @@ def test_dw_groups_of_many_chunks(chunk):
     assert_close(sdH, rdH, *tg, "dH (two-call)")
     assert_close(sdW, rdW, *tg, "dW (two-call)")
     assert_close(sdb, rdb, *tg, "db (two-call)")
+
+
+@pytest.mark.parametrize("tab", ["f32", "bf16"])
+def test_pairs_run_as_working_chunks(tab):
+    """Chunks whose dH has 128 or more tiles pair for dW, and with dW or db
+    requested a pair runs as one working chunk: 1024-token chunks at D = 8192
+    (4 x 32 dH tiles each) give working chunks of 2048 tokens and a ragged
+    452. Both paths, with bias, an FP32 or a bf16 table. The stored softmax
+    parts do not depend on the chunking (per-token values, power-of-two chunk
+    scales), so dW and db equal those of one unchunked call up to the order
+    of the fp32 additions: a token dropped or added twice by the schedule
+    would move them by about 1e-3 of their largest element. Against the
+    oracle: at D = 8192 the logits spread enough (std 1.8) that some
+    vocabulary rows collect large softmax terms that cancel, so the stated
+    tolerance takes the first-order bound of their bf16 storage (three
+    roundings on the single call, one on the two-call path), plus a bf16
+    table's rounding budget over the 1024-token chunks. logp, lse and dH are
+    bitwise those of a dH-only call, which keeps the caller's chunks."""
+    w = synth.LinearWorkload(f"pairs_{tab}", 2500, 8192, 1031, "bf16", True, 1024, "normal")
+    d = synth.make_linear_t(w, DEV)
+    host = synth.make_linear_np(w)
+    h64, W64, b64, t64, g64 = host["h64"], host["W64"], host["b64"], host["t"], host["g64"]
+    rdH, rdW, rdb = O.linear_logp_bwd(h64, W64, b64, t64, g64, True, True, True)
+    atol, rtol = TOL["bf16"]["grad"]
+    tdt = None if tab == "f32" else torch.bfloat16
+    got = fused(w, d, tdt=tdt)
+    one = fused(w, d, tdt=tdt, chunk=w.N)
+    only_dh = fused(w, d, want=(True, False, False))
+    assert bits_equal(only_dh[0], got[0]) and bits_equal(only_dh[1], got[1]) and bits_equal(only_dh[2], got[2])
+    assert_close(got[2], rdH, atol, rtol, "dH")
+    _, _, sdH, sdW, sdb = split(w, d, tdt=tdt)
+    _, _, _, sdW1, sdb1 = split(w, d, tdt=tdt, chunk=w.N)
+    assert_close(sdH, rdH, atol, rtol, "dH (two-call)")
+    _, bW1, bb1 = propagated_bound(h64, W64, b64, t64, g64, "bf16", 1)
+    _, bW3, bb3 = propagated_bound(h64, W64, b64, t64, g64, "bf16", 3)
+    if tab == "f32":
+        for name, x, y in (("dW", got[3], one[3]), ("db", got[4], one[4]), ("dW (two-call)", sdW, sdW1),
+                           ("db (two-call)", sdb, sdb1)):
+            e = norm_err(x, to64(y))
+            assert e < 1e-5, f"{name}: paired schedule vs one chunk {e:.2e}"
+        bw = bb = 0.0
+    else:
+        bw, bb = chunk_rounding_budget(w, host, 8)
+    needed = [assert_within(x, r, atol, rtol, b + e, f"{name} ({tab} table)")
+              for name, x, r, b, e in (("dW", got[3], rdW, bw, bW3), ("db", got[4], rdb, bb, bb3),
+                                       ("dW (two-call)", sdW, rdW, bw, bW1), ("db (two-call)", sdb, rdb, bb, bb1))]
+    assert all(x.dtype == (torch.float32 if tab == "f32" else torch.bfloat16) for x in (got[3], got[4], sdW, sdb))
+    say(f"pairs {tab} table: elements beyond the stated tolerance (dW, db, two-call dW, db) = {needed}")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
