@@ -334,7 +334,7 @@ def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
     16-bit operands, fewer than 128 dH tiles; or 16-bit operands with
     D % 8 == 0) the two-call path accumulate dW once per group of G chunks:
     G = 2, for small chunks up to 4096 group columns and 1 GiB of group
-    buffer, at most K."""
+    buffer, at most K, then balanced: ceil(K / ceil(K / G))."""
     few = esize == 2 and -(-C // 256) * -(-D // 256) < 128
     ld = -(-C // 8) * 8
     lim = 0x7FFFFFF0
@@ -344,7 +344,8 @@ def dw_group(N, D, V, C, K, esize, fused, table_f32=True):
     g = 2
     if few:
         g = max(g, min(4096 // ld, (1 << 30) // (V * ld * esize)))
-    return min(g, K)
+    g = min(g, K)
+    return -(-K // -(-K // g))  # as many groups as g needs, of balanced sizes
 
 
 def schedule(N, D, V, C, K, esize, fused, table_f32=True):

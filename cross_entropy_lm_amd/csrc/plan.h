@@ -182,7 +182,8 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
   const bool small = few && p->C % 8 == 0;
   // Group size from the shapes alone (which outputs are requested does not
   // change the schedule): 2 chunks, or for small chunks up to kGroupCols
-  // columns and kGroupBytes of group buffer. 16-bit operands with D % 8 == 0 whose W and pair of chunk columns each
+  // columns and kGroupBytes of group buffer, balanced over the groups.
+  // 16-bit operands with D % 8 == 0 whose W and pair of chunk columns each
   // span < 2 GiB (the layout the overlapped backward reads as stored): the
   // two-call path pairs chunks too, its next chunk's dlogits recompute filling
   // the launches that carry no dW
@@ -204,6 +205,9 @@ inline int plan_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk, i
       if (m > g) g = m;
     }
     gc = g < p->K ? g : p->K;
+    // as many groups as that size needs, of balanced sizes (a last group of a
+    // few chunks would leave its launches' token tiles part empty)
+    gc = ceil_div(p->K, ceil_div(p->K, gc));
   }
   p->G = want_dW ? gc : 1;
   // 16-bit operands with D % 8 == 0 whose operands (W, and a group's

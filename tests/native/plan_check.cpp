@@ -73,6 +73,8 @@ static void check_layout(int64_t N, int64_t D, int64_t V, int dt, int64_t chunk,
   EXPECT(p.G >= 1 && p.G <= (p.K > 1 ? p.K : 1) && p.ldP >= p.G * p.ldSt);
   EXPECT(p.ldP == (p.G * p.ldSt > round_up(p.Cw, 8) ? p.G * p.ldSt : round_up(p.Cw, 8)));
   if (p.G > 2) EXPECT(p.G * p.ldSt <= 4096 && V * p.ldP * esize(dt) <= (int64_t(1) << 30));
+  // balanced groups: G is the smallest size that gives its number of groups
+  if (p.G >= 2) EXPECT(p.G == (p.K + (p.K + p.G - 1) / p.G - 1) / ((p.K + p.G - 1) / p.G));
   if (!dw) EXPECT(p.G == 1);
   // the layout holds only what the requested outputs need
   EXPECT(p.kmajor == (dh && esize(dt) == 2 && D % 8 == 0 && (p.off_Wt < 0)));

@@ -108,12 +108,13 @@ def test_workspace_queries():
     single = fq(16384, 4096, 32000, BF16, 2048, True, True, False, True)
     expect_single = 2 * 32000 * 4096 * 2 + 4096 * 4096 * 2 + 2 * 250 * 4096 * 8
     assert expect_single <= single < expect_single + (1 << 20)
-    # 110-token chunks at V = 151936: groups of 31 chunks (a 1 GiB group
-    # buffer holds 31 x 112 columns) run as one 3410-token working chunk: two
-    # group buffers, h^T of a group, two working chunks' forward partials, 5
-    # dH parts of a working chunk
+    # 110-token chunks at V = 151936: a 1 GiB group buffer holds 31 x 112
+    # columns, so the 75 chunks need three groups, balanced to 25 chunks each,
+    # which run as 2750-token working chunks: two group buffers, h^T of a
+    # group, two working chunks' forward partials, 5 dH parts of a working
+    # chunk
     big = fq(8192, 4096, 151936, BF16, 0, True, True, True, True)
-    expect_big = (2 * 151936 * 31 * 112 * 2 + 4096 * 31 * 112 * 2 + 2 * 1188 * 3410 * 8 + 5 * 3410 * 4096 * 4 +
+    expect_big = (2 * 151936 * 25 * 112 * 2 + 4096 * 25 * 112 * 2 + 2 * 1188 * 2750 * 8 + 5 * 2750 * 4096 * 4 +
                   151936 * 4)
     assert expect_big <= big < expect_big + (1 << 20)
 

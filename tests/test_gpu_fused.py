@@ -452,9 +452,9 @@ def test_fused_masked_vocab_blocks(dt):
 def test_dw_groups_of_many_chunks(chunk):
     """Small chunks accumulate dW once per group of G chunks, and with an FP32
     table a group runs as one working chunk. At V = 65536 the 4096-column cap
-    holds G to 64 chunks of 64 columns (4096 tokens at chunk 64, 3840 at
-    chunk 60), so 5000 tokens make a full working chunk and a partial one (and
-    dH sums two vocabulary parts). Both paths (single call and two-call), FP32
+    holds G to 64 chunks of 64 columns, so 5000 tokens need two groups,
+    balanced: working chunks of 2560 + 2440 tokens at chunk 64, 2520 + 2480
+    at chunk 60 (and dH sums two vocabulary parts). Both paths (single call and two-call), FP32
     table with bias, against the oracle; each path's dH bitwise equal to its
     own unchunked run (the two paths round the softmax part differently)."""
     w = synth.LinearWorkload(f"groups_{chunk}", 5000, 136, 65536, "bf16", True, chunk, "normal")
