@@ -403,12 +403,27 @@ __global__ void db_accum_kernel(const T* __restrict__ dSt, int64_t ldSt, int64_t
   const int lane = threadIdx.x & 63;
   const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (v >= V) return;  // uniform per wave
+  // the row in 16-byte pieces when its start allows (lane l sums pieces l,
+  // l + 64, ..., each piece's elements in order), then the remaining
+  // elements one per lane; in per-token mode each stored value is multiplied
+  // by its token's factor (chunk-local cq) first
+  constexpr int kv = 16 / (int)sizeof(T);
+  typedef __attribute__((__vector_size__(16))) unsigned int u32x4;
+  const T* row = dSt + v * ldSt;
+  const int64_t nv = (reinterpret_cast<uintptr_t>(row) % 16 == 0) ? C / kv : 0;  // whole pieces
   float s = 0.0f;
-  if (cq == nullptr) {
-    for (int64_t c = lane; c < C; c += 64) s += (float)dSt[v * ldSt + c];
-  } else {  // per-token mode: the stored value times the token's factor (chunk-local cq)
-    for (int64_t c = lane; c < C; c += 64) s += (float)dSt[v * ldSt + c] * cq[c];
+  for (int64_t q = lane; q < nv; q += 64) {
+    T x[kv];
+    *reinterpret_cast<u32x4*>(x) = *reinterpret_cast<const u32x4*>(row + q * kv);
+    if (cq == nullptr) {
+#pragma unroll
+      for (int i = 0; i < kv; ++i) s += (float)x[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kv; ++i) s += (float)x[i] * cq[q * kv + i];
+    }
   }
+  for (int64_t c = nv * kv + lane; c < C; c += 64) s += cq == nullptr ? (float)row[c] : (float)row[c] * cq[c];
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) {
     float val = s * scales[chunk].x;
