@@ -55,10 +55,14 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """The library's kernel sources and the build script that sets their
+    compiler flags (either changes the kernels the counters measured)."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "cross_entropy_lm_amd", "csrc"))):
         with open(os.path.join(ROOT, "cross_entropy_lm_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    with open(os.path.join(ROOT, "cross_entropy_lm_amd", "build.py"), "rb") as fh:
+        h.update(b"build.py" + fh.read())
     return h.hexdigest()[:16]
 
 
