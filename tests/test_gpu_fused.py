@@ -492,7 +492,8 @@ def test_pairs_run_as_working_chunks(tab):
     tolerance takes the first-order bound of their bf16 storage (three
     roundings on the single call, one on the two-call path), plus a bf16
     table's rounding budget over the 1024-token chunks. logp, lse and dH are
-    bitwise those of a dH-only call, which keeps the caller's chunks."""
+    bitwise those of a dH-only call, which keeps the caller's chunks; a
+    dW-only and a db-only call give the full call's dW and db bit for bit."""
     w = synth.LinearWorkload(f"pairs_{tab}", 2500, 8192, 1031, "bf16", True, 1024, "normal")
     d = synth.make_linear_t(w, DEV)
     host = synth.make_linear_np(w)
@@ -504,6 +505,11 @@ def test_pairs_run_as_working_chunks(tab):
     one = fused(w, d, tdt=tdt, chunk=w.N)
     only_dh = fused(w, d, want=(True, False, False))
     assert bits_equal(only_dh[0], got[0]) and bits_equal(only_dh[1], got[1]) and bits_equal(only_dh[2], got[2])
+    # dW alone and db alone run the same working chunks as the full call
+    only_dw = fused(w, d, tdt=tdt, want=(False, True, False))
+    only_db = fused(w, d, tdt=tdt, want=(False, False, True))
+    assert bits_equal(only_dw[3], got[3]) and only_dw[2] is None and only_dw[4] is None
+    assert bits_equal(only_db[4], got[4]) and only_db[2] is None and only_db[3] is None
     assert_close(got[2], rdH, atol, rtol, "dH")
     _, _, sdH, sdW, sdb = split(w, d, tdt=tdt)
     _, _, _, sdW1, sdb1 = split(w, d, tdt=tdt, chunk=w.N)
