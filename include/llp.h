@@ -152,15 +152,16 @@ LLP_API int linear_logp_fwd_noalloc(int64_t N, int64_t D, int64_t V, int dtype,
  * need). It holds a chunk's softmax part in the operand dtype, vocab-major
  * (the chunk workspace of RL-Kernel issue #261, "Static traffic model"), the
  * chunk's h transposed, and per-token scalars. The schedule, and with it the
- * size, is decided from the shapes alone: with an FP32 dW table the chunks
- * are taken in groups whose dW is one contraction (pairs; for small chunks up
- * to 4096 columns, run as one working chunk), so these buffers hold a group's
+ * size, is decided from the shapes alone: the chunks are taken in groups
+ * whose dW is one contraction (pairs; small chunks in balanced groups of up
+ * to 4096 columns within a 1 GiB buffer), so these buffers hold a group's
  * columns; with 16-bit operands and D % 8 == 0 (V D and V x the group's
  * columns each below 2^30 elements) dH reads W as stored, no transposed copy
- * of W is held, and a second softmax-part buffer lets the next chunk's
- * logits recompute run beside a chunk's dH / dW; with V above one
- * vocabulary part (32768 rows for 16-bit operands, 8192 for fp32) dH's fp32
- * sums over the parts are held too.
+ * of W is held, a group runs as one working chunk of its tokens when dW or
+ * db is requested (a group of small chunks always), and a second
+ * softmax-part buffer lets the next chunk's logits recompute run beside a
+ * chunk's dH / dW; with V above one vocabulary part (32768 rows for 16-bit
+ * operands, 8192 for fp32) dH's fp32 sums over the parts are held too.
  */
 LLP_API int linear_logp_bwd_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t chunk,
                                    int want_dH, int want_dW, int want_db, int have_lse,
@@ -213,10 +214,11 @@ LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t 
  * "Benchmark results", "Methodology"). With bf16 operands the numerators are
  * exp(z) itself wherever a block's maximum lies in [-40, 64] (else as above),
  * and each token's gradient factor is applied by the dH, dW and db steps.
- * With an FP32 dW table and two or more chunks, dW is accumulated once per
- * group of consecutive chunks (pairs; small chunks in larger groups), so the
- * table is read and written once per group; the workspace then holds the
- * group's columns side by side, twice (the next chunk's forward runs beside a
+ * With two or more chunks, dW is accumulated once per group of consecutive
+ * chunks (pairs; small chunks in larger groups), so the table is read and
+ * written once per group; with 16-bit operands and D % 8 == 0 the group runs
+ * as one working chunk. The workspace then holds the group's columns side by
+ * side, twice with an FP32 table (the next chunk's forward runs beside a
  * chunk's dH / dW).
  * logp and lse are bit-identical to linear_logp_fwd's. The gradients round
  * the softmax part twice (the stored numerator, then the gradient or, for
