@@ -218,8 +218,9 @@ LLP_API int linear_logp_bwd(int64_t N, int64_t D, int64_t V, int dtype, int64_t 
  * chunks (pairs; small chunks in larger groups), so the table is read and
  * written once per group; with 16-bit operands and D % 8 == 0 the group runs
  * as one working chunk. The workspace then holds the group's columns side by
- * side, twice with an FP32 table (the next chunk's forward runs beside a
- * chunk's dH / dW).
+ * side, twice (with an FP32 table the next chunk's forward runs beside a
+ * chunk's dH / dW; an operand-dtype table leaves the second copy unused, as
+ * the workspace query does not know the table's dtype).
  * logp and lse are bit-identical to linear_logp_fwd's. The gradients round
  * the softmax part twice (the stored numerator, then the gradient or, for
  * bf16, the h row scaled by the token's factor), so they match
