@@ -85,6 +85,9 @@ static void check_layout(int64_t N, int64_t D, int64_t V, int dt, int64_t chunk,
   // (Cw does not depend on which outputs are requested: G is the group of the dW schedule)
   EXPECT(p.Cw >= p.C && p.Cw <= (N > p.C ? N : p.C) && (p.Cw - p.C) % p.C == 0 || p.Cw == N);
   if (dw && p.Cw > p.C) EXPECT(p.G >= 2 && p.Cw == (p.G * p.C < N ? p.G * p.C : N));
+  // a dH-only call on chunks of 128 or more dH tiles keeps the caller's chunk
+  // (no group buffer to reuse, and dH does not depend on the chunking)
+  if (dh && !dw && !db && (p.C + kTile - 1) / kTile * ((D + kTile - 1) / kTile) >= 128) EXPECT(p.Cw == p.C);
   // a group of two or more chunks on the layout without W^T runs as one working chunk
   if (dw && p.G >= 2 && esize(dt) == 2 && D % 8 == 0 && V * D * 2 < 0x7FFFFFF0LL &&
       V * p.ldP * 2 < 0x7FFFFFF0LL)
